@@ -1,0 +1,223 @@
+"""libaqlm_mi355x: additive-quantized GEMV / small-batch GEMM on MI355X (gfx950).
+
+Thin ctypes binding over the C ABI declared in ``include/aqlm_mi355x.h``.  It
+only marshals arguments -- every step of the product runs in the HIP kernels of
+``libaqlm_mi355x.so``.  PyTorch supplies device memory and the current stream.
+There is no CPU fallback: if the library is missing, importing the compute
+functions raises.
+
+Format (page "AQLM (Additive Quantization for LLMs)", section "Niveau
+intermediaire"): codes [out][in/8][K] (uint8 for 8-bit codes, int16/uint16 bit
+patterns for 16-bit codes), codebooks [K][2^B][8] fp16, x [batch][in] fp16,
+y [batch][out] fp16.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = ["gemv", "gemm", "gemv_variant", "dequantize", "bits_per_weight", "codes_bytes",
+           "codebooks_bytes", "variant_supported", "selected_variant", "VARIANTS", "library_path",
+           "AqlmError", "version"]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libaqlm_mi355x.so")
+
+VARIANTS = {"auto": 0, "generic": 1, "lds": 2, "lut": 3, "l2": 4, "mfma": 5}
+_STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "HIP error"}
+
+
+class AqlmError(RuntimeError):
+    """A non-OK status from libaqlm_mi355x."""
+
+    def __init__(self, status: int, msg: str):
+        super().__init__(msg)
+        self.status = status
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run additive_quantized_gemv_amd/build.py "
+                          "(hipcc --offload-arch=gfx950)")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i64, ci = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    prod = [vp, vp, vp, vp, i64, i64, ci, ci, ci, vp]
+    for name in ("aqlm_gemv", "aqlm_gemm"):
+        getattr(lib, name).argtypes = prod
+        getattr(lib, name).restype = ci
+    lib.aqlm_gemv_variant.argtypes = [ci] + prod
+    lib.aqlm_gemv_variant.restype = ci
+    lib.aqlm_variant_supported.argtypes = [ci, vp, vp, vp, vp, i64, i64, ci, ci, ci]
+    lib.aqlm_variant_supported.restype = ci
+    lib.aqlm_selected_variant.argtypes = [ci, vp, vp, vp, vp, i64, i64, ci, ci, ci]
+    lib.aqlm_selected_variant.restype = ci
+    lib.aqlm_dequantize.argtypes = [vp, vp, vp, ci, i64, i64, ci, ci, vp]
+    lib.aqlm_dequantize.restype = ci
+    lib.aqlm_bits_per_weight.argtypes = [ci, ci, ci]
+    lib.aqlm_bits_per_weight.restype = ctypes.c_double
+    lib.aqlm_codes_bytes.argtypes = [i64, i64, ci, ci]
+    lib.aqlm_codes_bytes.restype = i64
+    lib.aqlm_codebooks_bytes.argtypes = [ci, ci]
+    lib.aqlm_codebooks_bytes.restype = i64
+    for name in ("aqlm_version", "aqlm_last_error"):
+        getattr(lib, name).argtypes = []
+        getattr(lib, name).restype = ctypes.c_char_p
+    lib.aqlm_status_string.argtypes = [ci]
+    lib.aqlm_status_string.restype = ctypes.c_char_p
+    lib.aqlm_variant_name.argtypes = [ci]
+    lib.aqlm_variant_name.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        lib = _load()
+        detail = lib.aqlm_last_error().decode() if status == 3 else ""
+        raise AqlmError(status, f"{what}: {lib.aqlm_status_string(status).decode()}"
+                                f"{' (' + detail + ')' if detail else ''}")
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _bits_of(codes) -> int:
+    torch = _torch()
+    if codes.dtype == torch.uint8:
+        return 8
+    if codes.dtype in (torch.int16, getattr(torch, "uint16", torch.int16)):
+        return 16
+    raise TypeError("codes must be uint8 (8-bit codes) or int16/uint16 (16-bit codes)")
+
+
+def _prep(codes, codebooks, x, K, B):
+    torch = _torch()
+    if codes.dim() != 3:
+        raise ValueError("codes must be [out][in/8][K]")
+    Bc = _bits_of(codes)
+    K = codes.shape[2] if K is None else int(K)
+    B = Bc if B is None else int(B)
+    if B != Bc or K != codes.shape[2]:
+        raise ValueError("K/B do not match the codes tensor")
+    if codebooks.dtype != torch.float16 or tuple(codebooks.shape) != (K, 1 << B, 8):
+        raise ValueError(f"codebooks must be float16 [{K}][{1 << B}][8]")
+    if x.dtype != torch.float16:
+        raise TypeError("x must be float16")
+    x2 = x.unsqueeze(0) if x.dim() == 1 else x
+    if x2.dim() != 2 or x2.shape[1] != codes.shape[1] * 8:
+        raise ValueError("x must be [batch][in] with in = 8 * codes.shape[1]")
+    for t, n in ((codes, "codes"), (codebooks, "codebooks"), (x2, "x")):
+        if not t.is_cuda:
+            raise ValueError(f"{n} must be a device tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{n} must be contiguous")
+    return K, B, x2
+
+
+def _stream():
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _product(fn_name, codes, codebooks, x, K=None, B=None, out=None, variant=None):
+    torch = _torch()
+    lib = _load()
+    K, B, x2 = _prep(codes, codebooks, x, K, B)
+    out_f, in_f, batch = codes.shape[0], codes.shape[1] * 8, x2.shape[0]
+    y = out if out is not None else torch.empty((batch, out_f), dtype=torch.float16,
+                                                 device=codes.device)
+    if y.dtype != torch.float16 or tuple(y.shape) != (batch, out_f) or not y.is_contiguous():
+        raise ValueError("out must be a contiguous float16 [batch][out] tensor")
+    args = (codes.data_ptr(), codebooks.data_ptr(), x2.data_ptr(), y.data_ptr(), out_f, in_f,
+            K, B, batch, _stream())
+    if variant is None:
+        _check(getattr(lib, fn_name)(*args), fn_name)
+    else:
+        v = VARIANTS[variant] if isinstance(variant, str) else int(variant)
+        _check(lib.aqlm_gemv_variant(v, *args), f"aqlm_gemv_variant({variant})")
+    return y if x.dim() == 2 else y[0]
+
+
+def gemv(codes, codebooks, x, K=None, B=None, out=None):
+    """y = W x (token generation path: gather / lookup-table kernels)."""
+    return _product("aqlm_gemv", codes, codebooks, x, K, B, out)
+
+
+def gemm(codes, codebooks, x, K=None, B=None, out=None):
+    """Y = X W^T; for batch >= 16 decodes to fp16 and runs on the matrix cores."""
+    return _product("aqlm_gemm", codes, codebooks, x, K, B, out)
+
+
+def gemv_variant(variant, codes, codebooks, x, K=None, B=None, out=None):
+    """The product with a named kernel variant ('generic', 'lds', 'lut', 'l2', 'mfma')."""
+    return _product(None, codes, codebooks, x, K, B, out, variant=variant)
+
+
+def variant_supported(variant, codes, codebooks, x, K=None, B=None) -> bool:
+    torch = _torch()
+    lib = _load()
+    K, B, x2 = _prep(codes, codebooks, x, K, B)
+    v = VARIANTS[variant] if isinstance(variant, str) else int(variant)
+    y = torch.empty((x2.shape[0], codes.shape[0]), dtype=torch.float16, device=codes.device)
+    return bool(lib.aqlm_variant_supported(v, codes.data_ptr(), codebooks.data_ptr(),
+                                           x2.data_ptr(), y.data_ptr(), codes.shape[0],
+                                           codes.shape[1] * 8, K, B, x2.shape[0]))
+
+
+def selected_variant(codes, codebooks, x, gemm: bool = False, K=None, B=None) -> str:
+    """Name of the kernel aqlm_gemv (or aqlm_gemm) would run for these tensors."""
+    torch = _torch()
+    lib = _load()
+    K, B, x2 = _prep(codes, codebooks, x, K, B)
+    y = torch.empty((x2.shape[0], codes.shape[0]), dtype=torch.float16, device=codes.device)
+    v = lib.aqlm_selected_variant(1 if gemm else 0, codes.data_ptr(), codebooks.data_ptr(),
+                                  x2.data_ptr(), y.data_ptr(), codes.shape[0], codes.shape[1] * 8,
+                                  K, B, x2.shape[0])
+    return lib.aqlm_variant_name(v).decode()
+
+
+def dequantize(codes, codebooks, K=None, B=None, dtype=None, out=None):
+    """Dense W [out][in]: float32 (the exact fp32 fold) or float16 (rounded once)."""
+    torch = _torch()
+    lib = _load()
+    dtype = torch.float32 if dtype is None else dtype
+    if dtype not in (torch.float32, torch.float16):
+        raise TypeError("dtype must be float32 or float16")
+    dummy_x = torch.empty((1, codes.shape[1] * 8), dtype=torch.float16, device=codes.device)
+    K, B, _ = _prep(codes, codebooks, dummy_x, K, B)
+    out_f, in_f = codes.shape[0], codes.shape[1] * 8
+    W = out if out is not None else torch.empty((out_f, in_f), dtype=dtype, device=codes.device)
+    if W.dtype != dtype or tuple(W.shape) != (out_f, in_f) or not W.is_contiguous():
+        raise ValueError("out must be a contiguous [out][in] tensor of the requested dtype")
+    _check(lib.aqlm_dequantize(codes.data_ptr(), codebooks.data_ptr(), W.data_ptr(),
+                               1 if dtype == torch.float16 else 0, out_f, in_f, K, B, _stream()),
+           "aqlm_dequantize")
+    return W
+
+
+def bits_per_weight(K: int, B: int, group: int = 8) -> float:
+    return _load().aqlm_bits_per_weight(K, B, group)
+
+
+def codes_bytes(out_features: int, in_features: int, K: int, B: int) -> int:
+    return _load().aqlm_codes_bytes(out_features, in_features, K, B)
+
+
+def codebooks_bytes(K: int, B: int) -> int:
+    return _load().aqlm_codebooks_bytes(K, B)
+
+
+def version() -> str:
+    return _load().aqlm_version().decode()

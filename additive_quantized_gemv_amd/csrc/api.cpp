@@ -1,0 +1,312 @@
+// C ABI of libaqlm_mi355x: argument checks, kernel choice, launch, error mapping.
+// The operation and layouts are documented in include/aqlm_mi355x.h.
+#include "aqlm_mi355x.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <utility>
+
+#include "kernels.hpp"
+
+namespace {
+
+constexpr int kGroup = 8;
+constexpr int kMfmaMinBatchDefault = 16;
+
+thread_local char g_last_error[256] = "";
+
+void set_error(const char *what, hipError_t e) {
+    std::snprintf(g_last_error, sizeof(g_last_error), "%s: %s", what, hipGetErrorString(e));
+}
+
+bool log_enabled() {
+    static const bool on = [] {
+        const char *v = std::getenv("AQLM_LOG");
+        return v && *v && std::strcmp(v, "0") != 0;
+    }();
+    return on;
+}
+
+int forced_variant() {
+    const char *v = std::getenv("AQLM_FORCE_VARIANT");
+    if (!v || !*v) return AQLM_VARIANT_AUTO;
+    if (!std::strcmp(v, "generic")) return AQLM_VARIANT_GENERIC;
+    if (!std::strcmp(v, "lds")) return AQLM_VARIANT_LDS;
+    if (!std::strcmp(v, "lut")) return AQLM_VARIANT_LUT;
+    if (!std::strcmp(v, "l2")) return AQLM_VARIANT_L2;
+    if (!std::strcmp(v, "mfma")) return AQLM_VARIANT_MFMA;
+    return AQLM_VARIANT_AUTO;
+}
+
+int mfma_min_batch() {
+    const char *v = std::getenv("AQLM_MFMA_MIN_BATCH");
+    if (!v || !*v) return kMfmaMinBatchDefault;
+    const int n = std::atoi(v);
+    return n >= 1 ? n : kMfmaMinBatchDefault;
+}
+
+// [a, a+na) and [b, b+nb) overlap?
+bool overlaps(const void *a, int64_t na, const void *b, int64_t nb) {
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return x < y + uint64_t(nb) && y < x + uint64_t(na);
+}
+
+bool mul_ok(int64_t a, int64_t b, int64_t *r) { return !__builtin_mul_overflow(a, b, r); }
+
+struct Sizes {
+    int64_t codes, codebooks, x, y;
+};
+
+// Validates shape arguments and computes byte sizes; false on any error.
+bool check_shape(int64_t out, int64_t in, int K, int B, int64_t batch, Sizes *s) {
+    if (out < 1 || in < 1 || batch < 1) return false;
+    if (in % kGroup) return false;
+    if (K < 1 || K > 8) return false;
+    if (B != 8 && B != 16) return false;
+    int64_t t;
+    if (!mul_ok(out, in / kGroup, &t) || !mul_ok(t, int64_t(K) * (B / 8), &s->codes)) return false;
+    s->codebooks = int64_t(K) * (int64_t(1) << B) * kGroup * 2;
+    if (!mul_ok(batch, in, &t) || !mul_ok(t, 2, &s->x)) return false;
+    if (!mul_ok(batch, out, &t) || !mul_ok(t, 2, &s->y)) return false;
+    return true;
+}
+
+aqlm_status_t check_args(const void *codes, const void *cb, const void *x, const void *y,
+                         int64_t out, int64_t in, int K, int B, int batch, Sizes *s) {
+    if (!codes || !cb || !x || !y) return AQLM_ERR_INVALID_ARGUMENT;
+    if (!check_shape(out, in, K, B, batch, s)) return AQLM_ERR_INVALID_ARGUMENT;
+    // element alignment: 2-byte codes for B = 16, fp16 data everywhere
+    const uintptr_t a = reinterpret_cast<uintptr_t>(cb) | reinterpret_cast<uintptr_t>(x) |
+                        reinterpret_cast<uintptr_t>(y) |
+                        (B == 16 ? reinterpret_cast<uintptr_t>(codes) : 0);
+    if (a & 1u) return AQLM_ERR_INVALID_ARGUMENT;
+    if (overlaps(y, s->y, codes, s->codes) || overlaps(y, s->y, cb, s->codebooks) ||
+        overlaps(y, s->y, x, s->x))
+        return AQLM_ERR_INVALID_ARGUMENT;
+    return AQLM_OK;
+}
+
+aqlm::Problem make_problem(const void *codes, const void *cb, const void *x, void *y, int64_t out,
+                           int64_t in, int K, int B, int batch, void *stream) {
+    return aqlm::Problem{codes, cb, x, y, out, in, K, B, batch,
+                         static_cast<hipStream_t>(stream)};
+}
+
+bool supported(int variant, const aqlm::Problem &p) {
+    switch (variant) {
+        case AQLM_VARIANT_GENERIC: return true;
+        case AQLM_VARIANT_LDS: return p.B == 8 && aqlm::gather_supported(p);
+        case AQLM_VARIANT_LUT: return aqlm::lut_supported(p);
+        case AQLM_VARIANT_L2: return p.B == 16 && aqlm::gather_supported(p);
+        case AQLM_VARIANT_MFMA: return aqlm::mfma_supported(p);
+        default: return false;
+    }
+}
+
+int choose(bool gemm, const aqlm::Problem &p) {
+    const int forced = forced_variant();
+    if (forced != AQLM_VARIANT_AUTO && supported(forced, p)) return forced;
+    if (gemm && p.batch >= mfma_min_batch() && supported(AQLM_VARIANT_MFMA, p))
+        return AQLM_VARIANT_MFMA;
+    if (supported(AQLM_VARIANT_LUT, p)) return AQLM_VARIANT_LUT;
+    if (p.B == 8 && supported(AQLM_VARIANT_LDS, p)) return AQLM_VARIANT_LDS;
+    if (p.B == 16 && supported(AQLM_VARIANT_L2, p)) return AQLM_VARIANT_L2;
+    return AQLM_VARIANT_GENERIC;
+}
+
+// Split-slice partial sums of the lookup-table kernel live in one workspace per
+// (device, stream), grown on demand and kept until the process exits.  Calls on
+// one stream are ordered, so they can share it.
+struct Workspace {
+    void *ptr = nullptr;
+    size_t bytes = 0;
+};
+std::mutex g_ws_mutex;
+std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
+
+hipError_t get_workspace(hipStream_t stream, size_t bytes, void **out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    std::lock_guard<std::mutex> lock(g_ws_mutex);
+    Workspace &w = g_ws[std::make_pair(dev, stream)];
+    if (w.bytes < bytes) {
+        if (w.ptr) {
+            e = hipStreamSynchronize(stream);  // earlier launches may still use it
+            if (e != hipSuccess) return e;
+            (void)hipFree(w.ptr);
+            w.ptr = nullptr;
+            w.bytes = 0;
+        }
+        size_t nb = bytes < (size_t(1) << 20) ? (size_t(1) << 20) : bytes;
+        e = hipMalloc(&w.ptr, nb);
+        if (e != hipSuccess) return e;
+        e = hipMemsetAsync(w.ptr, 0, nb, stream);  // counters start at zero
+        if (e != hipSuccess) return e;
+        w.bytes = nb;
+    }
+    *out = w.ptr;
+    return hipSuccess;
+}
+
+aqlm_status_t run(int variant, const aqlm::Problem &p) {
+    hipError_t e = hipSuccess;
+    if (log_enabled())
+        std::fprintf(stderr, "[aqlm] %s out=%lld in=%lld K=%d B=%d batch=%d\n",
+                     aqlm_variant_name(variant), (long long)p.out, (long long)p.in, p.K, p.B,
+                     p.batch);
+    switch (variant) {
+        case AQLM_VARIANT_LDS:
+        case AQLM_VARIANT_L2: e = aqlm::launch_gather(p); break;
+        case AQLM_VARIANT_LUT: {
+            void *ws = nullptr;
+            e = get_workspace(p.stream, aqlm::lut_workspace_bytes(p), &ws);
+            if (e == hipSuccess) e = aqlm::launch_lut(p, ws);
+            break;
+        }
+        case AQLM_VARIANT_MFMA: e = aqlm::launch_mfma(p); break;
+        default: e = aqlm::launch_generic(p); break;
+    }
+    if (e != hipSuccess) {
+        set_error(aqlm_variant_name(variant), e);
+        return AQLM_ERR_HIP;
+    }
+    return AQLM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+aqlm_status_t aqlm_gemv(const void *codes, const void *codebooks, const void *x, void *y,
+                        int64_t out_features, int64_t in_features, int K, int B, int batch,
+                        void *stream) {
+    Sizes s;
+    aqlm_status_t st = check_args(codes, codebooks, x, y, out_features, in_features, K, B, batch, &s);
+    if (st != AQLM_OK) return st;
+    const aqlm::Problem p = make_problem(codes, codebooks, x, y, out_features, in_features, K, B,
+                                         batch, stream);
+    return run(choose(false, p), p);
+}
+
+aqlm_status_t aqlm_gemm(const void *codes, const void *codebooks, const void *x, void *y,
+                        int64_t out_features, int64_t in_features, int K, int B, int batch,
+                        void *stream) {
+    Sizes s;
+    aqlm_status_t st = check_args(codes, codebooks, x, y, out_features, in_features, K, B, batch, &s);
+    if (st != AQLM_OK) return st;
+    const aqlm::Problem p = make_problem(codes, codebooks, x, y, out_features, in_features, K, B,
+                                         batch, stream);
+    return run(choose(true, p), p);
+}
+
+aqlm_status_t aqlm_gemv_variant(int variant, const void *codes, const void *codebooks,
+                                const void *x, void *y, int64_t out_features,
+                                int64_t in_features, int K, int B, int batch, void *stream) {
+    Sizes s;
+    aqlm_status_t st = check_args(codes, codebooks, x, y, out_features, in_features, K, B, batch, &s);
+    if (st != AQLM_OK) return st;
+    const aqlm::Problem p = make_problem(codes, codebooks, x, y, out_features, in_features, K, B,
+                                         batch, stream);
+    if (variant == AQLM_VARIANT_AUTO) return run(choose(false, p), p);
+    if (!supported(variant, p)) return AQLM_ERR_UNSUPPORTED;
+    return run(variant, p);
+}
+
+int aqlm_variant_supported(int variant, const void *codes, const void *codebooks, const void *x,
+                           const void *y, int64_t out_features, int64_t in_features, int K, int B,
+                           int batch) {
+    Sizes s;
+    if (check_args(codes, codebooks, x, y, out_features, in_features, K, B, batch, &s) != AQLM_OK)
+        return 0;
+    const aqlm::Problem p = make_problem(codes, codebooks, x, const_cast<void *>(y), out_features,
+                                         in_features, K, B, batch, nullptr);
+    if (variant == AQLM_VARIANT_AUTO) return 1;
+    return supported(variant, p) ? 1 : 0;
+}
+
+int aqlm_selected_variant(int gemm, const void *codes, const void *codebooks, const void *x,
+                          const void *y, int64_t out_features, int64_t in_features, int K, int B,
+                          int batch) {
+    Sizes s;
+    if (check_args(codes, codebooks, x, y, out_features, in_features, K, B, batch, &s) != AQLM_OK)
+        return -1;
+    const aqlm::Problem p = make_problem(codes, codebooks, x, const_cast<void *>(y), out_features,
+                                         in_features, K, B, batch, nullptr);
+    return choose(gemm != 0, p);
+}
+
+aqlm_status_t aqlm_dequantize(const void *codes, const void *codebooks, void *W, int w_dtype,
+                              int64_t out_features, int64_t in_features, int K, int B,
+                              void *stream) {
+    if (!codes || !codebooks || !W) return AQLM_ERR_INVALID_ARGUMENT;
+    if (w_dtype != 0 && w_dtype != 1) return AQLM_ERR_INVALID_ARGUMENT;
+    Sizes s;
+    if (!check_shape(out_features, in_features, K, B, 1, &s)) return AQLM_ERR_INVALID_ARGUMENT;
+    int64_t wbytes;
+    if (!mul_ok(out_features, in_features, &wbytes) || !mul_ok(wbytes, w_dtype ? 2 : 4, &wbytes))
+        return AQLM_ERR_INVALID_ARGUMENT;
+    const uintptr_t a = reinterpret_cast<uintptr_t>(codebooks) |
+                        (B == 16 ? reinterpret_cast<uintptr_t>(codes) : 0);
+    if ((a & 1u) || (reinterpret_cast<uintptr_t>(W) & (w_dtype ? 1u : 3u)))
+        return AQLM_ERR_INVALID_ARGUMENT;
+    if (overlaps(W, wbytes, codes, s.codes) || overlaps(W, wbytes, codebooks, s.codebooks))
+        return AQLM_ERR_INVALID_ARGUMENT;
+    const aqlm::Problem p = make_problem(codes, codebooks, nullptr, nullptr, out_features,
+                                         in_features, K, B, 1, stream);
+    const hipError_t e = aqlm::launch_dequantize(p, W, w_dtype);
+    if (e != hipSuccess) {
+        set_error("dequantize", e);
+        return AQLM_ERR_HIP;
+    }
+    return AQLM_OK;
+}
+
+double aqlm_bits_per_weight(int K, int B, int group) {
+    if (group < 1) return 0.0;
+    return double(K) * double(B) / double(group);
+}
+
+int64_t aqlm_codes_bytes(int64_t out_features, int64_t in_features, int K, int B) {
+    Sizes s;
+    if (!check_shape(out_features, in_features, K, B, 1, &s)) return -1;
+    return s.codes;
+}
+
+int64_t aqlm_codebooks_bytes(int K, int B) {
+    if (K < 1 || K > 8 || (B != 8 && B != 16)) return -1;
+    return int64_t(K) * (int64_t(1) << B) * kGroup * 2;
+}
+
+const char *aqlm_status_string(aqlm_status_t status) {
+    switch (status) {
+        case AQLM_OK: return "ok";
+        case AQLM_ERR_INVALID_ARGUMENT: return "invalid argument";
+        case AQLM_ERR_UNSUPPORTED: return "variant does not support these arguments";
+        case AQLM_ERR_HIP: return "HIP error";
+        default: return "unknown status";
+    }
+}
+
+const char *aqlm_variant_name(int variant) {
+    switch (variant) {
+        case AQLM_VARIANT_AUTO: return "auto";
+        case AQLM_VARIANT_GENERIC: return "generic";
+        case AQLM_VARIANT_LDS: return "lds";
+        case AQLM_VARIANT_LUT: return "lut";
+        case AQLM_VARIANT_L2: return "l2";
+        case AQLM_VARIANT_MFMA: return "mfma";
+        default: return "unknown";
+    }
+}
+
+const char *aqlm_version(void) { return "0.1.0"; }
+
+const char *aqlm_last_error(void) { return g_last_error; }
+
+}  // extern "C"

@@ -1,0 +1,120 @@
+// Generic additive-quantized GEMV and the dequantize kernel (gfx950).
+//
+// Decode rule (page "AQLM (Additive Quantization for LLMs)", section "Niveau
+// intermediaire"): group j of row o is the sum of one 8-wide fp16 vector from
+// each of the K codebooks.  Here the sum is the fp32 left fold in codebook
+// order, which is also what the dense dequantized W holds.
+//
+// The generic kernel is the always-correct fallback: one wave per output row,
+// lanes striding over the row's groups, codebooks read through the caches,
+// fp32 accumulation, DPP wave reduction, one fp16 store per (token, row).
+#include "device_common.hpp"
+#include "kernels.hpp"
+
+namespace aqlm {
+namespace {
+
+constexpr int kGenericTokens = 8;  // tokens accumulated per pass over a row
+
+__device__ __forceinline__ uint32_t read_code(const void *codes, int B, int64_t idx) {
+    return B == 8 ? static_cast<uint32_t>(static_cast<const uint8_t *>(codes)[idx])
+                  : static_cast<uint32_t>(static_cast<const uint16_t *>(codes)[idx]);
+}
+
+// Fold the K codebook vectors of group (o, j) into w[0..7] (fp32, codebook order).
+__device__ __forceinline__ void decode_group(const void *codes, const uint16_t *cb, int K, int B,
+                                             int64_t G, int64_t o, int64_t j, float w[8]) {
+    const int64_t entries = int64_t(1) << B;
+    const int64_t base = (o * G + j) * K;
+    for (int k = 0; k < K; ++k) {
+        const uint32_t c = read_code(codes, B, base + k);
+        const uint16_t *v = cb + (k * entries + c) * kGroup;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const float f = h2f(v[t]);
+            w[t] = (k == 0) ? f : w[t] + f;
+        }
+    }
+}
+
+__global__ void __launch_bounds__(256)
+generic_kernel(const void *__restrict__ codes, const uint16_t *__restrict__ cb,
+               const uint16_t *__restrict__ x, uint16_t *__restrict__ y, int64_t out,
+               int64_t in, int K, int B, int batch) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t o = int64_t(blockIdx.x) * (blockDim.x / kWave) + (threadIdx.x / kWave);
+    if (o >= out) return;
+    const int64_t G = in / kGroup;
+    for (int b0 = 0; b0 < batch; b0 += kGenericTokens) {
+        const int nb = min(kGenericTokens, batch - b0);
+        float acc[kGenericTokens];
+#pragma unroll
+        for (int b = 0; b < kGenericTokens; ++b) acc[b] = 0.0f;
+        for (int64_t j = lane; j < G; j += kWave) {
+            float w[8];
+            decode_group(codes, cb, K, B, G, o, j, w);
+#pragma unroll
+            for (int b = 0; b < kGenericTokens; ++b) {
+                if (b < nb) {
+                    const uint16_t *xv = x + (b0 + b) * in + j * kGroup;
+#pragma unroll
+                    for (int t = 0; t < 8; ++t) acc[b] = fmaf(w[t], h2f(xv[t]), acc[b]);
+                }
+            }
+        }
+#pragma unroll
+        for (int b = 0; b < kGenericTokens; ++b) {
+            if (b < nb) {
+                const float s = wave_sum(acc[b]);
+                if (lane == 0) y[(b0 + b) * out + o] = f2h_bits(s);
+            }
+        }
+    }
+}
+
+__global__ void __launch_bounds__(256)
+dequantize_kernel(const void *__restrict__ codes, const uint16_t *__restrict__ cb, void *W,
+                  int64_t out, int64_t in, int K, int B, int w_fp16) {
+    const int64_t G = in / kGroup;
+    const int64_t n = out * G;
+    for (int64_t g = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; g < n;
+         g += int64_t(gridDim.x) * blockDim.x) {
+        const int64_t o = g / G, j = g - o * G;
+        float w[8];
+        decode_group(codes, cb, K, B, G, o, j, w);
+        if (w_fp16) {
+            uint16_t *dst = static_cast<uint16_t *>(W) + g * kGroup;
+#pragma unroll
+            for (int t = 0; t < 8; ++t) dst[t] = f2h_bits(w[t]);
+        } else {
+            float *dst = static_cast<float *>(W) + g * kGroup;
+#pragma unroll
+            for (int t = 0; t < 8; ++t) dst[t] = w[t];
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_generic(const Problem &p) {
+    const int waves_per_block = 4;
+    const int64_t blocks = (p.out + waves_per_block - 1) / waves_per_block;
+    hipLaunchKernelGGL(generic_kernel, dim3(static_cast<unsigned>(blocks)),
+                       dim3(waves_per_block * kWave), 0, p.stream, p.codes,
+                       static_cast<const uint16_t *>(p.codebooks),
+                       static_cast<const uint16_t *>(p.x), static_cast<uint16_t *>(p.y), p.out,
+                       p.in, p.K, p.B, p.batch);
+    return hipGetLastError();
+}
+
+hipError_t launch_dequantize(const Problem &p, void *W, int w_fp16) {
+    const int64_t n = p.out * (p.in / kGroup);
+    int64_t blocks = (n + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    hipLaunchKernelGGL(dequantize_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
+                       p.stream, p.codes, static_cast<const uint16_t *>(p.codebooks), W, p.out,
+                       p.in, p.K, p.B, w_fp16);
+    return hipGetLastError();
+}
+
+}  // namespace aqlm

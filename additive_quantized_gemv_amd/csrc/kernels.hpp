@@ -1,0 +1,43 @@
+// Host-visible launchers of the gfx950 kernels (implemented in the *.hip files).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace aqlm {
+
+struct Problem {
+    const void *codes;
+    const void *codebooks;
+    const void *x;
+    void *y;
+    int64_t out;
+    int64_t in;
+    int K;
+    int B;
+    int batch;
+    hipStream_t stream;
+};
+
+// Every launcher returns the hipError_t of its launch (hipSuccess when queued).
+
+// Generic: any K in 1..8, B in {8,16}, any batch, any in % 8 == 0.
+hipError_t launch_generic(const Problem &p);
+
+// Dense W (fp32 when w_fp16 == 0, fp16 otherwise).
+hipError_t launch_dequantize(const Problem &p, void *W, int w_fp16);
+
+// Gather kernels: B = 8 (codebooks in LDS) or B = 16 (codebook through L2), batch <= 8.
+bool gather_supported(const Problem &p);
+hipError_t launch_gather(const Problem &p);
+
+// Lookup-table kernel for K = 2, B = 8, batch 1 (split over input slices).
+bool lut_supported(const Problem &p);
+size_t lut_workspace_bytes(const Problem &p);
+hipError_t launch_lut(const Problem &p, void *workspace);
+
+// Decode-to-fp16 fragments + MFMA, K in {1,2}, B in {8,16}, any batch.
+bool mfma_supported(const Problem &p);
+hipError_t launch_mfma(const Problem &p);
+
+}  // namespace aqlm

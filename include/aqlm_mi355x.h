@@ -1,0 +1,136 @@
+/*
+ * aqlm_mi355x.h -- C ABI of libaqlm_mi355x: additive-quantized matrix-vector and
+ * small-batch matrix-matrix products on AMD Instinct MI355X (gfx950).
+ *
+ * The operation (page "AQLM (Additive Quantization for LLMs)", section
+ * "Niveau intermediaire"; groups of 8 along the input axis from page
+ * "AQLM -- ...", section "Kak eto rabotaet tekhnicheski?"):
+ *
+ *   W is never stored dense.  Row o, input group j (columns 8j .. 8j+7) is
+ *       W[o][8j+t] = C_0[i_0(o,j)][t] + C_1[i_1(o,j)][t] + ... + C_{K-1}[i_{K-1}(o,j)][t]
+ *   with K codebooks of 2^B entries of 8 fp16 values each, and the product is
+ *       Y[b][o] = sum_i W[o][i] * X[b][i].
+ *   Storage costs K*B/8 bits per weight (same section, bitrate formula):
+ *   scheme 1x16 (K=1, B=16) and 2x8 (K=2, B=8) both give 2 bits per weight.
+ *
+ * Layouts (all tensors dense, row-major, in device memory, owned by the caller):
+ *   codes     [out_features][in_features/8][K]   uint8 when B = 8, 16-bit unsigned
+ *                                                (little-endian) when B = 16
+ *   codebooks [K][2^B][8]                        fp16 (IEEE binary16)
+ *   x         [batch][in_features]               fp16
+ *   y         [batch][out_features]              fp16, written (round to nearest even)
+ *   W         [out_features][in_features]        fp32 or fp16 (aqlm_dequantize only)
+ *
+ * Numerics: products are accumulated in fp32.  The decoded weight is the fp32
+ * left fold C_0 + C_1 + ... in codebook order; aqlm_dequantize writes it exactly
+ * (fp32) or rounded once to fp16 (nearest even).  The batched (MFMA) path feeds
+ * that fp16 rounding of W to the matrix cores.
+ *
+ * Calls are asynchronous: work is enqueued on `stream` (a hipStream_t; NULL is
+ * the default stream) and the call returns before it finishes.  The library
+ * keeps no pointer after a call returns, allocates no memory and holds no
+ * state; calls on different streams may run concurrently.
+ *
+ * Errors: argument errors are reported synchronously, before any device work:
+ * a null pointer, a size < 1, in_features not a multiple of 8, K outside
+ * 1..8, B not 8 or 16, sizes whose byte counts overflow int64, or an output
+ * buffer that overlaps an input.  A launch failure (no device, no gfx950 code
+ * object) returns AQLM_ERR_HIP; aqlm_last_error() then gives the HIP message.
+ * Tuned kernels that cannot take a shape (rows not a multiple of 16 bytes,
+ * unaligned pointers, too much LDS) are silently replaced by the generic
+ * kernel; AQLM_ERR_UNSUPPORTED comes only from aqlm_gemv_variant.
+ */
+#ifndef AQLM_MI355X_H
+#define AQLM_MI355X_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    AQLM_OK = 0,
+    AQLM_ERR_INVALID_ARGUMENT = 1,
+    AQLM_ERR_UNSUPPORTED = 2,
+    AQLM_ERR_HIP = 3
+} aqlm_status_t;
+
+/* Kernel variants, for aqlm_gemv_variant and aqlm_variant_name. */
+typedef enum {
+    AQLM_VARIANT_AUTO = 0,    /* library's choice (what aqlm_gemv / aqlm_gemm do)          */
+    AQLM_VARIANT_GENERIC = 1, /* any K in 1..8, B in {8,16}, any batch and shape             */
+    AQLM_VARIANT_LDS = 2,     /* B = 8: codebooks staged in LDS, gather + fp32 dot, batch<=8 */
+    AQLM_VARIANT_LUT = 3,     /* K = 2, B = 8, batch 1: per-group codebook.x lookup tables   */
+    AQLM_VARIANT_L2 = 4,      /* B = 16: codebook gathered through L2, batch <= 8            */
+    AQLM_VARIANT_MFMA = 5     /* decode to fp16 fragments + fp16 matrix cores, any batch     */
+} aqlm_variant_t;
+
+/*
+ * y = W x for a batch of activation rows (token generation).  Picks a
+ * gather/lookup kernel for the (K, B, batch, shape); never the matrix cores.
+ * Arguments: device pointers as laid out above; out_features, in_features >= 1
+ * with in_features % 8 == 0; K in 1..8; B in {8, 16}; batch >= 1.
+ */
+aqlm_status_t aqlm_gemv(const void *codes, const void *codebooks, const void *x, void *y,
+                        int64_t out_features, int64_t in_features, int K, int B, int batch,
+                        void *stream);
+
+/*
+ * Same product and arguments as aqlm_gemv; for batch >= 16 it uses the
+ * dequantize-to-fp16 + MFMA kernel, below that it behaves as aqlm_gemv.
+ */
+aqlm_status_t aqlm_gemm(const void *codes, const void *codebooks, const void *x, void *y,
+                        int64_t out_features, int64_t in_features, int K, int B, int batch,
+                        void *stream);
+
+/*
+ * Same product with a named kernel variant (benchmarks, A/B tests).  Returns
+ * AQLM_ERR_UNSUPPORTED, with nothing launched, if that variant cannot take
+ * the arguments (see aqlm_variant_supported).
+ */
+aqlm_status_t aqlm_gemv_variant(int variant, const void *codes, const void *codebooks,
+                                const void *x, void *y, int64_t out_features,
+                                int64_t in_features, int K, int B, int batch, void *stream);
+
+/* 1 if aqlm_gemv_variant(variant, ...) would run for these arguments, else 0. */
+int aqlm_variant_supported(int variant, const void *codes, const void *codebooks, const void *x,
+                           const void *y, int64_t out_features, int64_t in_features, int K,
+                           int B, int batch);
+
+/* The variant aqlm_gemv (gemm = 0) or aqlm_gemm (gemm = 1) would run. */
+int aqlm_selected_variant(int gemm, const void *codes, const void *codebooks, const void *x,
+                          const void *y, int64_t out_features, int64_t in_features, int K,
+                          int B, int batch);
+
+/*
+ * Dense W [out][in] from codes and codebooks: w_dtype 0 writes the fp32 fold
+ * exactly, 1 writes it rounded once to fp16 (nearest even).  Same argument
+ * rules as aqlm_gemv; W must not overlap the inputs.
+ */
+aqlm_status_t aqlm_dequantize(const void *codes, const void *codebooks, void *W, int w_dtype,
+                              int64_t out_features, int64_t in_features, int K, int B,
+                              void *stream);
+
+/* K*B/group bits per weight (bitrate formula of the decode section). */
+double aqlm_bits_per_weight(int K, int B, int group);
+
+/* Bytes of codes for an out x in matrix: out * (in/8) * K * B/8; -1 on bad arguments. */
+int64_t aqlm_codes_bytes(int64_t out_features, int64_t in_features, int K, int B);
+
+/* Bytes of codebooks: K * 2^B * 8 * 2; -1 on bad arguments. */
+int64_t aqlm_codebooks_bytes(int K, int B);
+
+/* Static strings; never NULL. */
+const char *aqlm_status_string(aqlm_status_t status);
+const char *aqlm_variant_name(int variant);
+const char *aqlm_version(void);
+
+/* Text of the last HIP error seen by this thread's calls ("" if none). */
+const char *aqlm_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* AQLM_MI355X_H */

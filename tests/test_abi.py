@@ -1,0 +1,134 @@
+"""C-ABI checks that need no GPU: the library loads, exports every declared
+symbol, and rejects bad arguments before touching the device."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "aqlm_mi355x.h")
+GOLDEN = os.path.join(ROOT, "tests", "golden")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import additive_quantized_gemv_amd as aq
+    if not os.path.exists(aq.library_path()):
+        from additive_quantized_gemv_amd import build
+        build.build()
+    return aq._load()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(aqlm_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared_functions()
+    assert {"aqlm_gemv", "aqlm_gemm", "aqlm_dequantize", "aqlm_gemv_variant"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_bitrate_matches_worked_examples(lib):
+    with open(os.path.join(GOLDEN, "bitrate_examples.txt")) as f:
+        rows = [ln.split() for ln in f if ln.strip() and not ln.startswith("#")]
+    for K, entries, g, bits, *_ in rows:
+        B = int(np.log2(int(entries)))
+        assert lib.aqlm_bits_per_weight(int(K), B, int(g)) == float(bits)
+
+
+def test_sizes(lib):
+    assert lib.aqlm_codes_bytes(11008, 4096, 2, 8) == 11272192
+    assert lib.aqlm_codes_bytes(4096, 4096, 1, 16) == 4194304
+    assert lib.aqlm_codes_bytes(28672, 8192, 1, 16) == 58720256
+    assert lib.aqlm_codes_bytes(10, 12, 2, 8) == -1      # in not a multiple of 8
+    assert lib.aqlm_codes_bytes(10, 16, 9, 8) == -1      # K out of range
+    assert lib.aqlm_codebooks_bytes(2, 8) == 8192
+    assert lib.aqlm_codebooks_bytes(1, 16) == 1 << 20
+    assert lib.aqlm_codebooks_bytes(1, 12) == -1
+
+
+def test_strings(lib):
+    for s in range(4):
+        assert lib.aqlm_status_string(s)
+    names = [lib.aqlm_variant_name(v).decode() for v in range(6)]
+    assert names == ["auto", "generic", "lds", "lut", "l2", "mfma"]
+    assert lib.aqlm_variant_name(99) == b"unknown"
+    assert lib.aqlm_version()
+
+
+# fake, well-separated "device" addresses: validation must fail before any use
+C, CB, X, Y = 0x10000000, 0x20000000, 0x30000000, 0x40000000
+
+
+@pytest.mark.parametrize("args", [
+    (0, CB, X, Y, 16, 64, 2, 8, 1),          # null codes
+    (C, 0, X, Y, 16, 64, 2, 8, 1),           # null codebooks
+    (C, CB, 0, Y, 16, 64, 2, 8, 1),          # null x
+    (C, CB, X, 0, 16, 64, 2, 8, 1),          # null y
+    (C, CB, X, Y, 0, 64, 2, 8, 1),           # out < 1
+    (C, CB, X, Y, 16, 0, 2, 8, 1),           # in < 1
+    (C, CB, X, Y, 16, 60, 2, 8, 1),          # in % 8
+    (C, CB, X, Y, 16, 64, 0, 8, 1),          # K < 1
+    (C, CB, X, Y, 16, 64, 9, 8, 1),          # K > 8
+    (C, CB, X, Y, 16, 64, 2, 4, 1),          # B not 8/16
+    (C, CB, X, Y, 16, 64, 2, 8, 0),          # batch < 1
+    (C, CB, X, Y, 1 << 62, 1 << 40, 2, 8, 1),  # byte counts overflow
+    (C, CB, X, C + 8, 16, 64, 2, 8, 1),      # y overlaps codes
+    (C, CB, X, X, 16, 64, 2, 8, 1),          # y overlaps x
+    (C, CB + 1, X, Y, 16, 64, 2, 8, 1),      # misaligned fp16 codebooks
+    (C + 1, CB, X, Y, 16, 64, 1, 16, 1),     # misaligned 16-bit codes
+])
+def test_invalid_arguments_rejected(lib, args):
+    for fn in (lib.aqlm_gemv, lib.aqlm_gemm):
+        assert fn(*args, None) == 1
+    assert lib.aqlm_gemv_variant(1, *args, None) == 1
+    assert lib.aqlm_variant_supported(1, *args) == 0
+    assert lib.aqlm_selected_variant(0, *args) == -1
+
+
+def test_dequantize_invalid(lib):
+    assert lib.aqlm_dequantize(C, CB, Y, 2, 16, 64, 2, 8, None) == 1    # bad dtype
+    assert lib.aqlm_dequantize(C, CB, C, 0, 16, 64, 2, 8, None) == 1    # W overlaps codes
+    assert lib.aqlm_dequantize(C, CB, Y + 2, 0, 16, 64, 2, 8, None) == 1  # fp32 W misaligned
+    assert lib.aqlm_dequantize(0, CB, Y, 0, 16, 64, 2, 8, None) == 1
+
+
+def test_variant_choice_host_logic(lib):
+    # pointers aligned to 256 B, shapes of the benchmark configurations
+    def sel(gemm, out, in_, K, B, batch):
+        return lib.aqlm_variant_name(
+            lib.aqlm_selected_variant(gemm, C, CB, X, Y, out, in_, K, B, batch)).decode()
+    assert sel(0, 11008, 4096, 2, 8, 1) == "lut"
+    assert sel(0, 4096, 11008, 2, 8, 1) == "lut"
+    assert sel(0, 4096, 4096, 2, 8, 4) == "lds"
+    assert sel(0, 4096, 4096, 1, 16, 1) == "l2"
+    assert sel(0, 8192, 28672, 1, 16, 4) == "l2"
+    assert sel(1, 4096, 4096, 2, 8, 16) == "mfma"
+    assert sel(1, 4096, 4096, 1, 16, 128) == "mfma"
+    assert sel(1, 4096, 4096, 2, 8, 8) == "lds"
+    assert sel(0, 64, 24, 3, 8, 1) == "generic"
+    assert lib.aqlm_variant_supported(3, C, CB, X, Y, 4096, 4096, 1, 16, 1) == 0  # lut needs 2x8
+    assert lib.aqlm_variant_supported(5, C, CB, X, Y, 4096, 4096, 3, 8, 16) == 0  # mfma: K<=2
+
+
+def test_no_device_reports_hip_error(lib):
+    """With no GPU present a valid call fails as AQLM_ERR_HIP, with a message."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present; this checks the no-device path only")
+    assert lib.aqlm_gemv_variant(1, C, CB, X, Y, 16, 64, 2, 8, 1, None) == 3
+    assert lib.aqlm_last_error()
+
+
+def test_python_binding_fails_loudly_without_library(tmp_path, monkeypatch):
+    import additive_quantized_gemv_amd as aq
+    monkeypatch.setattr(aq, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(aq, "_lib", None)
+    with pytest.raises(ImportError):
+        aq._load()

@@ -1,0 +1,249 @@
+"""GPU parity: every kernel variant against the CPU oracle on the same seeded bytes.
+
+Bars (decode rule of page "AQLM (Additive Quantization for LLMs)", section
+"Niveau intermediaire"):
+  * dequantized W: fp32 output equal to the oracle's fp32 fold element by
+    element (+0 == -0); fp16 output bit-equal to the round-to-nearest-even fp16
+    of the oracle's W;
+  * y: for every token b, max_o |y - y_ref| / (max_o |y_ref| + 1e-6) <= 2e-3,
+    y_ref being the oracle's unrounded double result.
+"""
+import numpy as np
+import pytest
+
+from additive_quantized_gemv_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-3
+
+
+@pytest.fixture(scope="module")
+def aq():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import additive_quantized_gemv_amd as aq
+    aq._load()
+    return aq
+
+
+def _dev(p):
+    import torch
+    codes = p["codes"]
+    if codes.dtype == np.uint16:
+        codes = codes.view(np.int16)
+    return (torch.from_numpy(np.ascontiguousarray(codes)).cuda(),
+            torch.from_numpy(np.ascontiguousarray(p["codebooks"])).cuda(),
+            torch.from_numpy(np.ascontiguousarray(p["x"])).cuda())
+
+
+def rel_err(y, yref):
+    y = np.asarray(y, dtype=np.float64)
+    return np.max(np.abs(y - yref), axis=1) / (np.max(np.abs(yref), axis=1) + 1e-6)
+
+
+def check_y(y_t, yref, what):
+    import torch
+    torch.cuda.synchronize()
+    y = y_t.float().cpu().numpy()
+    if y.ndim == 1:
+        y = y[None]
+    assert np.all(np.isfinite(y)), what
+    e = rel_err(y, yref)
+    assert np.all(e <= TOL), f"{what}: max rel err {e.max():.3e}"
+    return e.max()
+
+
+def _variants_for(K, B, batch):
+    v = ["generic", "mfma"]
+    if B == 8:
+        v.append("lds")
+    if B == 16:
+        v.append("l2")
+    if K == 2 and B == 8 and batch == 1:
+        v.append("lut")
+    return v
+
+
+SMALL = [
+    # out, in, K, B, batch, sigma
+    (256, 512, 2, 8, 1, 0.05),      # the tiny 2x8 workload
+    (300, 1024, 2, 8, 1, 0.02),
+    (65, 520, 2, 8, 1, 0.02),       # ragged rows and a partial 64-group slice
+    (17, 4160, 2, 8, 1, 0.02),
+    (1, 64, 2, 8, 1, 0.02),
+    (200, 768, 1, 16, 1, 0.02),
+    (129, 2048, 1, 16, 4, 0.02),
+    (96, 512, 2, 8, 4, 0.02),
+    (96, 512, 2, 8, 3, 0.02),
+    (64, 512, 1, 8, 2, 0.05),
+    (64, 512, 4, 8, 1, 0.02),
+    (64, 512, 8, 8, 8, 0.01),
+    (80, 256, 2, 16, 2, 0.02),
+    (70, 24, 3, 8, 2, 0.02),        # generic only (K = 3, in = 24)
+    (33, 8, 1, 16, 1, 0.02),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: "x".join(map(str, c[:5])))
+def test_small_all_variants(aq, orc, case):
+    out, in_, K, B, batch, sigma = case
+    p = synth.make_problem(out, in_, K, B, batch=batch, sigma_cb=sigma, config=101 + out + in_)
+    codes, cb, x = _dev(p)
+    yref = orc.gemv(p["codes"], p["codebooks"], p["x"], K, B)
+    ran = []
+    for v in _variants_for(K, B, batch):
+        if not aq.variant_supported(v, codes, cb, x):
+            continue
+        check_y(aq.gemv_variant(v, codes, cb, x), yref, f"{v} {case}")
+        ran.append(v)
+    check_y(aq.gemv(codes, cb, x), yref, f"auto gemv {case}")
+    check_y(aq.gemm(codes, cb, x), yref, f"auto gemm {case}")
+    assert "generic" in ran
+
+
+@pytest.mark.parametrize("batch", [1, 2, 3, 4, 8, 15, 16, 17, 33, 64, 128])
+@pytest.mark.parametrize("KB", [(2, 8), (1, 16)])
+def test_batches(aq, orc, batch, KB):
+    K, B = KB
+    out, in_ = 160, 1024
+    p = synth.make_problem(out, in_, K, B, batch=batch, sigma_cb=0.02, config=500 + batch)
+    codes, cb, x = _dev(p)
+    yref = orc.gemv(p["codes"], p["codebooks"], p["x"], K, B)
+    check_y(aq.gemm(codes, cb, x), yref, f"gemm b={batch}")
+    check_y(aq.gemv(codes, cb, x), yref, f"gemv b={batch}")
+    check_y(aq.gemv_variant("mfma", codes, cb, x), yref, f"mfma b={batch}")
+    if batch >= 16:
+        assert aq.selected_variant(codes, cb, x, gemm=True) == "mfma"
+
+
+@pytest.mark.parametrize("KB", [(1, 8), (2, 8), (3, 8), (4, 8), (8, 8), (1, 16), (2, 16)])
+def test_dequantize_bit_exact(aq, orc, KB):
+    import torch
+    K, B = KB
+    p = synth.make_problem(96, 256, K, B, batch=1, sigma_cb=0.02, config=700 + K * B)
+    codes, cb, _ = _dev(p)
+    Wref = orc.decode(p["codes"], p["codebooks"], K, B)
+    W32 = aq.dequantize(codes, cb, dtype=torch.float32).cpu().numpy()
+    assert np.array_equal(W32, Wref)
+    W16 = aq.dequantize(codes, cb, dtype=torch.float16).cpu().numpy()
+    assert np.array_equal(W16.view(np.uint16), Wref.astype(np.float16).view(np.uint16))
+
+
+def test_dequantize_special_values(aq, orc):
+    """fp16 subnormals, signed zeros and +-65504 in the codebooks (2x8 and 1x16)."""
+    import torch
+    for K, B in [(2, 8), (1, 16), (3, 8)]:
+        p = synth.make_problem(64, 128, K, B, batch=1, sigma_cb=0.02, config=800 + K)
+        cb = p["codebooks"].copy()
+        sub = np.arange(1, 1024, 37, dtype=np.uint16).view(np.float16)   # subnormals
+        cb.reshape(-1)[: sub.size] = sub
+        cb.reshape(-1)[-sub.size:] = -sub
+        cb[0, 5] = np.float16(-0.0)
+        cb[-1, 6] = np.float16(0.0)
+        cb[0, 7] = np.float16(65504)
+        cb[-1, 8] = np.float16(-65504)
+        codes = p["codes"].copy()
+        codes[:, :, 0] = np.arange(codes.shape[0] * codes.shape[1]).reshape(codes.shape[:2]) % 16
+        p["codebooks"] = cb
+        p["codes"] = codes
+        ct, cbt, _ = _dev(p)
+        Wref = orc.decode(codes, cb, K, B)
+        W32 = aq.dequantize(ct, cbt, dtype=torch.float32).cpu().numpy()
+        assert np.array_equal(W32, Wref)
+        with np.errstate(over="ignore"):
+            ref16 = Wref.astype(np.float16)
+        W16 = aq.dequantize(ct, cbt, dtype=torch.float16).cpu().numpy()
+        same = (W16.view(np.uint16) == ref16.view(np.uint16)) | ((W16 == 0) & (ref16 == 0))
+        assert np.all(same)
+
+
+def test_special_inputs(aq, orc):
+    """x = 0 gives 0; x = e_i gives column i; subnormal codebooks; identical codes everywhere."""
+    import torch
+    for K, B in [(2, 8), (1, 16)]:
+        p = synth.make_problem(130, 1024, K, B, batch=1, sigma_cb=0.02, config=900 + K)
+        codes, cb, x = _dev(p)
+        variants = [v for v in _variants_for(K, B, 1) if aq.variant_supported(v, codes, cb, x)]
+        zero = torch.zeros_like(x)
+        for v in variants:
+            assert torch.all(aq.gemv_variant(v, codes, cb, zero).float() == 0), v
+        W = orc.decode(p["codes"], p["codebooks"], K, B)
+        for i in (0, 7, 513, 1023):
+            e = torch.zeros_like(x)
+            e[0, i] = 1
+            for v in variants:
+                y = aq.gemv_variant(v, codes, cb, e).float().cpu().numpy()[0]
+                assert np.array_equal(y, W[:, i].astype(np.float16).astype(np.float32)), (v, i)
+        # all group-rows use the same code (every lane gathers the same entry)
+        same = p["codes"].copy()
+        same[...] = 7
+        ct, _, _ = _dev(dict(p, codes=same))
+        yref = orc.gemv(same, p["codebooks"], p["x"], K, B)
+        for v in variants:
+            check_y(aq.gemv_variant(v, ct, cb, x), yref, f"same-code {v}")
+        # codebooks made of subnormals only
+        cbs = (np.abs(p["codebooks"].astype(np.float64)) * 2.0 ** -12).astype(np.float16)
+        cbs = np.where(p["codebooks"] < 0, -cbs, cbs).astype(np.float16)
+        assert np.mean(np.abs(cbs) < 2.0 ** -14) > 0.9
+        _, cbt, _ = _dev(dict(p, codebooks=cbs))
+        yref = orc.gemv(p["codes"], cbs, p["x"], K, B)
+        for v in variants:
+            check_y(aq.gemv_variant(v, codes, cbt, x), yref, f"subnormal {v}")
+
+
+def test_lut_repeat_and_regrow(aq, orc):
+    """The lookup kernel's workspace and counters survive repeated and growing calls."""
+    shapes = [(100, 1024), (3000, 8192), (100, 1024), (5000, 520), (3000, 8192)]
+    for i, (out, in_) in enumerate(shapes):
+        p = synth.make_problem(out, in_, 2, 8, batch=1, sigma_cb=0.02, config=1000 + i)
+        codes, cb, x = _dev(p)
+        yref = orc.gemv(p["codes"], p["codebooks"], p["x"], 2, 8)
+        ys = [aq.gemv_variant("lut", codes, cb, x) for _ in range(3)]
+        check_y(ys[0], yref, f"lut {out}x{in_}")
+        for y in ys[1:]:
+            assert bool((y == ys[0]).all())     # deterministic slice order
+
+
+def test_binding_rejects_host_tensors(aq):
+    import torch
+    p = synth.make_problem(16, 64, 2, 8)
+    with pytest.raises(ValueError):
+        aq.gemv(torch.from_numpy(p["codes"]), torch.from_numpy(p["codebooks"]),
+                torch.from_numpy(p["x"]))
+
+
+# ----------------------------------------------------------------- full sizes
+# The benchmark workloads at full size, in the launch configuration the
+# benchmark uses (auto variant choice), checked on sampled rows.
+
+def _sampled_rows(out, n=192, seed=0):
+    rng = np.random.default_rng(seed)
+    rows = np.unique(np.concatenate([[0, out - 1], rng.integers(0, out, n)]))
+    return rows
+
+
+FULL = []
+for _name, _cfg in synth.CONFIGS.items():
+    for _si, _shape in enumerate(dict.fromkeys(_cfg["shapes"])):
+        for _b in _cfg["batches"]:
+            FULL.append((_name, _shape[0], _shape[1], _cfg["K"], _cfg["B"], _b, _cfg["sigma_cb"]))
+
+
+@pytest.mark.parametrize("case", FULL, ids=lambda c: f"{c[0]}-{c[1]}x{c[2]}-b{c[5]}")
+def test_full_size_sampled(aq, orc, case):
+    name, out, in_, K, B, batch, sigma = case
+    cid = list(synth.CONFIGS).index(name)
+    p = synth.make_problem(out, in_, K, B, batch=batch, sigma_cb=sigma, config=cid)
+    codes, cb, x = _dev(p)
+    rows = _sampled_rows(out, seed=cid)
+    yref = orc.gemv_rows(p["codes"], p["codebooks"], p["x"], K, B, rows)
+    fn = aq.gemm if batch >= 16 else aq.gemv
+    y = fn(codes, cb, x)
+    import torch
+    torch.cuda.synchronize()
+    ys = y.float().cpu().numpy()[:, rows]
+    e = rel_err(ys, yref)
+    assert np.all(e <= TOL), f"{case}: {e.max():.3e}"
+    assert np.all(np.isfinite(y.float().cpu().numpy()))
