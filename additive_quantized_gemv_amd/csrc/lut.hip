@@ -38,24 +38,31 @@ __device__ __forceinline__ float lds_f32(const char *base, uint32_t byte_addr) {
     return *reinterpret_cast<const float *>(base + byte_addr);
 }
 
+// Sum of the two halves returned by a permlane swap.  The halves are taken as
+// plain scalars first: bit-casting an element of the builtin's two-element result
+// directly reads element 0 twice with this compiler.
+__device__ __forceinline__ float swap_sum(uint32_t lo, uint32_t hi) {
+    return __builtin_bit_cast(float, lo) + __builtin_bit_cast(float, hi);
+}
+
 // sum over the 64 lanes of 16 values v[0..15]; afterwards lane l holds the total of
 // value (l >> 2).
 __device__ __forceinline__ float transpose_reduce16(float v[16], int lane) {
     // lanes 0-31 keep rows 0..7, lanes 32-63 keep rows 8..15
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        auto s = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, v[i]),
-                                                  __builtin_bit_cast(uint32_t, v[i + 8]),
-                                                  false, false);
-        v[i] = __builtin_bit_cast(float, s[0]) + __builtin_bit_cast(float, s[1]);
+        const auto s = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, v[i]),
+                                                        __builtin_bit_cast(uint32_t, v[i + 8]),
+                                                        false, false);
+        v[i] = swap_sum(s[0], s[1]);
     }
     // bit 4 of the lane selects rows i or i+4
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        auto s = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, v[i]),
-                                                  __builtin_bit_cast(uint32_t, v[i + 4]),
-                                                  false, false);
-        v[i] = __builtin_bit_cast(float, s[0]) + __builtin_bit_cast(float, s[1]);
+        const auto s = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, v[i]),
+                                                        __builtin_bit_cast(uint32_t, v[i + 4]),
+                                                        false, false);
+        v[i] = swap_sum(s[0], s[1]);
     }
     // bit 3: pair with the mirrored lane of the 16-lane row
     const bool b3 = lane & 8;
