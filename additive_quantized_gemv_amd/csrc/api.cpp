@@ -102,7 +102,7 @@ bool supported(int variant, const aqlm::Problem &p) {
         case AQLM_VARIANT_GENERIC: return true;
         case AQLM_VARIANT_LDS: return p.B == 8 && aqlm::gather_supported(p);
         case AQLM_VARIANT_LUT: return aqlm::lut_supported(p);
-        case AQLM_VARIANT_L2: return p.B == 16 && aqlm::gather_supported(p);
+        case AQLM_VARIANT_L2: return aqlm::l2_supported(p);
         case AQLM_VARIANT_MFMA: return aqlm::mfma_supported(p);
         default: return false;
     }
@@ -114,8 +114,8 @@ int choose(bool gemm, const aqlm::Problem &p) {
     if (gemm && p.batch >= mfma_min_batch() && supported(AQLM_VARIANT_MFMA, p))
         return AQLM_VARIANT_MFMA;
     if (supported(AQLM_VARIANT_LUT, p)) return AQLM_VARIANT_LUT;
-    if (p.B == 8 && supported(AQLM_VARIANT_LDS, p)) return AQLM_VARIANT_LDS;
-    if (p.B == 16 && supported(AQLM_VARIANT_L2, p)) return AQLM_VARIANT_L2;
+    if (supported(AQLM_VARIANT_LDS, p)) return AQLM_VARIANT_LDS;
+    if (supported(AQLM_VARIANT_L2, p)) return AQLM_VARIANT_L2;
     return AQLM_VARIANT_GENERIC;
 }
 
@@ -129,13 +129,23 @@ struct Workspace {
 std::mutex g_ws_mutex;
 std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
 
+// Returns the stream's workspace of at least `bytes`.  A stream that is being
+// captured into a graph cannot allocate: if it has no large enough workspace
+// yet, *out is left null (the caller then picks a kernel that needs none).
 hipError_t get_workspace(hipStream_t stream, size_t bytes, void **out) {
+    *out = nullptr;
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &cap) != hipSuccess) {
+        (void)hipGetLastError();  // a stream that cannot be queried is not capturing
+        cap = hipStreamCaptureStatusNone;
+    }
     std::lock_guard<std::mutex> lock(g_ws_mutex);
     Workspace &w = g_ws[std::make_pair(dev, stream)];
     if (w.bytes < bytes) {
+        if (cap != hipStreamCaptureStatusNone) return hipSuccess;
         if (w.ptr) {
             e = hipStreamSynchronize(stream);  // earlier launches may still use it
             if (e != hipSuccess) return e;
@@ -145,8 +155,6 @@ hipError_t get_workspace(hipStream_t stream, size_t bytes, void **out) {
         }
         size_t nb = bytes < (size_t(1) << 20) ? (size_t(1) << 20) : bytes;
         e = hipMalloc(&w.ptr, nb);
-        if (e != hipSuccess) return e;
-        e = hipMemsetAsync(w.ptr, 0, nb, stream);  // counters start at zero
         if (e != hipSuccess) return e;
         w.bytes = nb;
     }
@@ -161,12 +169,21 @@ aqlm_status_t run(int variant, const aqlm::Problem &p) {
                      aqlm_variant_name(variant), (long long)p.out, (long long)p.in, p.K, p.B,
                      p.batch);
     switch (variant) {
-        case AQLM_VARIANT_LDS:
-        case AQLM_VARIANT_L2: e = aqlm::launch_gather(p); break;
+        case AQLM_VARIANT_LDS: e = aqlm::launch_gather(p); break;
+        case AQLM_VARIANT_L2: e = aqlm::launch_l2(p); break;
         case AQLM_VARIANT_LUT: {
             void *ws = nullptr;
             e = get_workspace(p.stream, aqlm::lut_workspace_bytes(p), &ws);
-            if (e == hipSuccess) e = aqlm::launch_lut(p, ws);
+            if (e != hipSuccess) break;
+            if (ws) {
+                e = aqlm::launch_lut(p, ws);
+            } else {
+                // capturing stream without a workspace: same product, no workspace needed
+                if (log_enabled())
+                    std::fprintf(stderr, "[aqlm] lut: no workspace on a capturing stream, "
+                                         "using the gather kernel\n");
+                e = aqlm::gather_supported(p) ? aqlm::launch_gather(p) : aqlm::launch_generic(p);
+            }
             break;
         }
         case AQLM_VARIANT_MFMA: e = aqlm::launch_mfma(p); break;

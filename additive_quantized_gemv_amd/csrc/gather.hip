@@ -1,14 +1,11 @@
-// Gather GEMV kernels for token generation (batch 1..8) on gfx950.
+// Gather GEMV kernel for 8-bit codes, token generation (batch 1..8), gfx950.
 //
 // y[b][o] = sum_j sum_k C_k[i_k(o,j)] . x[b][8j .. 8j+7]   (distributing the dot
 // product over the additive decode of page "AQLM (Additive Quantization for
 // LLMs)", section "Niveau intermediaire"; W is never materialised).
 //
-// * B = 8: all K codebooks (K x 256 x 16 B, 8 KiB for 2x8) are staged in LDS
-//   once per workgroup; every group-row gathers K 16-byte entries from LDS.
-// * B = 16: the 65536 x 16 B codebook (1 MiB) stays in global memory and is
-//   served by the per-XCD L2 (4 MiB) and the Infinity Cache; codes are streamed
-//   with non-temporal loads so they do not evict it.
+// All K codebooks (K x 256 x 16 B, 8 KiB for 2x8) are staged in LDS once per
+// workgroup; every group-row gathers K 16-byte entries from LDS.
 //
 // Mapping: a wave owns RPW consecutive rows at a time; lane l reads 16-byte
 // chunks l, l+64, ... of each of those rows (one chunk = 16/(K*B/8) groups),
@@ -171,8 +168,7 @@ hipError_t launch_kb(const Problem &p) {
 
 bool gather_supported(const Problem &p) {
     if (p.batch < 1 || p.batch > 8) return false;
-    if (p.B == 8 && !(p.K == 1 || p.K == 2 || p.K == 4 || p.K == 8)) return false;
-    if (p.B == 16 && !(p.K == 1 || p.K == 2)) return false;
+    if (p.B != 8 || !(p.K == 1 || p.K == 2 || p.K == 4 || p.K == 8)) return false;
     const GatherCfg c = gather_cfg(p);
     const int64_t G = p.in / kGroup;
     if (c.groups_per_chunk == 0 || G % c.groups_per_chunk) return false;
@@ -187,16 +183,12 @@ bool gather_supported(const Problem &p) {
 }
 
 hipError_t launch_gather(const Problem &p) {
-    if (p.B == 8) {
-        switch (p.K) {
-            case 1: return launch_kb<1, 8>(p);
-            case 2: return launch_kb<2, 8>(p);
-            case 4: return launch_kb<4, 8>(p);
-            default: return launch_kb<8, 8>(p);
-        }
+    switch (p.K) {
+        case 1: return launch_kb<1, 8>(p);
+        case 2: return launch_kb<2, 8>(p);
+        case 4: return launch_kb<4, 8>(p);
+        default: return launch_kb<8, 8>(p);
     }
-    if (p.K == 1) return launch_kb<1, 16>(p);
-    return launch_kb<2, 16>(p);
 }
 
 }  // namespace aqlm

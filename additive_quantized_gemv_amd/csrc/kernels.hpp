@@ -27,9 +27,13 @@ hipError_t launch_generic(const Problem &p);
 // Dense W (fp32 when w_fp16 == 0, fp16 otherwise).
 hipError_t launch_dequantize(const Problem &p, void *W, int w_fp16);
 
-// Gather kernels: B = 8 (codebooks in LDS) or B = 16 (codebook through L2), batch <= 8.
+// Gather kernel for 8-bit codes (codebooks staged in LDS), batch <= 8.
 bool gather_supported(const Problem &p);
 hipError_t launch_gather(const Problem &p);
+
+// Gather kernel for 16-bit codes (codebook through L2), K in {1,2}, batch <= 8.
+bool l2_supported(const Problem &p);
+hipError_t launch_l2(const Problem &p);
 
 // Lookup-table kernel for K = 2, B = 8, batch 1 (split over input slices).
 bool lut_supported(const Problem &p);

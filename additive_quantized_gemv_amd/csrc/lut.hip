@@ -17,9 +17,14 @@
 // * Each wave takes 16 rows at a time (one 2-byte code load per lane per row),
 //   then reduces the 16 row partials across the 64 lanes with a transposing
 //   butterfly (permlane32/permlane16 swaps, then DPP), ~2 ops per row.
-// * Slice partials go to a workspace; the last workgroup to finish a row range
-//   (atomic counter) sums the slices in slice order and writes fp16 y, then
-//   resets its counter.  Results are deterministic.
+// * Slice partials go to a workspace; a second small kernel sums them in slice
+//   order and writes fp16 y (deterministic).  The kernel boundary is what makes
+//   partials written on one XCD visible to another.  An in-kernel handoff (last
+//   workgroup of a row range sums the slices) needs an agent-scope release fence
+//   per workgroup, i.e. an L2 write-back; measured on MI355X that single-kernel
+//   form took 24 us per 11008x4096 product against 7 + 4 us for the two kernels.
+// * Every code load of a wave (up to 32 rows) is issued before the tables are
+//   built, so each wave waits for HBM once.
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -28,9 +33,9 @@ namespace {
 
 constexpr int kSlice = 64;              // groups per slice (= lanes)
 constexpr int kLutWaves = 16;           // 1024 threads
-constexpr int kRowsPerIter = 16;        // rows a wave handles at once
+constexpr int kReduceRows = 16;         // rows reduced together by the butterfly
+constexpr int kRowsPerWave = 32;        // rows of one wave (all loaded up front)
 constexpr int kLutBytes = 2 * 256 * kSlice * 4;
-constexpr size_t kCounterBytes = 4096;  // room for 1024 row-range counters (at most 256 used)
 
 typedef _Float16 half4 __attribute__((ext_vector_type(4)));
 
@@ -87,10 +92,9 @@ __device__ __forceinline__ float transpose_reduce16(float v[16], int lane) {
 
 __global__ void __launch_bounds__(kLutWaves * kWave)
 lut_kernel(const uint16_t *__restrict__ codes, const uint16_t *__restrict__ cb,
-           const uint16_t *__restrict__ x, uint16_t *__restrict__ y, float *__restrict__ partial,
-           unsigned *__restrict__ counters, int out, int G, int rows_per_block, int nslices) {
+           const uint16_t *__restrict__ x, float *__restrict__ partial, int out, int G,
+           int rows_per_block, int nslices) {
     __shared__ __attribute__((aligned(16))) char lut[kLutBytes];
-    __shared__ int last_flag;
 
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
@@ -101,15 +105,19 @@ lut_kernel(const uint16_t *__restrict__ codes, const uint16_t *__restrict__ cb,
     const bool jvalid = j0 + jl < G;
     const int r_begin = rblock * rows_per_block;
     const int r_end = min(out, r_begin + rows_per_block);
+    // this wave's rows: a contiguous run of rows_per_block / kLutWaves (<= kRowsPerWave)
+    const int rpw = rows_per_block / kLutWaves;
+    const int w_begin = r_begin + wave * rpw;
+    const int w_rows = max(0, min(rpw, r_end - w_begin));
 
-    // issue the first row group's code loads before building the tables
-    int rg = r_begin + wave * kRowsPerIter;
-    uint32_t code[kRowsPerIter];
+    // issue every code load of this wave before building the tables, so the
+    // whole wave waits for HBM once
+    uint32_t code[kRowsPerWave];
 #pragma unroll
-    for (int r = 0; r < kRowsPerIter; ++r) {
-        const int o = min(rg + r, out - 1);
-        code[r] = jvalid ? uint32_t(__builtin_nontemporal_load(codes + size_t(o) * G + j0 + jl))
-                         : 0u;
+    for (int r = 0; r < kRowsPerWave; ++r) {
+        code[r] = 0u;
+        if (jvalid && r < w_rows)
+            code[r] = uint32_t(__builtin_nontemporal_load(codes + size_t(w_begin + r) * G + j0 + jl));
     }
 
     // ---- build L[e][jl] = C[e] . x_{j0+jl} for the 512 entries e = k*256 + c
@@ -137,50 +145,41 @@ lut_kernel(const uint16_t *__restrict__ codes, const uint16_t *__restrict__ cb,
 
     // byte-address template: byte0 = 4*jl, byte2 = 1 selects the second table half
     const uint32_t lanebase = (uint32_t(jl) << 2) | (1u << 16);
-    for (; rg < r_end; rg += kLutWaves * kRowsPerIter) {
-        float v[kRowsPerIter];
 #pragma unroll
-        for (int r = 0; r < kRowsPerIter; ++r) {
+    for (int h = 0; h < kRowsPerWave / kReduceRows; ++h) {
+        if (h * kReduceRows >= w_rows) break;
+        float v[kReduceRows];
+#pragma unroll
+        for (int r = 0; r < kReduceRows; ++r) {
             // addr0 = [4jl, i0, 0, 0], addr1 = [4jl, i1, 1, 0]
-            const uint32_t a0 = __builtin_amdgcn_perm(lanebase, code[r], 0x0C0C0004u);
-            const uint32_t a1 = __builtin_amdgcn_perm(lanebase, code[r], 0x0C060104u);
+            const uint32_t c = code[h * kReduceRows + r];
+            const uint32_t a0 = __builtin_amdgcn_perm(lanebase, c, 0x0C0C0004u);
+            const uint32_t a1 = __builtin_amdgcn_perm(lanebase, c, 0x0C060104u);
             v[r] = lds_f32(lut, a0) + lds_f32(lut, a1);
         }
-        // prefetch the next row group of this wave
-        const int rn = rg + kLutWaves * kRowsPerIter;
-        if (rn < r_end) {
-#pragma unroll
-            for (int r = 0; r < kRowsPerIter; ++r) {
-                const int o = min(rn + r, out - 1);
-                code[r] = jvalid ? uint32_t(__builtin_nontemporal_load(codes + size_t(o) * G +
-                                                                       j0 + jl))
-                                 : 0u;
-            }
-        }
         const float s = transpose_reduce16(v, lane);
-        const int row = rg + (lane >> 2);
-        if ((lane & 3) == 0 && row < r_end) partial[size_t(slice) * out + row] = s;
+        const int r = h * kReduceRows + (lane >> 2);
+        if ((lane & 3) == 0 && r < w_rows) partial[size_t(slice) * out + w_begin + r] = s;
     }
+}
 
-    // ---- last workgroup of this row range sums the slices
-    __threadfence();
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        const unsigned prev = __hip_atomic_fetch_add(&counters[rblock], 1u, __ATOMIC_ACQ_REL,
-                                                     __HIP_MEMORY_SCOPE_AGENT);
-        last_flag = (prev == unsigned(nslices - 1));
+// y[row] = sum over slices (in slice order) of the partial sums, rounded to fp16.
+// Loads are issued eight at a time so that a row waits for memory ceil(n/8) times.
+__global__ void __launch_bounds__(256)
+lut_reduce_kernel(const float *__restrict__ partial, uint16_t *__restrict__ y, int out,
+                  int nslices) {
+    const int row = blockIdx.x * blockDim.x + threadIdx.x;
+    if (row >= out) return;
+    float s = 0.0f;
+    for (int s0 = 0; s0 < nslices; s0 += 8) {
+        float t[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            t[i] = (s0 + i < nslices) ? partial[size_t(s0 + i) * out + row] : 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) s += t[i];
     }
-    __syncthreads();
-    if (!last_flag) return;
-    __threadfence();
-    for (int row = r_begin + threadIdx.x; row < r_end; row += blockDim.x) {
-        float s = 0.0f;
-        for (int sl = 0; sl < nslices; ++sl)
-            s += __builtin_nontemporal_load(partial + size_t(sl) * out + row);
-        y[row] = f2h_bits(s);
-    }
-    if (threadIdx.x == 0)
-        __hip_atomic_store(&counters[rblock], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    y[row] = f2h_bits(s);
 }
 
 struct LutCfg {
@@ -191,12 +190,15 @@ LutCfg lut_cfg(const Problem &p) {
     LutCfg c{};
     const int64_t G = p.in / kGroup;
     c.nslices = int((G + kSlice - 1) / kSlice);
-    int nrb = c.nslices >= 256 ? 1 : 256 / c.nslices;
-    const int64_t max_rb = (p.out + kRowsPerIter - 1) / kRowsPerIter;
-    if (nrb > max_rb) nrb = int(max_rb);
-    if (nrb < 1) nrb = 1;
+    // one workgroup per CU: about 256 / nslices row ranges, each at most
+    // kLutWaves * kRowsPerWave rows (a wave's rows are all loaded at once)
+    const int64_t max_rows = int64_t(kLutWaves) * kRowsPerWave;
+    int64_t nrb = c.nslices >= 256 ? 1 : 256 / c.nslices;
+    const int64_t need = (p.out + max_rows - 1) / max_rows;
+    if (nrb < need) nrb = need;
     int64_t rpb = (p.out + nrb - 1) / nrb;
-    rpb = (rpb + kRowsPerIter - 1) / kRowsPerIter * kRowsPerIter;
+    rpb = (rpb + kLutWaves - 1) / kLutWaves * kLutWaves;   // whole rows per wave
+    if (rpb < kLutWaves) rpb = kLutWaves;
     c.rows_per_block = int(rpb);
     c.nrblocks = int((p.out + rpb - 1) / rpb);
     return c;
@@ -215,22 +217,23 @@ bool lut_supported(const Problem &p) {
 
 size_t lut_workspace_bytes(const Problem &p) {
     const LutCfg c = lut_cfg(p);
-    return kCounterBytes + size_t(c.nslices) * size_t(p.out) * sizeof(float);
+    return size_t(c.nslices) * size_t(p.out) * sizeof(float);
 }
 
-// workspace: [kCounterBytes of counters, all zero between calls][partials: nslices x out fp32].
-// The counters sit at a fixed offset so that calls with different shapes reuse
-// them: every counter a call uses is back at zero when the call ends.
+// workspace: partial sums, nslices x out fp32 (no initial contents needed)
 hipError_t launch_lut(const Problem &p, void *workspace) {
     const LutCfg c = lut_cfg(p);
-    unsigned *counters = static_cast<unsigned *>(workspace);
-    float *partial = reinterpret_cast<float *>(static_cast<char *>(workspace) + kCounterBytes);
+    float *partial = static_cast<float *>(workspace);
     const int grid = c.nslices * c.nrblocks;
     hipLaunchKernelGGL(lut_kernel, dim3(grid), dim3(kLutWaves * kWave), 0, p.stream,
                        static_cast<const uint16_t *>(p.codes),
                        static_cast<const uint16_t *>(p.codebooks),
-                       static_cast<const uint16_t *>(p.x), static_cast<uint16_t *>(p.y), partial,
-                       counters, int(p.out), int(p.in / kGroup), c.rows_per_block, c.nslices);
+                       static_cast<const uint16_t *>(p.x), partial, int(p.out),
+                       int(p.in / kGroup), c.rows_per_block, c.nslices);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(lut_reduce_kernel, dim3(unsigned((p.out + 255) / 256)), dim3(256), 0,
+                       p.stream, partial, static_cast<uint16_t *>(p.y), int(p.out), c.nslices);
     return hipGetLastError();
 }
 

@@ -1,0 +1,276 @@
+#!/usr/bin/env python3
+"""Benchmark of the additive-quantized GEMV (token generation, batch 1) on one MI355X.
+
+Workload: the Llama-2-7B MLP projection shapes out x in = 11008 x 4096 and
+4096 x 11008, each in the 2x8 scheme (two 256-entry codebooks, 8-bit codes) and
+the 1x16 scheme (one 65536-entry codebook, 16-bit codes), 2 bits per weight,
+fp16 activations, batch 1.  Codes, codebooks and activations are seeded
+synthetic data (uniform codes, N(0, 0.02^2) codebooks, N(0, 1) activations).
+
+One step = the four products (2 shapes x 2 schemes).  Every launch reads a
+different copy of codes and codebooks from a rotation set larger than twice
+the 256 MB Infinity Cache, so weights stream from HBM as in a real decode step.
+Launches are replayed from captured HIP graphs; HIP events on the launch stream
+bracket the timed region.
+
+value = algorithmic bytes per step (codes + codebooks + x + y of the four
+products, each counted once) / time per step, in GB/s.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "AQLM GEMV µs/call + achieved HBM GB/s (% of peak), 2x8 & 1x16, batch 1"
+HBM_PEAK_GBPS = 8000.0
+MALL_BYTES = 256 << 20
+WORKLOAD = [  # name, out, in, K, B
+    ("2x8 11008x4096", 11008, 4096, 2, 8),
+    ("2x8 4096x11008", 4096, 11008, 2, 8),
+    ("1x16 11008x4096", 11008, 4096, 1, 16),
+    ("1x16 4096x11008", 4096, 11008, 1, 16),
+]
+SIGMA_CB = 0.02
+CONFIG_IDS = {8: 2, 16: 3}     # seed namespace per scheme (the 2x8 and 1x16 MLP workloads)
+PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "hbm_traffic.md")
+KERNEL_SOURCES = {"lut": "lut.hip", "lds": "gather.hip", "l2": "l2gather.hip", "mfma": "mfma.hip",
+                  "generic": "generic.hip"}
+
+
+def algorithmic_bytes(out, in_, K, B, batch=1):
+    codes = out * (in_ // 8) * K * (B // 8)
+    codebooks = K * (1 << B) * 8 * 2
+    return codes + codebooks + batch * in_ * 2 + batch * out * 2
+
+
+def source_sha(variant):
+    path = os.path.join(ROOT, "additive_quantized_gemv_amd", "csrc", KERNEL_SOURCES[variant])
+    h = hashlib.sha256()
+    for p in (path, os.path.join(ROOT, "additive_quantized_gemv_amd", "csrc", "device_common.hpp")):
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(config_name, variant):
+    """HBM bytes per launch from the committed counter summary, if it is for this kernel source."""
+    if not os.path.exists(PROFILE_TRAFFIC):
+        return None
+    want_sha = source_sha(variant)
+    for line in open(PROFILE_TRAFFIC):
+        m = re.match(r"\|\s*traffic\s*\|\s*([^|]+?)\s*\|\s*(\w+)\s*\|\s*([0-9a-f]+)\s*\|\s*(\d+)\s*\|",
+                     line)
+        if m and m.group(1) == config_name and m.group(2) == variant and m.group(3) == want_sha:
+            return int(m.group(4))
+    return None
+
+
+def build_inputs(torch, synth, copies):
+    """Device tensors: per copy, per workload entry (codes, codebooks, x); plus y buffers."""
+    import numpy as np
+    dev = torch.device("cuda:0")
+    sets = []
+    for r in range(copies):
+        entry = []
+        for name, out, in_, K, B in WORKLOAD:
+            p = synth.make_problem(out, in_, K, B, batch=1, sigma_cb=SIGMA_CB,
+                                   config=CONFIG_IDS[B] * 10 + (0 if out > in_ else 1), copy=r)
+            codes = p["codes"] if B == 8 else p["codes"].view(np.int16)
+            entry.append((torch.from_numpy(codes).to(dev), torch.from_numpy(p["codebooks"]).to(dev),
+                          torch.from_numpy(p["x"]).to(dev), p))
+        sets.append(entry)
+    ys = [torch.empty((1, out), dtype=torch.float16, device=dev) for _, out, _, _, _ in WORKLOAD]
+    return sets, ys
+
+
+def time_graph(torch, g, replays):
+    stream = torch.cuda.current_stream()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(replays):
+        g.replay()
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) * 1e-3  # seconds
+
+
+def cpu_baseline(sets, ys_copy0, budget_s):
+    """The oracle as it stands, on the host cores, over the four products of copy 0."""
+    import numpy as np
+    from oracle import Oracle
+    orc = Oracle()
+    cores = orc.max_threads()
+    t0 = time.perf_counter()
+    done_bytes, reps, max_err = 0, 0, 0.0
+    while True:
+        for (name, out, in_, K, B), (_, _, _, p), yg in zip(WORKLOAD, sets[0], ys_copy0):
+            yref = orc.gemv(p["codes"], p["codebooks"], p["x"], K, B)
+            done_bytes += algorithmic_bytes(out, in_, K, B)
+            if reps == 0:
+                e = np.max(np.abs(yg - yref)) / (np.max(np.abs(yref)) + 1e-6)
+                max_err = max(max_err, float(e))
+        reps += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": round(done_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": cores,
+            "kind": "oracle",
+            "sample": f"full decode to fp32 W + double matvec of the four products of one step "
+                      f"(copy 0), repeated {reps}x in {dt:.1f} s",
+            "ms_per_step": round(dt / reps * 1e3, 1),
+            "gpu_vs_oracle_max_rel_err": max_err}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--copies", type=int, default=0, help="rotation copies (0 = auto, > 2x MALL)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--warm", action="store_true", help="also time cache-resident (no rotation)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this library has no multi-GPU path "
+              "(rows would shard with no exchange; see the design notes). Run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import additive_quantized_gemv_amd as aq
+    from additive_quantized_gemv_amd import synth
+
+    if not torch.cuda.is_available():
+        print("no GPU available", file=sys.stderr)
+        sys.exit(1)
+    aq._load()
+
+    per_copy = sum(algorithmic_bytes(o, i, K, B) for _, o, i, K, B in WORKLOAD)
+    copies = args.copies or max(2, math.ceil(2 * MALL_BYTES / per_copy))
+    t_gen = time.perf_counter()
+    sets, ys = build_inputs(torch, synth, copies)
+    torch.cuda.synchronize()
+    print(f"[bench] {copies} rotation copies, {per_copy * copies / 2**20:.0f} MiB, "
+          f"built in {time.perf_counter() - t_gen:.1f} s", file=sys.stderr, flush=True)
+
+    def call(entry_idx, r):
+        codes, cb, x, _ = sets[r][entry_idx]
+        aq.gemv(codes, cb, x, out=ys[entry_idx])
+
+    variants = [aq.selected_variant(*sets[0][i][:3]) for i in range(len(WORKLOAD))]
+
+    # one stream for warmup, capture, replay and events: the warmup's eager calls
+    # give it the lookup kernel's workspace before anything is captured
+    stream = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        for s in range(args.warmup):
+            for i in range(len(WORKLOAD)):
+                call(i, s % copies)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        return _timed(args, torch, np, aq, sets, ys, copies, per_copy, call, variants, stream)
+
+
+def capture_on(torch, stream, fn):
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        fn()
+    return g
+
+
+def _timed(args, torch, np, aq, sets, ys, copies, per_copy, call, variants, stream):
+
+    def steps_fn(nsteps):
+        def f():
+            for s in range(nsteps):
+                for i in range(len(WORKLOAD)):
+                    call(i, s % copies)
+        return f
+
+    # main timed region: exactly args.steps steps
+    full = capture_on(torch, stream, steps_fn(copies))
+    tail_n = args.steps % copies
+    tail = capture_on(torch, stream, steps_fn(tail_n)) if tail_n else None
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(args.steps // copies):
+        full.replay()
+    if tail is not None:
+        tail.replay()
+    end.record(stream)
+    torch.cuda.synchronize()
+    step_s = start.elapsed_time(end) * 1e-3 / args.steps
+    print(f"[bench] timed {args.steps} steps: {step_s * 1e6:.2f} us/step", file=sys.stderr,
+          flush=True)
+
+    # per-product launches, same rotation, for per-kernel averages
+    per_call = []
+    launches = max(copies, (args.steps // copies) * copies)
+    for i, (name, out, in_, K, B) in enumerate(WORKLOAD):
+        g = capture_on(torch, stream, lambda i=i: [call(i, r) for r in range(copies)])
+        dt = time_graph(torch, g, launches // copies) / ((launches // copies) * copies)
+        nbytes = algorithmic_bytes(out, in_, K, B)
+        rec = {"product": name, "variant": variants[i], "us_per_call": round(dt * 1e6, 3),
+               "gbps": round(nbytes / dt / 1e9, 1),
+               "pct_hbm_peak": round(100 * nbytes / dt / 1e9 / HBM_PEAK_GBPS, 1),
+               "algorithmic_bytes": nbytes}
+        if args.warm:
+            gw = capture_on(torch, stream, lambda i=i: [call(i, 0) for _ in range(copies)])
+            dtw = time_graph(torch, gw, launches // copies) / ((launches // copies) * copies)
+            rec["us_per_call_cache_resident"] = round(dtw * 1e6, 3)
+        per_call.append(rec)
+        print(f"[bench] {name} ({variants[i]}): {rec['us_per_call']} us, {rec['gbps']} GB/s",
+              file=sys.stderr, flush=True)
+
+    step_bytes = per_copy
+    value = step_bytes / step_s / 1e9
+    dom = max(range(len(WORKLOAD)), key=lambda i: per_call[i]["us_per_call"])
+    d = per_call[dom]
+    achieved = d["algorithmic_bytes"] / (d["us_per_call"] * 1e-6) / 1e9
+    traffic = measured_traffic(d["product"], d["variant"])
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                "kernel": f"{d['variant']} ({d['product']})",
+                "algorithmic_bytes_per_launch": d["algorithmic_bytes"]}
+
+    result = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(step_s * 1e3, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp16 x fp16 -> fp32 (u8/u16 codes)", "data": "synthetic",
+        "config": {"workload": "Llama-2-7B MLP projections 11008x4096 and 4096x11008, "
+                               "2x8 and 1x16 (2 bits/weight), batch 1",
+                   "batch": 1, "rotation_copies": copies,
+                   "rotation_bytes": per_copy * copies, "launch": "hip graph replay",
+                   "step": "4 products (2 shapes x 2 schemes)"},
+        "per_call": per_call,
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        ys_copy0 = []
+        for i in range(len(WORKLOAD)):
+            call(i, 0)
+            torch.cuda.synchronize()
+            ys_copy0.append(ys[i].float().cpu().numpy().astype(np.float64))
+        result["cpu_baseline"] = cpu_baseline(sets, ys_copy0, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

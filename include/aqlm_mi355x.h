@@ -28,8 +28,15 @@
  *
  * Calls are asynchronous: work is enqueued on `stream` (a hipStream_t; NULL is
  * the default stream) and the call returns before it finishes.  The library
- * keeps no pointer after a call returns, allocates no memory and holds no
- * state; calls on different streams may run concurrently.
+ * keeps no pointer to caller memory after a call returns.  Memory: the only
+ * allocation is a workspace for the batch-1 2x8 lookup-table kernel
+ * (out x ceil(in/512) fp32 partial sums), one per (device, stream), made on
+ * the first such call on that stream, grown when a larger shape needs it and
+ * kept until the process exits.  Calls on different streams may run
+ * concurrently.  On a stream that is being captured into a HIP graph and has no
+ * workspace yet, that product runs on the workspace-free gather kernel instead
+ * (same result within the stated tolerance); make one call on the stream
+ * before capturing to get the lookup-table kernel in the graph.
  *
  * Errors: argument errors are reported synchronously, before any device work:
  * a null pointer, a size < 1, in_features not a multiple of 8, K outside

@@ -247,3 +247,54 @@ def test_full_size_sampled(aq, orc, case):
     e = rel_err(ys, yref)
     assert np.all(e <= TOL), f"{case}: {e.max():.3e}"
     assert np.all(np.isfinite(y.float().cpu().numpy()))
+
+
+def test_graph_capture_replay(aq, orc):
+    """Products captured in a HIP graph and replayed several times, with eager work and
+    synchronisations between replays, match the eager results every time."""
+    import torch
+    cases = [(1000, 4096, 2, 8, 1), (1000, 4096, 1, 16, 1), (512, 1024, 2, 8, 4),
+             (512, 1024, 2, 8, 32), (512, 1024, 1, 16, 16)]
+    stream = torch.cuda.Stream()
+    probs, eager, outs = [], [], []
+    with torch.cuda.stream(stream):
+        for i, (out, in_, K, B, batch) in enumerate(cases):
+            p = synth.make_problem(out, in_, K, B, batch=batch, sigma_cb=0.02, config=1200 + i)
+            t = _dev(p)
+            probs.append((p, t))
+            eager.append(aq.gemm(*t).clone())       # also gives this stream its workspace
+            outs.append(torch.empty_like(eager[-1]))
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for (p, t), o in zip(probs, outs):
+                aq.gemm(*t, out=o)
+        for rep in range(4):
+            for o in outs:
+                o.fill_(7.0)                         # eager work between replays
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            for e, o in zip(eager, outs):
+                assert bool((e == o).all()), f"replay {rep}"
+    for (p, _), e in zip(probs, eager):
+        yref = orc.gemv(p["codes"], p["codebooks"], p["x"], p["K"], p["B"])
+        check_y(e, yref, "eager before capture")
+
+
+def test_capture_without_workspace_falls_back(aq, orc):
+    """A lookup-table call first seen on a capturing stream runs the workspace-free kernel."""
+    import torch
+    p = synth.make_problem(700, 2048, 2, 8, batch=1, sigma_cb=0.02, config=1300)
+    t = _dev(p)
+    y = torch.empty((1, 700), dtype=torch.float16, device="cuda")
+    stream = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        aq.gemv(*t, out=y)
+    yref = orc.gemv(p["codes"], p["codebooks"], p["x"], 2, 8)
+    for _ in range(3):
+        y.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        check_y(y, yref, "captured fallback")
