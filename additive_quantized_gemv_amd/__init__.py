@@ -16,14 +16,15 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["gemv", "gemm", "gemv_variant", "dequantize", "bits_per_weight", "codes_bytes",
+__all__ = ["gemv", "gemm", "gemv_variant", "gemv_packed", "pack_codebooks", "unpack_codebooks",
+           "dequantize", "bits_per_weight", "codes_bytes",
            "codebooks_bytes", "variant_supported", "selected_variant", "VARIANTS", "library_path",
            "AqlmError", "version"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libaqlm_mi355x.so")
 
-VARIANTS = {"auto": 0, "generic": 1, "lds": 2, "lut": 3, "l2": 4, "mfma": 5}
+VARIANTS = {"auto": 0, "generic": 1, "lds": 2, "lut": 3, "l2": 4, "mfma": 5, "split": 6}
 _STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "HIP error"}
 
 
@@ -61,6 +62,11 @@ def _load():
     lib.aqlm_variant_supported.restype = ci
     lib.aqlm_selected_variant.argtypes = [ci, vp, vp, vp, vp, i64, i64, ci, ci, ci]
     lib.aqlm_selected_variant.restype = ci
+    lib.aqlm_gemv_packed.argtypes = prod
+    lib.aqlm_gemv_packed.restype = ci
+    for name in ("aqlm_pack_codebooks", "aqlm_unpack_codebooks"):
+        getattr(lib, name).argtypes = [vp, vp, ci, ci, vp]
+        getattr(lib, name).restype = ci
     lib.aqlm_dequantize.argtypes = [vp, vp, vp, ci, i64, i64, ci, ci, vp]
     lib.aqlm_dequantize.restype = ci
     lib.aqlm_bits_per_weight.argtypes = [ci, ci, ci]
@@ -102,7 +108,7 @@ def _bits_of(codes) -> int:
     raise TypeError("codes must be uint8 (8-bit codes) or int16/uint16 (16-bit codes)")
 
 
-def _prep(codes, codebooks, x, K, B):
+def _prep(codes, codebooks, x, K, B, packed=False):
     torch = _torch()
     if codes.dim() != 3:
         raise ValueError("codes must be [out][in/8][K]")
@@ -111,8 +117,9 @@ def _prep(codes, codebooks, x, K, B):
     B = Bc if B is None else int(B)
     if B != Bc or K != codes.shape[2]:
         raise ValueError("K/B do not match the codes tensor")
-    if codebooks.dtype != torch.float16 or tuple(codebooks.shape) != (K, 1 << B, 8):
-        raise ValueError(f"codebooks must be float16 [{K}][{1 << B}][8]")
+    want = (K, 8, 1 << B) if packed else (K, 1 << B, 8)
+    if codebooks.dtype != torch.float16 or tuple(codebooks.shape) != want:
+        raise ValueError(f"codebooks must be float16 {list(want)}")
     if x.dtype != torch.float16:
         raise TypeError("x must be float16")
     x2 = x.unsqueeze(0) if x.dim() == 1 else x
@@ -134,7 +141,7 @@ def _stream():
 def _product(fn_name, codes, codebooks, x, K=None, B=None, out=None, variant=None):
     torch = _torch()
     lib = _load()
-    K, B, x2 = _prep(codes, codebooks, x, K, B)
+    K, B, x2 = _prep(codes, codebooks, x, K, B, packed=(fn_name == "aqlm_gemv_packed"))
     out_f, in_f, batch = codes.shape[0], codes.shape[1] * 8, x2.shape[0]
     y = out if out is not None else torch.empty((batch, out_f), dtype=torch.float16,
                                                  device=codes.device)
@@ -158,6 +165,41 @@ def gemv(codes, codebooks, x, K=None, B=None, out=None):
 def gemm(codes, codebooks, x, K=None, B=None, out=None):
     """Y = X W^T; for batch >= 16 decodes to fp16 and runs on the matrix cores."""
     return _product("aqlm_gemm", codes, codebooks, x, K, B, out)
+
+
+def gemv_packed(codes, packed_codebooks, x, K=None, B=None, out=None):
+    """y = W x with codebooks in the packed plane-major layout [K][8][2^B] (pack_codebooks)."""
+    return _product("aqlm_gemv_packed", codes, packed_codebooks, x, K, B, out)
+
+
+def pack_codebooks(codebooks, out=None):
+    """Plane-major copy [K][8][2^B] of codebooks [K][2^B][8] (a one-time weight layout change)."""
+    torch = _torch()
+    lib = _load()
+    K, E, g = codebooks.shape
+    if codebooks.dtype != torch.float16 or g != 8 or E not in (256, 65536) or not codebooks.is_cuda \
+            or not codebooks.is_contiguous():
+        raise ValueError("codebooks must be a contiguous device float16 [K][2^B][8] tensor")
+    P = out if out is not None else torch.empty((K, 8, E), dtype=torch.float16,
+                                                 device=codebooks.device)
+    _check(lib.aqlm_pack_codebooks(codebooks.data_ptr(), P.data_ptr(), K, E.bit_length() - 1,
+                                   _stream()), "aqlm_pack_codebooks")
+    return P
+
+
+def unpack_codebooks(packed, out=None):
+    """Inverse of pack_codebooks: [K][8][2^B] -> [K][2^B][8]."""
+    torch = _torch()
+    lib = _load()
+    K, g, E = packed.shape
+    if packed.dtype != torch.float16 or g != 8 or E not in (256, 65536) or not packed.is_cuda \
+            or not packed.is_contiguous():
+        raise ValueError("packed must be a contiguous device float16 [K][8][2^B] tensor")
+    C = out if out is not None else torch.empty((K, E, 8), dtype=torch.float16,
+                                                 device=packed.device)
+    _check(lib.aqlm_unpack_codebooks(packed.data_ptr(), C.data_ptr(), K, E.bit_length() - 1,
+                                     _stream()), "aqlm_unpack_codebooks")
+    return C
 
 
 def gemv_variant(variant, codes, codebooks, x, K=None, B=None, out=None):

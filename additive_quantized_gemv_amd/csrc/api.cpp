@@ -40,6 +40,7 @@ int forced_variant() {
     if (!std::strcmp(v, "lut")) return AQLM_VARIANT_LUT;
     if (!std::strcmp(v, "l2")) return AQLM_VARIANT_L2;
     if (!std::strcmp(v, "mfma")) return AQLM_VARIANT_MFMA;
+    if (!std::strcmp(v, "split")) return AQLM_VARIANT_SPLIT;
     return AQLM_VARIANT_AUTO;
 }
 
@@ -160,6 +161,23 @@ hipError_t get_workspace(hipStream_t stream, size_t bytes, void **out) {
     }
     *out = w.ptr;
     return hipSuccess;
+}
+
+// Packs or unpacks codebooks; shared argument checks.
+aqlm_status_t pack_common(const void *src, void *dst, int K, int B, void *stream, bool pack) {
+    if (!src || !dst || K < 1 || K > 8 || (B != 8 && B != 16)) return AQLM_ERR_INVALID_ARGUMENT;
+    const int64_t bytes = int64_t(K) * (int64_t(1) << B) * kGroup * 2;
+    if (((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) & 1u) ||
+        overlaps(src, bytes, dst, bytes))
+        return AQLM_ERR_INVALID_ARGUMENT;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const hipError_t e = pack ? aqlm::launch_pack_codebooks(src, dst, K, B, s)
+                              : aqlm::launch_unpack_codebooks(src, dst, K, B, s);
+    if (e != hipSuccess) {
+        set_error(pack ? "pack_codebooks" : "unpack_codebooks", e);
+        return AQLM_ERR_HIP;
+    }
+    return AQLM_OK;
 }
 
 aqlm_status_t run(int variant, const aqlm::Problem &p) {
@@ -318,11 +336,63 @@ const char *aqlm_variant_name(int variant) {
         case AQLM_VARIANT_LUT: return "lut";
         case AQLM_VARIANT_L2: return "l2";
         case AQLM_VARIANT_MFMA: return "mfma";
+        case AQLM_VARIANT_SPLIT: return "split";
         default: return "unknown";
     }
 }
 
-const char *aqlm_version(void) { return "0.1.0"; }
+aqlm_status_t aqlm_pack_codebooks(const void *codebooks, void *packed, int K, int B,
+                                  void *stream) {
+    return pack_common(codebooks, packed, K, B, stream, true);
+}
+
+aqlm_status_t aqlm_unpack_codebooks(const void *packed, void *codebooks, int K, int B,
+                                    void *stream) {
+    return pack_common(packed, codebooks, K, B, stream, false);
+}
+
+aqlm_status_t aqlm_gemv_packed(const void *codes, const void *packed_codebooks, const void *x,
+                               void *y, int64_t out_features, int64_t in_features, int K, int B,
+                               int batch, void *stream) {
+    Sizes s;
+    aqlm_status_t st = check_args(codes, packed_codebooks, x, y, out_features, in_features, K, B,
+                                  batch, &s);
+    if (st != AQLM_OK) return st;
+    aqlm::Problem p = make_problem(codes, packed_codebooks, x, y, out_features, in_features, K, B,
+                                   batch, stream);
+    const bool split = aqlm::ds_supported(p) && forced_variant() != AQLM_VARIANT_GENERIC;
+    const size_t need = split ? aqlm::ds_workspace_bytes(p) : size_t(s.codebooks);
+    void *ws = nullptr;
+    hipError_t e = get_workspace(p.stream, need, &ws);
+    if (e != hipSuccess) {
+        set_error("workspace", e);
+        return AQLM_ERR_HIP;
+    }
+    if (!ws) return AQLM_ERR_UNSUPPORTED;   // capturing stream without a workspace
+    if (log_enabled())
+        std::fprintf(stderr, "[aqlm] packed %s out=%lld in=%lld K=%d B=%d batch=%d\n",
+                     split ? "split" : "unpack+auto", (long long)p.out, (long long)p.in, K, B,
+                     batch);
+    if (split) {
+        e = aqlm::launch_ds(p, ws);
+        if (e != hipSuccess) {
+            set_error("split", e);
+            return AQLM_ERR_HIP;
+        }
+        return AQLM_OK;
+    }
+    e = aqlm::launch_unpack_codebooks(packed_codebooks, ws, K, B, p.stream);
+    if (e != hipSuccess) {
+        set_error("unpack_codebooks", e);
+        return AQLM_ERR_HIP;
+    }
+    p.codebooks = ws;
+    int v = choose(false, p);
+    if (v == AQLM_VARIANT_LUT) v = AQLM_VARIANT_LDS;   // the workspace holds the codebooks
+    return run(v, p);
+}
+
+const char *aqlm_version(void) { return "0.2.0"; }
 
 const char *aqlm_last_error(void) { return g_last_error; }
 

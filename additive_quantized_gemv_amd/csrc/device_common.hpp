@@ -70,6 +70,88 @@ __device__ __forceinline__ float wave_sum(float v) {
         __builtin_bit_cast(int, wave_sum_to_lane63(v)), 63));
 }
 
+// Sum of the two halves returned by a permlane swap.  The halves are taken as
+// plain scalars: bit-casting an element of the builtin's two-element result
+// directly reads element 0 twice with this compiler.
+__device__ __forceinline__ float swap_sum(uint32_t lo, uint32_t hi) {
+    return __builtin_bit_cast(float, lo) + __builtin_bit_cast(float, hi);
+}
+
+// Exchange step over lane bit BIT: pairs (a, b) -> one value per lane, the sum over
+// the two lanes of `a` where the bit is clear and of `b` where it is set.
+template <int BIT>
+__device__ __forceinline__ float butterfly_step(float a, float b, int lane) {
+    if constexpr (BIT == 5) {
+        const auto s = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, a),
+                                                        __builtin_bit_cast(uint32_t, b), false,
+                                                        false);
+        return swap_sum(s[0], s[1]);
+    } else if constexpr (BIT == 4) {
+        const auto s = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, a),
+                                                        __builtin_bit_cast(uint32_t, b), false,
+                                                        false);
+        return swap_sum(s[0], s[1]);
+    } else {
+        const bool hi = (lane >> BIT) & 1;
+        const float send = hi ? a : b;
+        const float keep = hi ? b : a;
+        // partners: row_mirror flips bits 0-3, row_half_mirror bits 0-2, quad perms bit 1 / 0
+        if constexpr (BIT == 3) return keep + dpp_f<0x140>(send);
+        else if constexpr (BIT == 2) return keep + dpp_f<0x141>(send);
+        else if constexpr (BIT == 1) return keep + dpp_f<0x4E>(send);
+        else return keep + dpp_f<0xB1>(send);
+    }
+}
+
+// All-lane sum over lane bit BIT (the value of the partner lane is added).
+template <int BIT>
+__device__ __forceinline__ float allreduce_step(float v) {
+    if constexpr (BIT == 5) {
+        const uint32_t u = __builtin_bit_cast(uint32_t, v);
+        const auto s = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+        return swap_sum(s[0], s[1]);
+    } else if constexpr (BIT == 4) {
+        const uint32_t u = __builtin_bit_cast(uint32_t, v);
+        const auto s = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+        return swap_sum(s[0], s[1]);
+    } else if constexpr (BIT == 3) {
+        return v + dpp_f<0x140>(v);
+    } else if constexpr (BIT == 2) {
+        return v + dpp_f<0x141>(v);
+    } else if constexpr (BIT == 1) {
+        return v + dpp_f<0x4E>(v);
+    } else {
+        return v + dpp_f<0xB1>(v);
+    }
+}
+
+template <int R, int LEVEL>
+__device__ __forceinline__ void butterfly_levels(float *v, int lane) {
+    if constexpr (R > 1) {
+        constexpr int BIT = 5 - LEVEL;
+#pragma unroll
+        for (int i = 0; i < R / 2; ++i) v[i] = butterfly_step<BIT>(v[i], v[i + R / 2], lane);
+        butterfly_levels<R / 2, LEVEL + 1>(v, lane);
+    }
+}
+
+template <int LEVEL>
+__device__ __forceinline__ float allreduce_levels(float v) {
+    if constexpr (LEVEL < 6) return allreduce_levels<LEVEL + 1>(allreduce_step<5 - LEVEL>(v));
+    else return v;
+}
+
+// Sums v[0..R-1] over the 64 lanes of the wave at once (R a power of two <= 64,
+// about 2 instructions per value): afterwards lane l holds the total of value
+// l >> (6 - log2 R).
+template <int R>
+__device__ __forceinline__ float transpose_reduce(float *v, int lane) {
+    constexpr int LOG = R <= 1 ? 0 : R <= 2 ? 1 : R <= 4 ? 2 : R <= 8 ? 3 : R <= 16 ? 4 : R <= 32 ? 5 : 6;
+    static_assert((1 << LOG) == R, "R must be a power of two");
+    butterfly_levels<R, 0>(v, lane);
+    return allreduce_levels<LOG>(v[0]);
+}
+
 __device__ __forceinline__ int lane_id() { return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)); }
 
 // Streaming 16-byte load that should not stay in the caches (codes are read once).

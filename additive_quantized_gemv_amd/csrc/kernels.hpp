@@ -40,6 +40,13 @@ bool lut_supported(const Problem &p);
 size_t lut_workspace_bytes(const Problem &p);
 hipError_t launch_lut(const Problem &p, void *workspace);
 
+// 16-bit codes with the codebook split by vector position (packed planes), batch <= 4.
+bool ds_supported(const Problem &p);
+size_t ds_workspace_bytes(const Problem &p);
+hipError_t launch_ds(const Problem &p, void *workspace);
+hipError_t launch_pack_codebooks(const void *cb, void *planes, int K, int B, hipStream_t s);
+hipError_t launch_unpack_codebooks(const void *planes, void *cb, int K, int B, hipStream_t s);
+
 // Decode-to-fp16 fragments + MFMA, K in {1,2}, B in {8,16}, any batch.
 bool mfma_supported(const Problem &p);
 hipError_t launch_mfma(const Problem &p);

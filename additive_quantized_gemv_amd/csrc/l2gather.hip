@@ -41,13 +41,12 @@ l2_kernel(const uint8_t *__restrict__ codes, const uint4 *__restrict__ cb,
     int o = blockIdx.x * kL2Waves + threadIdx.x / kWave;
     if (o >= out) return;
 
+    // Branch-free (the chunk index is clamped into the row; clamped lanes are masked
+    // where the chunk is used): a conditional load would be waited for at once.
     auto load_chunk = [&](int row, int it) -> u32x4 {
-        const int c = lane + kWave * it;
-        u32x4 z = {0u, 0u, 0u, 0u};
-        if (c < NC)
-            z = __builtin_nontemporal_load(
-                reinterpret_cast<const u32x4 *>(codes + (size_t(row) * NC + c) * 16u));
-        return z;
+        const int c = min(lane + kWave * it, NC - 1);
+        return __builtin_nontemporal_load(
+            reinterpret_cast<const u32x4 *>(codes + (size_t(row) * NC + c) * 16u));
     };
 
     int it = 0;
@@ -62,7 +61,7 @@ l2_kernel(const uint8_t *__restrict__ codes, const uint4 *__restrict__ cb,
             it_n = 0;
             o_n = o + nwaves;
         }
-        const u32x4 nxt = (o_n < out) ? load_chunk(o_n, it_n) : u32x4{0u, 0u, 0u, 0u};
+        const u32x4 nxt = load_chunk(min(o_n, out - 1), it_n);
 
         const int c = lane + kWave * it;
         if (c < NC) {

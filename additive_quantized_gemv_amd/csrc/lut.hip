@@ -43,53 +43,6 @@ __device__ __forceinline__ float lds_f32(const char *base, uint32_t byte_addr) {
     return *reinterpret_cast<const float *>(base + byte_addr);
 }
 
-// Sum of the two halves returned by a permlane swap.  The halves are taken as
-// plain scalars first: bit-casting an element of the builtin's two-element result
-// directly reads element 0 twice with this compiler.
-__device__ __forceinline__ float swap_sum(uint32_t lo, uint32_t hi) {
-    return __builtin_bit_cast(float, lo) + __builtin_bit_cast(float, hi);
-}
-
-// sum over the 64 lanes of 16 values v[0..15]; afterwards lane l holds the total of
-// value (l >> 2).
-__device__ __forceinline__ float transpose_reduce16(float v[16], int lane) {
-    // lanes 0-31 keep rows 0..7, lanes 32-63 keep rows 8..15
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const auto s = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, v[i]),
-                                                        __builtin_bit_cast(uint32_t, v[i + 8]),
-                                                        false, false);
-        v[i] = swap_sum(s[0], s[1]);
-    }
-    // bit 4 of the lane selects rows i or i+4
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const auto s = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, v[i]),
-                                                        __builtin_bit_cast(uint32_t, v[i + 4]),
-                                                        false, false);
-        v[i] = swap_sum(s[0], s[1]);
-    }
-    // bit 3: pair with the mirrored lane of the 16-lane row
-    const bool b3 = lane & 8;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const float send = b3 ? v[i] : v[i + 2];
-        const float keep = b3 ? v[i + 2] : v[i];
-        v[i] = keep + dpp_f<0x140>(send);       // row_mirror
-    }
-    // bit 2: pair with the mirrored lane of the 8-lane half row
-    const bool b2 = lane & 4;
-    {
-        const float send = b2 ? v[0] : v[1];
-        const float keep = b2 ? v[1] : v[0];
-        v[0] = keep + dpp_f<0x141>(send);       // row_half_mirror
-    }
-    float t = v[0];
-    t += dpp_f<0xB1>(t);                         // xor 1
-    t += dpp_f<0x4E>(t);                         // xor 2
-    return t;
-}
-
 __global__ void __launch_bounds__(kLutWaves * kWave)
 lut_kernel(const uint16_t *__restrict__ codes, const uint16_t *__restrict__ cb,
            const uint16_t *__restrict__ x, float *__restrict__ partial, int out, int G,
@@ -157,7 +110,7 @@ lut_kernel(const uint16_t *__restrict__ codes, const uint16_t *__restrict__ cb,
             const uint32_t a1 = __builtin_amdgcn_perm(lanebase, c, 0x0C060104u);
             v[r] = lds_f32(lut, a0) + lds_f32(lut, a1);
         }
-        const float s = transpose_reduce16(v, lane);
+        const float s = transpose_reduce<kReduceRows>(v, lane);
         const int r = h * kReduceRows + (lane >> 2);
         if ((lane & 3) == 0 && r < w_rows) partial[size_t(slice) * out + w_begin + r] = s;
     }

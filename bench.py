@@ -7,7 +7,10 @@ the 1x16 scheme (one 65536-entry codebook, 16-bit codes), 2 bits per weight,
 fp16 activations, batch 1.  Codes, codebooks and activations are seeded
 synthetic data (uniform codes, N(0, 0.02^2) codebooks, N(0, 1) activations).
 
-One step = the four products (2 shapes x 2 schemes).  Every launch reads a
+One step = the four products (2 shapes x 2 schemes).  The 1x16 products use the
+library's packed-codebook entry point (codebooks stored plane-major once, at
+load time, like any weight layout); the canonical-layout call is timed beside
+it.  Every launch reads a
 different copy of codes and codebooks from a rotation set larger than twice
 the 256 MB Infinity Cache, so weights stream from HBM as in a real decode step.
 Launches are replayed from captured HIP graphs; HIP events on the launch stream
@@ -43,7 +46,7 @@ SIGMA_CB = 0.02
 CONFIG_IDS = {8: 2, 16: 3}     # seed namespace per scheme (the 2x8 and 1x16 MLP workloads)
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "hbm_traffic.md")
 KERNEL_SOURCES = {"lut": "lut.hip", "lds": "gather.hip", "l2": "l2gather.hip", "mfma": "mfma.hip",
-                  "generic": "generic.hip"}
+                  "generic": "generic.hip", "split": "dimsplit.hip"}
 
 
 def algorithmic_bytes(out, in_, K, B, batch=1):
@@ -74,8 +77,9 @@ def measured_traffic(config_name, variant):
     return None
 
 
-def build_inputs(torch, synth, copies):
-    """Device tensors: per copy, per workload entry (codes, codebooks, x); plus y buffers."""
+def build_inputs(torch, synth, aq, copies):
+    """Device tensors: per copy, per workload entry (codes, codebooks, x, problem, packed
+    codebooks or None); plus y buffers."""
     import numpy as np
     dev = torch.device("cuda:0")
     sets = []
@@ -85,8 +89,10 @@ def build_inputs(torch, synth, copies):
             p = synth.make_problem(out, in_, K, B, batch=1, sigma_cb=SIGMA_CB,
                                    config=CONFIG_IDS[B] * 10 + (0 if out > in_ else 1), copy=r)
             codes = p["codes"] if B == 8 else p["codes"].view(np.int16)
-            entry.append((torch.from_numpy(codes).to(dev), torch.from_numpy(p["codebooks"]).to(dev),
-                          torch.from_numpy(p["x"]).to(dev), p))
+            cb = torch.from_numpy(p["codebooks"]).to(dev)
+            packed = aq.pack_codebooks(cb) if B == 16 else None
+            entry.append((torch.from_numpy(codes).to(dev), cb, torch.from_numpy(p["x"]).to(dev), p,
+                          packed))
         sets.append(entry)
     ys = [torch.empty((1, out), dtype=torch.float16, device=dev) for _, out, _, _, _ in WORKLOAD]
     return sets, ys
@@ -113,7 +119,7 @@ def cpu_baseline(sets, ys_copy0, budget_s):
     t0 = time.perf_counter()
     done_bytes, reps, max_err = 0, 0, 0.0
     while True:
-        for (name, out, in_, K, B), (_, _, _, p), yg in zip(WORKLOAD, sets[0], ys_copy0):
+        for (name, out, in_, K, B), (_, _, _, p, _), yg in zip(WORKLOAD, sets[0], ys_copy0):
             yref = orc.gemv(p["codes"], p["codebooks"], p["x"], K, B)
             done_bytes += algorithmic_bytes(out, in_, K, B)
             if reps == 0:
@@ -162,16 +168,21 @@ def main():
     per_copy = sum(algorithmic_bytes(o, i, K, B) for _, o, i, K, B in WORKLOAD)
     copies = args.copies or max(2, math.ceil(2 * MALL_BYTES / per_copy))
     t_gen = time.perf_counter()
-    sets, ys = build_inputs(torch, synth, copies)
+    sets, ys = build_inputs(torch, synth, aq, copies)
     torch.cuda.synchronize()
     print(f"[bench] {copies} rotation copies, {per_copy * copies / 2**20:.0f} MiB, "
           f"built in {time.perf_counter() - t_gen:.1f} s", file=sys.stderr, flush=True)
 
-    def call(entry_idx, r):
-        codes, cb, x, _ = sets[r][entry_idx]
-        aq.gemv(codes, cb, x, out=ys[entry_idx])
+    def call(entry_idx, r, canonical=False):
+        codes, cb, x, _, packed = sets[r][entry_idx]
+        if packed is not None and not canonical:
+            aq.gemv_packed(codes, packed, x, out=ys[entry_idx])
+        else:
+            aq.gemv(codes, cb, x, out=ys[entry_idx])
 
-    variants = [aq.selected_variant(*sets[0][i][:3]) for i in range(len(WORKLOAD))]
+    variants = ["split" if sets[0][i][4] is not None else aq.selected_variant(*sets[0][i][:3])
+                for i in range(len(WORKLOAD))]
+    canonical_variants = [aq.selected_variant(*sets[0][i][:3]) for i in range(len(WORKLOAD))]
 
     # one stream for warmup, capture, replay and events: the warmup's eager calls
     # give it the lookup kernel's workspace before anything is captured
@@ -181,9 +192,11 @@ def main():
         for s in range(args.warmup):
             for i in range(len(WORKLOAD)):
                 call(i, s % copies)
+                call(i, s % copies, canonical=True)
     torch.cuda.synchronize()
     with torch.cuda.stream(stream):
-        return _timed(args, torch, np, aq, sets, ys, copies, per_copy, call, variants, stream)
+        return _timed(args, torch, np, aq, sets, ys, copies, per_copy, call, variants, stream,
+                      canonical_variants)
 
 
 def capture_on(torch, stream, fn):
@@ -193,7 +206,8 @@ def capture_on(torch, stream, fn):
     return g
 
 
-def _timed(args, torch, np, aq, sets, ys, copies, per_copy, call, variants, stream):
+def _timed(args, torch, np, aq, sets, ys, copies, per_copy, call, variants, stream,
+           canonical_variants):
 
     def steps_fn(nsteps):
         def f():
@@ -234,6 +248,13 @@ def _timed(args, torch, np, aq, sets, ys, copies, per_copy, call, variants, stre
             gw = capture_on(torch, stream, lambda i=i: [call(i, 0) for _ in range(copies)])
             dtw = time_graph(torch, gw, launches // copies) / ((launches // copies) * copies)
             rec["us_per_call_cache_resident"] = round(dtw * 1e6, 3)
+        if sets[0][i][4] is not None:       # also the canonical-layout call
+            gc = capture_on(torch, stream,
+                            lambda i=i: [call(i, r, canonical=True) for r in range(copies)])
+            dtc = time_graph(torch, gc, launches // copies) / ((launches // copies) * copies)
+            rec["canonical_layout"] = {"variant": canonical_variants[i],
+                                       "us_per_call": round(dtc * 1e6, 3),
+                                       "gbps": round(nbytes / dtc / 1e9, 1)}
         per_call.append(rec)
         print(f"[bench] {name} ({variants[i]}): {rec['us_per_call']} us, {rec['gbps']} GB/s",
               file=sys.stderr, flush=True)
@@ -258,7 +279,7 @@ def _timed(args, torch, np, aq, sets, ys, copies, per_copy, call, variants, stre
                                "2x8 and 1x16 (2 bits/weight), batch 1",
                    "batch": 1, "rotation_copies": copies,
                    "rotation_bytes": per_copy * copies, "launch": "hip graph replay",
-                   "step": "4 products (2 shapes x 2 schemes)"},
+                   "step": "4 products (2 shapes x 2 schemes); 1x16 with packed codebooks"},
         "per_call": per_call,
         "roofline": roofline,
     }

@@ -29,10 +29,11 @@
  * Calls are asynchronous: work is enqueued on `stream` (a hipStream_t; NULL is
  * the default stream) and the call returns before it finishes.  The library
  * keeps no pointer to caller memory after a call returns.  Memory: the only
- * allocation is a workspace for the batch-1 2x8 lookup-table kernel
- * (out x ceil(in/512) fp32 partial sums), one per (device, stream), made on
- * the first such call on that stream, grown when a larger shape needs it and
- * kept until the process exits.  Calls on different streams may run
+ * allocation is one workspace per (device, stream) for kernels that sum partial
+ * results in a second pass (the batch-1 2x8 lookup-table kernel: out x
+ * ceil(in/512) fp32; aqlm_gemv_packed: K*8 x batch x out fp32), made on the
+ * first such call on that stream, grown when a larger shape needs it and kept
+ * until the process exits.  Calls on different streams may run
  * concurrently.  On a stream that is being captured into a HIP graph and has no
  * workspace yet, that product runs on the workspace-free gather kernel instead
  * (same result within the stated tolerance); make one call on the stream
@@ -70,7 +71,9 @@ typedef enum {
     AQLM_VARIANT_LDS = 2,     /* B = 8: codebooks staged in LDS, gather + fp32 dot, batch<=8 */
     AQLM_VARIANT_LUT = 3,     /* K = 2, B = 8, batch 1: per-group codebook.x lookup tables   */
     AQLM_VARIANT_L2 = 4,      /* B = 16: codebook gathered through L2, batch <= 8            */
-    AQLM_VARIANT_MFMA = 5     /* decode to fp16 fragments + fp16 matrix cores, any batch     */
+    AQLM_VARIANT_MFMA = 5,    /* decode to fp16 fragments + fp16 matrix cores, any batch     */
+    AQLM_VARIANT_SPLIT = 6    /* B = 16, packed codebooks: one codebook position per CU,
+                                 batch <= 4 (aqlm_gemv_packed only)                        */
 } aqlm_variant_t;
 
 /*
@@ -118,6 +121,33 @@ int aqlm_selected_variant(int gemm, const void *codes, const void *codebooks, co
 aqlm_status_t aqlm_dequantize(const void *codes, const void *codebooks, void *W, int w_dtype,
                               int64_t out_features, int64_t in_features, int K, int B,
                               void *stream);
+
+/*
+ * Packed codebook layout for 16-bit codes: plane-major [K][8][2^B] fp16, i.e.
+ * packed[k][t][c] = codebooks[k][c][t].  Same bytes as the codebooks; a one-time
+ * change of the weights' layout (not part of the product).  It lets a CU keep
+ * one position of a 65536-entry codebook (128 KiB) in LDS.  B in {8, 16};
+ * `packed` must not overlap `codebooks`.
+ */
+aqlm_status_t aqlm_pack_codebooks(const void *codebooks, void *packed, int K, int B, void *stream);
+
+/* Exact inverse of aqlm_pack_codebooks. */
+aqlm_status_t aqlm_unpack_codebooks(const void *packed, void *codebooks, int K, int B,
+                                    void *stream);
+
+/*
+ * The product of aqlm_gemv with the codebooks given packed (aqlm_pack_codebooks).
+ * For 16-bit codes with K in {1,2} and batch <= 4 it runs the position-split
+ * kernel (AQLM_VARIANT_SPLIT): the K*8 codebook planes live in the LDS of K*8
+ * workgroups per row range and a second kernel adds their partial sums.  Other
+ * arguments are unpacked into the stream's workspace and run as aqlm_gemv.
+ * Uses the per-(device, stream) workspace (K*8*batch*out fp32, or the unpacked
+ * codebooks); on a capturing stream without a large enough workspace it
+ * returns AQLM_ERR_UNSUPPORTED (make one call on the stream first).
+ */
+aqlm_status_t aqlm_gemv_packed(const void *codes, const void *packed_codebooks, const void *x,
+                               void *y, int64_t out_features, int64_t in_features, int K, int B,
+                               int batch, void *stream);
 
 /* K*B/group bits per weight (bitrate formula of the decode section). */
 double aqlm_bits_per_weight(int K, int B, int group);

@@ -56,8 +56,8 @@ def test_sizes(lib):
 def test_strings(lib):
     for s in range(4):
         assert lib.aqlm_status_string(s)
-    names = [lib.aqlm_variant_name(v).decode() for v in range(6)]
-    assert names == ["auto", "generic", "lds", "lut", "l2", "mfma"]
+    names = [lib.aqlm_variant_name(v).decode() for v in range(7)]
+    assert names == ["auto", "generic", "lds", "lut", "l2", "mfma", "split"]
     assert lib.aqlm_variant_name(99) == b"unknown"
     assert lib.aqlm_version()
 
@@ -97,6 +97,16 @@ def test_dequantize_invalid(lib):
     assert lib.aqlm_dequantize(C, CB, C, 0, 16, 64, 2, 8, None) == 1    # W overlaps codes
     assert lib.aqlm_dequantize(C, CB, Y + 2, 0, 16, 64, 2, 8, None) == 1  # fp32 W misaligned
     assert lib.aqlm_dequantize(0, CB, Y, 0, 16, 64, 2, 8, None) == 1
+
+
+def test_pack_invalid(lib):
+    assert lib.aqlm_pack_codebooks(0, Y, 1, 16, None) == 1
+    assert lib.aqlm_pack_codebooks(CB, Y, 0, 16, None) == 1
+    assert lib.aqlm_pack_codebooks(CB, Y, 1, 12, None) == 1
+    assert lib.aqlm_pack_codebooks(CB, CB + 64, 1, 16, None) == 1     # overlapping
+    assert lib.aqlm_unpack_codebooks(CB + 1, Y, 1, 16, None) == 1     # misaligned
+    assert lib.aqlm_gemv_packed(0, CB, X, Y, 16, 64, 1, 16, 1, None) == 1
+    assert lib.aqlm_gemv_packed(C, CB, X, Y, 16, 60, 1, 16, 1, None) == 1
 
 
 def test_variant_choice_host_logic(lib):

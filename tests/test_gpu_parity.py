@@ -298,3 +298,81 @@ def test_capture_without_workspace_falls_back(aq, orc):
         g.replay()
         torch.cuda.synchronize()
         check_y(y, yref, "captured fallback")
+
+
+# ------------------------------------------------------------ packed codebooks
+
+@pytest.mark.parametrize("KB", [(1, 16), (2, 16), (2, 8)])
+def test_pack_unpack_exact(aq, KB):
+    import torch
+    K, B = KB
+    p = synth.make_problem(8, 64, K, B, sigma_cb=0.02, config=1400 + K)
+    cb = torch.from_numpy(p["codebooks"]).cuda()
+    P = aq.pack_codebooks(cb)
+    torch.cuda.synchronize()
+    assert np.array_equal(P.cpu().numpy().view(np.uint16),
+                          np.ascontiguousarray(p["codebooks"].transpose(0, 2, 1)).view(np.uint16))
+    assert np.array_equal(aq.unpack_codebooks(P).cpu().numpy().view(np.uint16),
+                          p["codebooks"].view(np.uint16))
+
+
+PACKED = [
+    # out, in, K, B, batch
+    (300, 4096, 1, 16, 1), (65, 520, 1, 16, 1), (1, 64, 1, 16, 1), (257, 11008, 1, 16, 1),
+    (130, 2048, 1, 16, 2), (77, 1024, 1, 16, 3), (160, 8192, 1, 16, 4), (96, 512, 2, 16, 1),
+    (50, 1024, 2, 16, 4), (64, 512, 1, 16, 8), (40, 512, 2, 8, 1), (1000, 28672, 1, 16, 1),
+]
+
+
+@pytest.mark.parametrize("case", PACKED, ids=lambda c: "x".join(map(str, c)))
+def test_gemv_packed(aq, orc, case):
+    out, in_, K, B, batch = case
+    p = synth.make_problem(out, in_, K, B, batch=batch, sigma_cb=0.02, config=1500 + out + in_)
+    codes, cb, x = _dev(p)
+    P = aq.pack_codebooks(cb)
+    yref = orc.gemv(p["codes"], p["codebooks"], p["x"], K, B)
+    ys = [aq.gemv_packed(codes, P, x) for _ in range(2)]
+    check_y(ys[0], yref, f"packed {case}")
+    assert bool((ys[0] == ys[1]).all())      # planes are summed in a fixed order
+
+
+@pytest.mark.parametrize("case", [("mlp_1x16_7b", 11008, 4096, 1), ("mlp_1x16_7b", 4096, 11008, 1),
+                                  ("mlp_1x16_70b", 28672, 8192, 4), ("mlp_1x16_70b", 8192, 28672, 1),
+                                  ("proj_1x16_4096", 4096, 4096, 1)],
+                         ids=lambda c: f"{c[0]}-{c[1]}x{c[2]}-b{c[3]}")
+def test_full_size_packed_sampled(aq, orc, case):
+    import torch
+    name, out, in_, batch = case
+    cfg = synth.CONFIGS[name]
+    cid = list(synth.CONFIGS).index(name)
+    p = synth.make_problem(out, in_, cfg["K"], cfg["B"], batch=batch, sigma_cb=cfg["sigma_cb"],
+                           config=cid)
+    codes, cb, x = _dev(p)
+    y = aq.gemv_packed(codes, aq.pack_codebooks(cb), x)
+    torch.cuda.synchronize()
+    rows = _sampled_rows(out, seed=cid)
+    yref = orc.gemv_rows(p["codes"], p["codebooks"], p["x"], cfg["K"], cfg["B"], rows)
+    e = rel_err(y.float().cpu().numpy()[:, rows], yref)
+    assert np.all(e <= TOL), f"{case}: {e.max():.3e}"
+
+
+def test_packed_graph_replay(aq, orc):
+    import torch
+    p = synth.make_problem(2000, 4096, 1, 16, batch=1, sigma_cb=0.02, config=1600)
+    codes, cb, x = _dev(p)
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        P = aq.pack_codebooks(cb)
+        eager = aq.gemv_packed(codes, P, x).clone()
+        y = torch.empty_like(eager)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            aq.gemv_packed(codes, P, x, out=y)
+        for _ in range(3):
+            y.fill_(3.0)
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            assert bool((y == eager).all())
+    check_y(eager, orc.gemv(p["codes"], p["codebooks"], p["x"], 1, 16), "packed eager")
