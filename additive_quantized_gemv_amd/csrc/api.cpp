@@ -204,7 +204,21 @@ aqlm_status_t run(int variant, const aqlm::Problem &p) {
             }
             break;
         }
-        case AQLM_VARIANT_MFMA: e = aqlm::launch_mfma(p); break;
+        case AQLM_VARIANT_MFMA: {
+            const size_t need = aqlm::mfma_workspace_bytes(p);
+            void *ws = nullptr;
+            if (need) {
+                e = get_workspace(p.stream, need, &ws);
+                if (e != hipSuccess) break;
+                if (!ws) {
+                    // capturing stream without a workspace: same product, no workspace needed
+                    e = aqlm::launch_generic(p);
+                    break;
+                }
+            }
+            e = aqlm::launch_mfma(p, ws);
+            break;
+        }
         default: e = aqlm::launch_generic(p); break;
     }
     if (e != hipSuccess) {

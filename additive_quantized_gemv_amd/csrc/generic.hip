@@ -94,7 +94,31 @@ dequantize_kernel(const void *__restrict__ codes, const uint16_t *__restrict__ c
     }
 }
 
+// y[i] = sum over parts (in order) of partial[part][i], rounded to fp16; the
+// loads are issued eight parts at a time.
+__global__ void __launch_bounds__(256)
+partial_sum_kernel(const float *__restrict__ partial, uint16_t *__restrict__ y, int64_t n,
+                   int parts) {
+    const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    float s = 0.0f;
+    for (int p0 = 0; p0 < parts; p0 += 8) {
+        float v[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) v[q] = (p0 + q < parts) ? partial[int64_t(p0 + q) * n + i] : 0.0f;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) s += v[q];
+    }
+    y[i] = f2h_bits(s);
+}
+
 }  // namespace
+
+hipError_t launch_partial_sum(const float *partial, void *y, int64_t n, int parts, hipStream_t s) {
+    hipLaunchKernelGGL(partial_sum_kernel, dim3(unsigned((n + 255) / 256)), dim3(256), 0, s,
+                       partial, static_cast<uint16_t *>(y), n, parts);
+    return hipGetLastError();
+}
 
 hipError_t launch_generic(const Problem &p) {
     const int waves_per_block = 4;

@@ -24,6 +24,9 @@ struct Problem {
 // Generic: any K in 1..8, B in {8,16}, any batch, any in % 8 == 0.
 hipError_t launch_generic(const Problem &p);
 
+// y[i] = fp16(sum over parts of partial[part][i]) for i < n (parts summed in order).
+hipError_t launch_partial_sum(const float *partial, void *y, int64_t n, int parts, hipStream_t s);
+
 // Dense W (fp32 when w_fp16 == 0, fp16 otherwise).
 hipError_t launch_dequantize(const Problem &p, void *W, int w_fp16);
 
@@ -47,8 +50,10 @@ hipError_t launch_ds(const Problem &p, void *workspace);
 hipError_t launch_pack_codebooks(const void *cb, void *planes, int K, int B, hipStream_t s);
 hipError_t launch_unpack_codebooks(const void *planes, void *cb, int K, int B, hipStream_t s);
 
-// Decode-to-fp16 fragments + MFMA, K in {1,2}, B in {8,16}, any batch.
+// Decode-to-fp16 fragments + MFMA, K in {1,2}, B in {8,16}, any batch; the input
+// axis may be split over workgroups (partial tiles in the workspace).
 bool mfma_supported(const Problem &p);
-hipError_t launch_mfma(const Problem &p);
+size_t mfma_workspace_bytes(const Problem &p);
+hipError_t launch_mfma(const Problem &p, void *workspace);
 
 }  // namespace aqlm

@@ -55,7 +55,6 @@ lut_kernel(const uint16_t *__restrict__ codes, const uint16_t *__restrict__ cb,
     const int rblock = blockIdx.x / nslices;
     const int j0 = slice * kSlice;
     const int jl = lane;
-    const bool jvalid = j0 + jl < G;
     const int r_begin = rblock * rows_per_block;
     const int r_end = min(out, r_begin + rows_per_block);
     // this wave's rows: a contiguous run of rows_per_block / kLutWaves (<= kRowsPerWave)
@@ -63,35 +62,38 @@ lut_kernel(const uint16_t *__restrict__ codes, const uint16_t *__restrict__ cb,
     const int w_begin = r_begin + wave * rpw;
     const int w_rows = max(0, min(rpw, r_end - w_begin));
 
-    // issue every code load of this wave before building the tables, so the
-    // whole wave waits for HBM once
+    // ---- build L[e][jl] = C[e] . x_{j0+jl} for the 512 entries e = k*256 + c
+    // wave w computes entries 32w .. 32w+31 for both 32-group halves of the slice.
+    // Its (L2-resident) operands are loaded before the code stream: loads complete
+    // in issue order, so the tables are built while the codes are still in flight.
+    const int e = wave * 32 + (lane & 31);
+    const int kq = (lane >> 5) * 4;              // this lane's 4 of the 8 vector positions
+    const half4 a = *reinterpret_cast<const half4 *>(cb + size_t(e) * kGroup + kq);
+    half4 bx[2];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+        const int j = min(j0 + nb * 32 + (lane & 31), G - 1);
+        bx[nb] = *reinterpret_cast<const half4 *>(x + size_t(j) * kGroup + kq);
+        if (j0 + nb * 32 + (lane & 31) >= G) bx[nb] = half4{0, 0, 0, 0};
+    }
+
+    // then every code load of this wave (up to 32 rows): the wave waits for HBM once
     uint32_t code[kRowsPerWave];
 #pragma unroll
     for (int r = 0; r < kRowsPerWave; ++r) {
-        code[r] = 0u;
-        if (jvalid && r < w_rows)
-            code[r] = uint32_t(__builtin_nontemporal_load(codes + size_t(w_begin + r) * G + j0 + jl));
+        const int row = min(w_begin + min(r, max(w_rows - 1, 0)), out - 1);
+        code[r] = uint32_t(__builtin_nontemporal_load(codes + size_t(row) * G + min(j0 + jl, G - 1)));
     }
 
-    // ---- build L[e][jl] = C[e] . x_{j0+jl} for the 512 entries e = k*256 + c
-    // wave w computes entries 32w .. 32w+31 for both 32-group halves of the slice
-    {
-        const int e = wave * 32 + (lane & 31);
-        const int kq = (lane >> 5) * 4;          // this lane's 4 of the 8 vector positions
-        const half4 a = *reinterpret_cast<const half4 *>(cb + size_t(e) * kGroup + kq);
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
-            const int j = j0 + nb * 32 + (lane & 31);
-            half4 bx = {0, 0, 0, 0};
-            if (j < G) bx = *reinterpret_cast<const half4 *>(x + size_t(j) * kGroup + kq);
-            float16v d = {};
-            d = __builtin_amdgcn_mfma_f32_32x32x8f16(a, bx, d, 0, 0, 0);
+    for (int nb = 0; nb < 2; ++nb) {
+        float16v d = {};
+        d = __builtin_amdgcn_mfma_f32_32x32x8f16(a, bx[nb], d, 0, 0, 0);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int m = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                const int n = nb * 32 + (lane & 31);
-                *reinterpret_cast<float *>(lut + (wave * 32 + m) * 256 + n * 4) = d[r];
-            }
+        for (int r = 0; r < 16; ++r) {
+            const int m = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+            const int n = nb * 32 + (lane & 31);
+            *reinterpret_cast<float *>(lut + (wave * 32 + m) * 256 + n * 4) = d[r];
         }
     }
     __syncthreads();

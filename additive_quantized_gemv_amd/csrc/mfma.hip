@@ -12,9 +12,14 @@
 //   fp16 rounding of the fp32 fold because fp32 carries more than 2*11+2 bits
 //   (double rounding through fp32 is innocuous for one fp16 addition).
 // * B = 8 codebooks are staged in LDS; the B = 16 codebook is read through L2.
-// * A workgroup is 4 waves on one tile of MS rows x (MS*NT) tokens; the waves
-//   split the input axis four ways and their accumulators are summed in LDS,
-//   so a 4096-row layer still yields 256+ workgroups.
+// * Workgroup = 4 waves on 4*MS consecutive rows x (MS*NT) tokens.  Waves own
+//   different rows and share the activations: chunks of CHG groups x all tokens
+//   are staged in LDS (double-buffered, rows padded by 16 B so the B-fragment
+//   reads of one instruction hit different banks).  While the MFMAs of chunk c
+//   run, the activations of chunk c+1 are loaded and its A fragments decoded.
+// * The input axis is split over KSPLIT workgroups so that every product fills
+//   the 256 CUs; partial tiles (fp32) go to a workspace and a second kernel adds
+//   the splits in order.  With KSPLIT = 1 the tile is written to y directly.
 // * MFMA operand layout used: A lane l = row (l % MS), k-block (l / MS);
 //   B lane l = token (l % MS), same k-block.  Both operands place the same 8
 //   inputs in a lane, so the product does not depend on how the hardware orders
@@ -68,116 +73,213 @@ __device__ __forceinline__ uint32_t block_code(const typename CodeBlock<K, BITS>
     }
 }
 
+template <int MS, int NT> struct Tile {
+    static constexpr int KB = 64 / MS;               // k-blocks (8 inputs) per MFMA
+    static constexpr int SS = KB * 4;                // groups per super-step (4 k-steps)
+    static constexpr int BN = MS * NT;               // tokens per workgroup
+    static constexpr int CHG = MS == 16 ? 32 : 16;   // groups per staged chunk
+    static constexpr int SPC = CHG / SS;             // super-steps per chunk
+    static constexpr int XROW = CHG * 8 + 8;         // halves per staged token row (+16 B pad)
+    static constexpr int XBUF = BN * XROW;           // halves per chunk buffer
+    static constexpr int XLOADS = BN * CHG / (kMfmaWaves * kWave);   // 16-B loads per thread
+};
+
 template <int K, int BITS, int MS, int NT>
 __global__ void __launch_bounds__(kMfmaWaves * kWave)
 mfma_kernel(const uint8_t *__restrict__ codes, const uint16_t *__restrict__ cb,
-            const uint16_t *__restrict__ x, uint16_t *__restrict__ y, int out, int in, int batch) {
+            const uint16_t *__restrict__ x, uint16_t *__restrict__ y, float *__restrict__ partial,
+            int out, int in, int batch, int groups_per_split) {
+    typedef Tile<MS, NT> T;
     typedef typename Acc<MS>::type acc_t;
     typedef typename CodeBlock<K, BITS>::type cblock_t;
-    constexpr int KB = 64 / MS;            // k-blocks (of 8 inputs) per MFMA
-    constexpr int SS = KB * 4;             // groups per super-step (4 MFMA k-steps)
     constexpr int CBE = BITS == 8 ? K * 256 : 0;
     constexpr int NACC = Acc<MS>::n;
+    constexpr int STEPS = T::SPC * 4;                // MFMA k-steps per chunk
     __shared__ uint4 cbs[CBE > 0 ? CBE : 1];
-    __shared__ float red[(kMfmaWaves - 1) * NT * NACC * kWave];
+    __shared__ __attribute__((aligned(16))) uint16_t xs[2][T::XBUF];
 
     const int lane = threadIdx.x & (kWave - 1);
-    const int wave = threadIdx.x / kWave;
-    for (int i = threadIdx.x; i < CBE; i += blockDim.x)
-        cbs[i] = reinterpret_cast<const uint4 *>(cb)[i];
-    if (CBE) __syncthreads();
-
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int G = in / kGroup;
-    const int row0 = blockIdx.x * MS;
-    const int tok0 = blockIdx.y * (MS * NT);
+    const int row0 = blockIdx.x * (kMfmaWaves * MS) + wave * MS;
+    const int tok0 = blockIdx.y * T::BN;
+    const int split = blockIdx.z;
+    const int g_begin = split * groups_per_split;
+    const int g_end = min(G, g_begin + groups_per_split);
+    const int nchunks = (g_end - g_begin + T::CHG - 1) / T::CHG;
+
     const int m = lane % MS;
     const int kb = lane / MS;
-    const int o = row0 + m;
-    const bool row_ok = o < out;
-    const cblock_t *crow = reinterpret_cast<const cblock_t *>(codes + size_t(row_ok ? o : 0) *
-                                                              size_t(G) * (K * BITS / 8));
+    const int o = min(row0 + m, out - 1);            // rows past the end are computed, not stored
+    const cblock_t *crow = reinterpret_cast<const cblock_t *>(
+        codes + size_t(o) * size_t(G) * (K * BITS / 8));
     const uint4 *cbg = reinterpret_cast<const uint4 *>(cb);
+
+    for (int i = threadIdx.x; i < CBE; i += blockDim.x)
+        cbs[i] = reinterpret_cast<const uint4 *>(cb)[i];
+
+    // activations of chunk c: token n, group g_begin + c*CHG + jj -> xs[buf][n*XROW + jj*8]
+    auto load_x = [&](int c, uint4 (&r)[T::XLOADS]) {
+#pragma unroll
+        for (int i = 0; i < T::XLOADS; ++i) {
+            const int e = threadIdx.x + i * (kMfmaWaves * kWave);
+            const int n = e / T::CHG, jj = e % T::CHG;
+            const int j = g_begin + c * T::CHG + jj;
+            const int tn = tok0 + n;
+            r[i] = make_uint4(0, 0, 0, 0);
+            if (tn < batch && j < g_end)
+                r[i] = *reinterpret_cast<const uint4 *>(x + size_t(tn) * in + size_t(j) * kGroup);
+        }
+    };
+    auto store_x = [&](int buf, const uint4 (&r)[T::XLOADS]) {
+#pragma unroll
+        for (int i = 0; i < T::XLOADS; ++i) {
+            const int e = threadIdx.x + i * (kMfmaWaves * kWave);
+            const int n = e / T::CHG, jj = e % T::CHG;
+            *reinterpret_cast<uint4 *>(&xs[buf][n * T::XROW + jj * 8]) = r[i];
+        }
+    };
+    // A fragments of chunk c: super-step q, k-step s -> group g_begin + c*CHG + q*SS + 4*kb + s.
+    // gather() only issues the codebook reads (raw vectors); fold() adds the K
+    // vectors and masks groups past the split, after the current chunk's MFMAs,
+    // so L2 latency of the 16-bit codebook overlaps with them.
+    auto gather = [&](int c, uint4 (&v0)[STEPS], uint4 (&v1)[STEPS], bool (&ok)[T::SPC]) {
+#pragma unroll
+        for (int q = 0; q < T::SPC; ++q) {
+            const int jb = g_begin + c * T::CHG + q * T::SS + 4 * kb;
+            ok[q] = jb < g_end;                      // g_end - g_begin is a multiple of 4
+            const cblock_t cw = __builtin_nontemporal_load(crow + min(jb, G - 4) / 4);
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const uint32_t c0 = block_code<K, BITS>(cw, s * K);
+                v0[q * 4 + s] = BITS == 8 ? cbs[c0] : cbg[c0];
+                if constexpr (K == 2) {
+                    const uint32_t c1 = block_code<K, BITS>(cw, s * K + 1);
+                    v1[q * 4 + s] = BITS == 8 ? cbs[256 + c1] : cbg[(1u << 16) + c1];
+                }
+            }
+        }
+    };
+    auto fold = [&](const uint4 (&v0)[STEPS], const uint4 (&v1)[STEPS], const bool (&ok)[T::SPC],
+                    half8 (&a)[STEPS]) {
+#pragma unroll
+        for (int st = 0; st < STEPS; ++st) {
+            half8 f = __builtin_bit_cast(half8, v0[st]);
+            if constexpr (K == 2) f = f + __builtin_bit_cast(half8, v1[st]);
+            a[st] = ok[st / 4] ? f : half8{};
+        }
+    };
 
     acc_t acc[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc[t] = acc_t{};
 
-    const int nsuper = (G + SS - 1) / SS;
-    for (int q = wave; q < nsuper; q += kMfmaWaves) {
-        const int jb = q * SS + 4 * kb;    // first of this lane's 4 groups
-        const bool blk_ok = row_ok && jb < G;
-        cblock_t cw{};
-        if (blk_ok) cw = __builtin_nontemporal_load(crow + jb / 4);
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            const int j = jb + s;
-            half8 a = {};
-            if (blk_ok) {
-                uint4 v0;
-                const uint32_t c0 = block_code<K, BITS>(cw, s * K);
-                v0 = BITS == 8 ? cbs[c0] : cbg[c0];
-                if constexpr (K == 1) {
-                    a = __builtin_bit_cast(half8, v0);
-                } else {
-                    const uint32_t c1 = block_code<K, BITS>(cw, s * K + 1);
-                    const uint4 v1 = BITS == 8 ? cbs[256 + c1] : cbg[(1u << 16) + c1];
-                    a = __builtin_bit_cast(half8, v0) + __builtin_bit_cast(half8, v1);
-                }
-            }
-#pragma unroll
-            for (int t = 0; t < NT; ++t) {
-                const int n = tok0 + t * MS + m;
-                half8 b = {};
-                if (n < batch && jb < G)
-                    b = *reinterpret_cast<const half8 *>(x + size_t(n) * in + size_t(j) * kGroup);
-                acc[t] = mfma<MS>(a, b, acc[t]);
-            }
-        }
+    uint4 xr[T::XLOADS];
+    half8 acur[STEPS];
+    uint4 g0[STEPS], g1[STEPS];                  // g1 only used when K = 2
+    bool gok[T::SPC];
+    if (nchunks > 0) {
+        load_x(0, xr);
+        if constexpr (BITS == 16) gather(0, g0, g1, gok);
     }
-
-    // sum the four waves' partial tiles
-    if (wave > 0) {
-#pragma unroll
-        for (int t = 0; t < NT; ++t)
-#pragma unroll
-            for (int r = 0; r < NACC; ++r)
-                red[(((wave - 1) * NT + t) * NACC + r) * kWave + lane] = acc[t][r];
+    if (CBE) __syncthreads();                        // codebooks staged
+    if (nchunks > 0) {
+        if constexpr (BITS == 8) gather(0, g0, g1, gok);   // LDS codebooks are ready only now
+        store_x(0, xr);
+        fold(g0, g1, gok, acur);
     }
     __syncthreads();
-    if (wave != 0) return;
+
+    for (int c = 0; c < nchunks; ++c) {
+        const int buf = c & 1;
+        const bool more = c + 1 < nchunks;
+        if (more) {
+            load_x(c + 1, xr);
+            gather(c + 1, g0, g1, gok);
+        }
+        const uint16_t *xb = xs[buf];
+#pragma unroll
+        for (int st = 0; st < STEPS; ++st) {
+            const int q = st / 4, s = st % 4;
+            const int jj = q * T::SS + 4 * kb + s;   // group inside the chunk (same as A)
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                const half8 b = *reinterpret_cast<const half8 *>(
+                    &xb[(t * MS + m) * T::XROW + jj * 8]);
+                acc[t] = mfma<MS>(acur[st], b, acc[t]);
+            }
+        }
+        if (more) {
+            store_x(buf ^ 1, xr);
+            fold(g0, g1, gok, acur);
+        }
+        __syncthreads();
+    }
+
+    // epilogue: partial tile (KSPLIT > 1) or y
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
 #pragma unroll
         for (int r = 0; r < NACC; ++r) {
-            float s = acc[t][r];
-#pragma unroll
-            for (int w = 1; w < kMfmaWaves; ++w) s += red[(((w - 1) * NT + t) * NACC + r) * kWave + lane];
             const int row = row0 + out_row<MS>(lane, r);
             const int n = tok0 + t * MS + (lane % MS);
-            if (row < out && n < batch) y[size_t(n) * out + row] = f2h_bits(s);
+            if (row < out && n < batch) {
+                if (partial)
+                    partial[(size_t(split) * batch + n) * out + row] = acc[t][r];
+                else
+                    y[size_t(n) * out + row] = f2h_bits(acc[t][r]);
+            }
         }
     }
 }
 
+struct MfmaCfg {
+    int ms, nt, ksplit, groups_per_split, grid_x, grid_y;
+};
+
+MfmaCfg mfma_cfg(const Problem &p) {
+    MfmaCfg c{};
+    if (p.batch <= 16) { c.ms = 16; c.nt = 1; }
+    else if (p.batch <= 32) { c.ms = 32; c.nt = 1; }
+    else if (p.batch <= 64) { c.ms = 32; c.nt = 2; }
+    else { c.ms = 32; c.nt = 4; }
+    const int64_t G = p.in / kGroup;
+    const int chg = c.ms == 16 ? 32 : 16;
+    c.grid_x = int((p.out + kMfmaWaves * c.ms - 1) / (kMfmaWaves * c.ms));
+    c.grid_y = (p.batch + c.ms * c.nt - 1) / (c.ms * c.nt);
+    const int64_t tiles = int64_t(c.grid_x) * c.grid_y;
+    const int64_t nchunks = (G + chg - 1) / chg;
+    int64_t ks = (512 + tiles - 1) / tiles;          // about two workgroups per CU
+    // each split writes and re-reads batch*out fp32: keep that within twice the codes
+    const int64_t code_bytes_per_row = p.in / 4;     // 2 bits per weight
+    const int64_t cap = (2 * code_bytes_per_row) / (int64_t(p.batch) * 8);
+    if (ks > cap) ks = cap;
+    if (ks > nchunks) ks = nchunks;
+    if (ks < 1) ks = 1;
+    // whole chunks per split (multiples of 4 groups keep code blocks whole)
+    int64_t gps = (nchunks + ks - 1) / ks * chg;
+    c.ksplit = int((G + gps - 1) / gps);
+    c.groups_per_split = int(gps);
+    return c;
+}
+
 template <int K, int BITS, int MS, int NT>
-hipError_t launch_t(const Problem &p) {
-    const int grid_x = int((p.out + MS - 1) / MS);
-    const int grid_y = (p.batch + MS * NT - 1) / (MS * NT);
-    hipLaunchKernelGGL((mfma_kernel<K, BITS, MS, NT>), dim3(grid_x, grid_y),
+hipError_t launch_t(const Problem &p, const MfmaCfg &c, float *partial) {
+    hipLaunchKernelGGL((mfma_kernel<K, BITS, MS, NT>), dim3(c.grid_x, c.grid_y, c.ksplit),
                        dim3(kMfmaWaves * kWave), 0, p.stream,
                        static_cast<const uint8_t *>(p.codes),
                        static_cast<const uint16_t *>(p.codebooks),
-                       static_cast<const uint16_t *>(p.x), static_cast<uint16_t *>(p.y),
-                       int(p.out), int(p.in), p.batch);
+                       static_cast<const uint16_t *>(p.x), static_cast<uint16_t *>(p.y), partial,
+                       int(p.out), int(p.in), p.batch, c.groups_per_split);
     return hipGetLastError();
 }
 
 template <int K, int BITS>
-hipError_t launch_kb(const Problem &p) {
-    if (p.batch <= 16) return launch_t<K, BITS, 16, 1>(p);
-    if (p.batch <= 32) return launch_t<K, BITS, 32, 1>(p);
-    if (p.batch <= 64) return launch_t<K, BITS, 32, 2>(p);
-    return launch_t<K, BITS, 32, 4>(p);
+hipError_t launch_kb(const Problem &p, const MfmaCfg &c, float *partial) {
+    if (c.ms == 16) return launch_t<K, BITS, 16, 1>(p, c, partial);
+    if (c.nt == 1) return launch_t<K, BITS, 32, 1>(p, c, partial);
+    if (c.nt == 2) return launch_t<K, BITS, 32, 2>(p, c, partial);
+    return launch_t<K, BITS, 32, 4>(p, c, partial);
 }
 
 }  // namespace
@@ -195,9 +297,20 @@ bool mfma_supported(const Problem &p) {
     return (a & 15u) == 0;
 }
 
-hipError_t launch_mfma(const Problem &p) {
-    if (p.B == 8) return p.K == 1 ? launch_kb<1, 8>(p) : launch_kb<2, 8>(p);
-    return p.K == 1 ? launch_kb<1, 16>(p) : launch_kb<2, 16>(p);
+size_t mfma_workspace_bytes(const Problem &p) {
+    const MfmaCfg c = mfma_cfg(p);
+    return c.ksplit > 1 ? size_t(c.ksplit) * size_t(p.batch) * size_t(p.out) * sizeof(float) : 0;
+}
+
+// workspace: KSPLIT x batch x out fp32 partial tiles (unused when KSPLIT = 1)
+hipError_t launch_mfma(const Problem &p, void *workspace) {
+    const MfmaCfg c = mfma_cfg(p);
+    float *partial = c.ksplit > 1 ? static_cast<float *>(workspace) : nullptr;
+    hipError_t e;
+    if (p.B == 8) e = p.K == 1 ? launch_kb<1, 8>(p, c, partial) : launch_kb<2, 8>(p, c, partial);
+    else e = p.K == 1 ? launch_kb<1, 16>(p, c, partial) : launch_kb<2, 16>(p, c, partial);
+    if (e != hipSuccess || c.ksplit == 1) return e;
+    return launch_partial_sum(partial, p.y, p.batch * p.out, c.ksplit, p.stream);
 }
 
 }  // namespace aqlm

@@ -146,6 +146,12 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--warm", action="store_true", help="also time cache-resident (no rotation)")
+    ap.add_argument("--workload", default="mlp", choices=["mlp", "layer7b"],
+                    help="mlp: the batch-1 MLP products (default, the headline line); "
+                         "layer7b: the seven linears of a Llama-2-7B layer through aqlm_gemm")
+    ap.add_argument("--batch", type=int, default=16, help="tokens for --workload layer7b")
+    ap.add_argument("--scheme", default="2x8", choices=["2x8", "1x16"],
+                    help="scheme for --workload layer7b")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -164,6 +170,9 @@ def main():
         print("no GPU available", file=sys.stderr)
         sys.exit(1)
     aq._load()
+
+    if args.workload == "layer7b":
+        return layer_bench(args, torch, np, aq, synth)
 
     per_copy = sum(algorithmic_bytes(o, i, K, B) for _, o, i, K, B in WORKLOAD)
     copies = args.copies or max(2, math.ceil(2 * MALL_BYTES / per_copy))
@@ -290,6 +299,86 @@ def _timed(args, torch, np, aq, sets, ys, copies, per_copy, call, variants, stre
             torch.cuda.synchronize()
             ys_copy0.append(ys[i].float().cpu().numpy().astype(np.float64))
         result["cpu_baseline"] = cpu_baseline(sets, ys_copy0, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+LAYER_7B = [("q", 4096, 4096), ("k", 4096, 4096), ("v", 4096, 4096), ("o", 4096, 4096),
+            ("gate", 11008, 4096), ("up", 11008, 4096), ("down", 4096, 11008)]
+MFMA_PEAK_FP16_TFLOPS = 2500.0
+
+
+def layer_bench(args, torch, np, aq, synth):
+    """The seven linears of a Llama-2-7B layer at one batch size through aqlm_gemm
+    (matrix cores from batch 16), rotating over copies larger than 2x the Infinity Cache."""
+    K, B = (2, 8) if args.scheme == "2x8" else (1, 16)
+    batch = args.batch
+    dev = torch.device("cuda:0")
+    per_copy = sum(algorithmic_bytes(o, i, K, B, batch) for _, o, i in LAYER_7B)
+    copies = args.copies or max(2, math.ceil(2 * MALL_BYTES / per_copy))
+    sets = []
+    for r in range(copies):
+        entry = []
+        for li, (name, out, in_) in enumerate(LAYER_7B):
+            p = synth.make_problem(out, in_, K, B, batch=batch, sigma_cb=SIGMA_CB,
+                                   config=400 + li, copy=r)
+            codes = p["codes"] if B == 8 else p["codes"].view(np.int16)
+            entry.append((torch.from_numpy(codes).to(dev), torch.from_numpy(p["codebooks"]).to(dev),
+                          torch.from_numpy(p["x"]).to(dev)))
+        sets.append(entry)
+    ys = [torch.empty((batch, out), dtype=torch.float16, device=dev) for _, out, _ in LAYER_7B]
+    variants = [aq.selected_variant(*sets[0][i], gemm=True) for i in range(len(LAYER_7B))]
+    stream = torch.cuda.Stream()
+
+    def call(i, r):
+        aq.gemm(*sets[r][i], out=ys[i])
+
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        for w in range(max(2, args.warmup // 10)):
+            for i in range(len(LAYER_7B)):
+                call(i, w % copies)
+        torch.cuda.synchronize()
+        layer = capture_on(torch, stream, lambda: [call(i, r) for r in range(copies)
+                                                   for i in range(len(LAYER_7B))])
+        reps = max(1, args.steps // copies)
+        dt_layer = time_graph(torch, layer, reps) / (reps * copies)
+        per = []
+        for i, (name, out, in_) in enumerate(LAYER_7B):
+            g = capture_on(torch, stream, lambda i=i: [call(i, r) for r in range(copies)])
+            dt = time_graph(torch, g, reps) / (reps * copies)
+            nbytes = algorithmic_bytes(out, in_, K, B, batch)
+            flops = 2.0 * out * in_ * batch
+            per.append({"linear": name, "shape": f"{out}x{in_}", "variant": variants[i],
+                        "us_per_call": round(dt * 1e6, 3), "gbps": round(nbytes / dt / 1e9, 1),
+                        "tflops": round(flops / dt / 1e12, 2)})
+    layer_bytes = per_copy
+    layer_flops = sum(2.0 * o * i * batch for _, o, i in LAYER_7B)
+    dom = max(range(len(per)), key=lambda i: per[i]["us_per_call"])
+    d = per[dom]
+    mfma = batch >= 16
+    if mfma:
+        achieved = 2.0 * LAYER_7B[dom][1] * LAYER_7B[dom][2] * batch / (d["us_per_call"] * 1e-6) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_PEAK_FP16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / MFMA_PEAK_FP16_TFLOPS, 4),
+                "traffic": None, "kernel": f"{d['variant']} ({d['linear']} {d['shape']})"}
+    else:
+        achieved = algorithmic_bytes(LAYER_7B[dom][1], LAYER_7B[dom][2], K, B, batch) / (d["us_per_call"] * 1e-6) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                "kernel": f"{d['variant']} ({d['linear']} {d['shape']})"}
+    result = {"metric": f"AQLM {args.scheme} Llama-2-7B layer (7 linears), batch {batch}: "
+                        "layer time and achieved rates",
+              "value": round(layer_bytes / dt_layer / 1e9, 1), "unit": "GB/s",
+              "n_gpus": 1, "steps": reps * copies, "warmup": max(2, args.warmup // 10),
+              "ms_per_step": round(dt_layer * 1e3, 5), "higher_is_better": True,
+              "scaling": "weak", "vs_baseline": None,
+              "dtype": "fp16 x fp16 -> fp32 (u8/u16 codes)", "data": "synthetic",
+              "config": {"workload": f"Llama-2-7B layer linears q,k,v,o 4096x4096; gate,up "
+                                     f"11008x4096; down 4096x11008; {args.scheme}, batch {batch}",
+                         "batch": batch, "rotation_copies": copies, "launch": "hip graph replay"},
+              "layer_us": round(dt_layer * 1e6, 2),
+              "layer_tflops": round(layer_flops / dt_layer / 1e12, 2),
+              "per_linear": per, "roofline": roof}
     print(json.dumps(result), flush=True)
 
 
