@@ -17,6 +17,7 @@ import ctypes
 import os
 
 __all__ = ["gemv", "gemm", "gemv_variant", "gemv_packed", "pack_codebooks", "unpack_codebooks",
+           "pack_codes", "unpack_codes", "packed_codes_bytes", "PackedWeights", "pack_weights",
            "dequantize", "bits_per_weight", "codes_bytes",
            "codebooks_bytes", "variant_supported", "selected_variant", "VARIANTS", "library_path",
            "AqlmError", "version"]
@@ -64,6 +65,11 @@ def _load():
     lib.aqlm_selected_variant.restype = ci
     lib.aqlm_gemv_packed.argtypes = prod
     lib.aqlm_gemv_packed.restype = ci
+    lib.aqlm_packed_codes_bytes.argtypes = [i64, i64, ci, ci]
+    lib.aqlm_packed_codes_bytes.restype = i64
+    for name in ("aqlm_pack_codes", "aqlm_unpack_codes"):
+        getattr(lib, name).argtypes = [vp, vp, i64, i64, ci, ci, vp]
+        getattr(lib, name).restype = ci
     for name in ("aqlm_pack_codebooks", "aqlm_unpack_codebooks"):
         getattr(lib, name).argtypes = [vp, vp, ci, ci, vp]
         getattr(lib, name).restype = ci
@@ -167,9 +173,90 @@ def gemm(codes, codebooks, x, K=None, B=None, out=None):
     return _product("aqlm_gemm", codes, codebooks, x, K, B, out)
 
 
-def gemv_packed(codes, packed_codebooks, x, K=None, B=None, out=None):
-    """y = W x with codebooks in the packed plane-major layout [K][8][2^B] (pack_codebooks)."""
-    return _product("aqlm_gemv_packed", codes, packed_codebooks, x, K, B, out)
+class PackedWeights:
+    """Codes and codebooks of one matrix in the packed layouts (pack_codes,
+    pack_codebooks), with the shape they describe."""
+
+    __slots__ = ("codes", "codebooks", "out_features", "in_features", "K", "B")
+
+    def __init__(self, codes, codebooks, out_features, in_features, K, B):
+        self.codes, self.codebooks = codes, codebooks
+        self.out_features, self.in_features, self.K, self.B = out_features, in_features, K, B
+
+
+def pack_weights(codes, codebooks) -> PackedWeights:
+    """Packed copies of codes [out][in/8][K] and codebooks [K][2^B][8] (one-time layout change)."""
+    K, B = codes.shape[2], _bits_of(codes)
+    return PackedWeights(pack_codes(codes), pack_codebooks(codebooks), codes.shape[0],
+                         codes.shape[1] * 8, K, B)
+
+
+def gemv_packed(weights: PackedWeights, x, out=None):
+    """y = W x from packed weights (aqlm_gemv_packed)."""
+    torch = _torch()
+    lib = _load()
+    w = weights
+    if w.codebooks.dtype != torch.float16 or tuple(w.codebooks.shape) != (w.K, 8, 1 << w.B):
+        raise ValueError("packed codebooks must be float16 [K][8][2^B]")
+    if w.codes.numel() * w.codes.element_size() != packed_codes_bytes(w.out_features,
+                                                                       w.in_features, w.K, w.B):
+        raise ValueError("packed codes have the wrong size")
+    if x.dtype != torch.float16:
+        raise TypeError("x must be float16")
+    x2 = x.unsqueeze(0) if x.dim() == 1 else x
+    if x2.dim() != 2 or x2.shape[1] != w.in_features:
+        raise ValueError("x must be [batch][in_features]")
+    for t, n in ((w.codes, "codes"), (w.codebooks, "codebooks"), (x2, "x")):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{n} must be a contiguous device tensor")
+    batch = x2.shape[0]
+    y = out if out is not None else torch.empty((batch, w.out_features), dtype=torch.float16,
+                                                 device=x2.device)
+    if y.dtype != torch.float16 or tuple(y.shape) != (batch, w.out_features) or \
+            not y.is_contiguous():
+        raise ValueError("out must be a contiguous float16 [batch][out] tensor")
+    _check(lib.aqlm_gemv_packed(w.codes.data_ptr(), w.codebooks.data_ptr(), x2.data_ptr(),
+                                y.data_ptr(), w.out_features, w.in_features, w.K, w.B, batch,
+                                _stream()), "aqlm_gemv_packed")
+    return y if x.dim() == 2 else y[0]
+
+
+def packed_codes_bytes(out_features, in_features, K, B) -> int:
+    return int(_load().aqlm_packed_codes_bytes(out_features, in_features, K, B))
+
+
+def pack_codes(codes, out=None):
+    """Packed copy of codes [out][in/8][K] as a flat uint8 device tensor (aqlm_pack_codes)."""
+    torch = _torch()
+    lib = _load()
+    if codes.dim() != 3 or not codes.is_cuda or not codes.is_contiguous():
+        raise ValueError("codes must be a contiguous device [out][in/8][K] tensor")
+    B, K = _bits_of(codes), codes.shape[2]
+    o, i = codes.shape[0], codes.shape[1] * 8
+    n = packed_codes_bytes(o, i, K, B)
+    if n < 0:
+        raise ValueError("bad code shape")
+    P = out if out is not None else torch.empty(n, dtype=torch.uint8, device=codes.device)
+    if P.numel() * P.element_size() != n or not P.is_contiguous():
+        raise ValueError(f"out must be a contiguous buffer of {n} bytes")
+    _check(lib.aqlm_pack_codes(codes.data_ptr(), P.data_ptr(), o, i, K, B, _stream()),
+           "aqlm_pack_codes")
+    return P
+
+
+def unpack_codes(packed, out_features, in_features, K, B):
+    """Inverse of pack_codes: codes [out][in/8][K] (uint8 for B = 8, int16 for B = 16)."""
+    torch = _torch()
+    lib = _load()
+    n = packed_codes_bytes(out_features, in_features, K, B)
+    if n < 0 or packed.numel() * packed.element_size() != n or not packed.is_cuda \
+            or not packed.is_contiguous():
+        raise ValueError("packed must be a contiguous device buffer of aqlm_packed_codes_bytes")
+    dt = torch.uint8 if B == 8 else torch.int16
+    C = torch.empty((out_features, in_features // 8, K), dtype=dt, device=packed.device)
+    _check(lib.aqlm_unpack_codes(packed.data_ptr(), C.data_ptr(), out_features, in_features, K, B,
+                                 _stream()), "aqlm_unpack_codes")
+    return C
 
 
 def pack_codebooks(codebooks, out=None):

@@ -98,6 +98,18 @@ aqlm::Problem make_problem(const void *codes, const void *cb, const void *x, voi
                          static_cast<hipStream_t>(stream)};
 }
 
+// Packed codes: tiles of 8 rows x 64 groups for 2x8 (the lookup-table kernel's
+// layout), the canonical layout (a plain copy) for every other (K, B).
+bool tiled_codes(int K, int B) { return K == 2 && B == 8; }
+
+int64_t packed_codes_size(int64_t out, int64_t in, int K, int B) {
+    Sizes s;
+    if (!check_shape(out, in, K, B, 1, &s)) return -1;
+    if (!tiled_codes(K, B)) return s.codes;
+    if (out > (int64_t(1) << 30) || in > (int64_t(1) << 30)) return -1;
+    return aqlm::lut_packed_codes_bytes(out, in);
+}
+
 bool supported(int variant, const aqlm::Problem &p) {
     switch (variant) {
         case AQLM_VARIANT_GENERIC: return true;
@@ -365,17 +377,67 @@ aqlm_status_t aqlm_unpack_codebooks(const void *packed, void *codebooks, int K, 
     return pack_common(packed, codebooks, K, B, stream, false);
 }
 
-aqlm_status_t aqlm_gemv_packed(const void *codes, const void *packed_codebooks, const void *x,
-                               void *y, int64_t out_features, int64_t in_features, int K, int B,
-                               int batch, void *stream) {
+int64_t aqlm_packed_codes_bytes(int64_t out_features, int64_t in_features, int K, int B) {
+    return packed_codes_size(out_features, in_features, K, B);
+}
+
+static aqlm_status_t pack_codes_common(const void *src, void *dst, int64_t out, int64_t in, int K,
+                                       int B, void *stream, bool pack) {
+    if (!src || !dst) return AQLM_ERR_INVALID_ARGUMENT;
+    const int64_t pbytes = packed_codes_size(out, in, K, B);
+    if (pbytes < 0) return AQLM_ERR_INVALID_ARGUMENT;
+    const int64_t cbytes = out * (in / kGroup) * K * (B / 8);
+    const int64_t sbytes = pack ? cbytes : pbytes, dbytes = pack ? pbytes : cbytes;
+    if (overlaps(src, sbytes, dst, dbytes)) return AQLM_ERR_INVALID_ARGUMENT;
+    const bool tiled = tiled_codes(K, B);
+    if (tiled && ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) & 1u))
+        return AQLM_ERR_INVALID_ARGUMENT;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const hipError_t e = tiled ? aqlm::launch_pack_codes_lut(src, dst, out, in, pack, s)
+                               : aqlm::launch_copy_bytes(src, dst, cbytes, s);
+    if (e != hipSuccess) {
+        set_error(pack ? "pack_codes" : "unpack_codes", e);
+        return AQLM_ERR_HIP;
+    }
+    return AQLM_OK;
+}
+
+aqlm_status_t aqlm_pack_codes(const void *codes, void *packed, int64_t out_features,
+                              int64_t in_features, int K, int B, void *stream) {
+    return pack_codes_common(codes, packed, out_features, in_features, K, B, stream, true);
+}
+
+aqlm_status_t aqlm_unpack_codes(const void *packed, void *codes, int64_t out_features,
+                                int64_t in_features, int K, int B, void *stream) {
+    return pack_codes_common(packed, codes, out_features, in_features, K, B, stream, false);
+}
+
+aqlm_status_t aqlm_gemv_packed(const void *packed_codes, const void *packed_codebooks,
+                               const void *x, void *y, int64_t out_features, int64_t in_features,
+                               int K, int B, int batch, void *stream) {
     Sizes s;
-    aqlm_status_t st = check_args(codes, packed_codebooks, x, y, out_features, in_features, K, B,
-                                  batch, &s);
+    aqlm_status_t st = check_args(packed_codes, packed_codebooks, x, y, out_features, in_features,
+                                  K, B, batch, &s);
     if (st != AQLM_OK) return st;
-    aqlm::Problem p = make_problem(codes, packed_codebooks, x, y, out_features, in_features, K, B,
-                                   batch, stream);
-    const bool split = aqlm::ds_supported(p) && forced_variant() != AQLM_VARIANT_GENERIC;
-    const size_t need = split ? aqlm::ds_workspace_bytes(p) : size_t(s.codebooks);
+    const int64_t pbytes = packed_codes_size(out_features, in_features, K, B);
+    if (pbytes < 0 || overlaps(y, s.y, packed_codes, pbytes)) return AQLM_ERR_INVALID_ARGUMENT;
+    aqlm::Problem p = make_problem(packed_codes, packed_codebooks, x, y, out_features, in_features,
+                                   K, B, batch, stream);
+    const bool generic = forced_variant() == AQLM_VARIANT_GENERIC;
+    const bool tiled = tiled_codes(K, B);
+    int path;  // 0: split kernel, 1: packed lookup-table kernel, 2: unpack into the workspace
+    size_t need;
+    const size_t cb_off = (size_t(s.codes) + 255) / 256 * 256;
+    if (!generic && !tiled && aqlm::ds_supported(p)) {
+        path = 0;
+        need = aqlm::ds_workspace_bytes(p);
+    } else if (!generic && tiled && aqlm::lut_packed_supported(p)) {
+        path = 1;
+        need = aqlm::lut_packed_workspace_bytes(p);
+    } else {
+        path = 2;
+        need = tiled ? cb_off + size_t(s.codebooks) : size_t(s.codebooks);
+    }
     void *ws = nullptr;
     hipError_t e = get_workspace(p.stream, need, &ws);
     if (e != hipSuccess) {
@@ -385,28 +447,39 @@ aqlm_status_t aqlm_gemv_packed(const void *codes, const void *packed_codebooks, 
     if (!ws) return AQLM_ERR_UNSUPPORTED;   // capturing stream without a workspace
     if (log_enabled())
         std::fprintf(stderr, "[aqlm] packed %s out=%lld in=%lld K=%d B=%d batch=%d\n",
-                     split ? "split" : "unpack+auto", (long long)p.out, (long long)p.in, K, B,
-                     batch);
-    if (split) {
-        e = aqlm::launch_ds(p, ws);
+                     path == 0 ? "split" : path == 1 ? "lut_packed" : "unpack+auto",
+                     (long long)p.out, (long long)p.in, K, B, batch);
+    if (path == 0 || path == 1) {
+        e = path == 0 ? aqlm::launch_ds(p, ws) : aqlm::launch_lut_packed(p, ws);
         if (e != hipSuccess) {
-            set_error("split", e);
+            set_error(path == 0 ? "split" : "lut_packed", e);
             return AQLM_ERR_HIP;
         }
         return AQLM_OK;
     }
-    e = aqlm::launch_unpack_codebooks(packed_codebooks, ws, K, B, p.stream);
+    char *wsb = static_cast<char *>(ws);
+    if (tiled) {
+        e = aqlm::launch_pack_codes_lut(packed_codes, wsb, out_features, in_features, false,
+                                        p.stream);
+        if (e != hipSuccess) {
+            set_error("unpack_codes", e);
+            return AQLM_ERR_HIP;
+        }
+        p.codes = wsb;
+    }
+    void *cbws = tiled ? wsb + cb_off : wsb;
+    e = aqlm::launch_unpack_codebooks(packed_codebooks, cbws, K, B, p.stream);
     if (e != hipSuccess) {
         set_error("unpack_codebooks", e);
         return AQLM_ERR_HIP;
     }
-    p.codebooks = ws;
+    p.codebooks = cbws;
     int v = choose(false, p);
-    if (v == AQLM_VARIANT_LUT) v = AQLM_VARIANT_LDS;   // the workspace holds the codebooks
+    if (v == AQLM_VARIANT_LUT) v = AQLM_VARIANT_LDS;   // the workspace holds the operands
     return run(v, p);
 }
 
-const char *aqlm_version(void) { return "0.2.0"; }
+const char *aqlm_version(void) { return "0.3.0"; }
 
 const char *aqlm_last_error(void) { return g_last_error; }
 

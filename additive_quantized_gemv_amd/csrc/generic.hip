@@ -114,6 +114,26 @@ partial_sum_kernel(const float *__restrict__ partial, uint16_t *__restrict__ y, 
 
 }  // namespace
 
+// byte copy, 16 bytes per thread where both pointers allow it
+__global__ void __launch_bounds__(256)
+copy_bytes_kernel(const uint8_t *__restrict__ src, uint8_t *__restrict__ dst, int64_t n) {
+    const int64_t stride = int64_t(gridDim.x) * blockDim.x;
+    const int64_t t0 = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+    const bool wide = ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) & 15u) == 0;
+    const int64_t nw = wide ? n / 16 : 0;
+    for (int64_t i = t0; i < nw; i += stride)
+        reinterpret_cast<uint4 *>(dst)[i] = reinterpret_cast<const uint4 *>(src)[i];
+    for (int64_t i = nw * 16 + t0; i < n; i += stride) dst[i] = src[i];
+}
+
+hipError_t launch_copy_bytes(const void *src, void *dst, int64_t n, hipStream_t s) {
+    const int64_t units = (n + 15) / 16;
+    const int blocks = int((units + 255) / 256 < 4096 ? (units + 255) / 256 : 4096);
+    hipLaunchKernelGGL(copy_bytes_kernel, dim3(blocks > 0 ? blocks : 1), dim3(256), 0, s,
+                       static_cast<const uint8_t *>(src), static_cast<uint8_t *>(dst), n);
+    return hipGetLastError();
+}
+
 hipError_t launch_partial_sum(const float *partial, void *y, int64_t n, int parts, hipStream_t s) {
     hipLaunchKernelGGL(partial_sum_kernel, dim3(unsigned((n + 255) / 256)), dim3(256), 0, s,
                        partial, static_cast<uint16_t *>(y), n, parts);

@@ -26,6 +26,7 @@ hipError_t launch_generic(const Problem &p);
 
 // y[i] = fp16(sum over parts of partial[part][i]) for i < n (parts summed in order).
 hipError_t launch_partial_sum(const float *partial, void *y, int64_t n, int parts, hipStream_t s);
+hipError_t launch_copy_bytes(const void *src, void *dst, int64_t n, hipStream_t s);
 
 // Dense W (fp32 when w_fp16 == 0, fp16 otherwise).
 hipError_t launch_dequantize(const Problem &p, void *W, int w_fp16);
@@ -42,6 +43,13 @@ hipError_t launch_l2(const Problem &p);
 bool lut_supported(const Problem &p);
 size_t lut_workspace_bytes(const Problem &p);
 hipError_t launch_lut(const Problem &p, void *workspace);
+// 2x8 lookup-table kernel over packed code tiles (8 rows x 64 groups) and plane-major codebooks
+int64_t lut_packed_codes_bytes(int64_t out, int64_t in);
+bool lut_packed_supported(const Problem &p);
+size_t lut_packed_workspace_bytes(const Problem &p);
+hipError_t launch_lut_packed(const Problem &p, void *workspace);
+hipError_t launch_pack_codes_lut(const void *src, void *dst, int64_t out, int64_t in, bool pack,
+                                 hipStream_t s);
 
 // 16-bit codes with the codebook split by vector position (packed planes), batch <= 4.
 bool ds_supported(const Problem &p);

@@ -25,6 +25,13 @@
 //   form took 24 us per 11008x4096 product against 7 + 4 us for the two kernels.
 // * Every code load of a wave (up to 32 rows) is issued before the tables are
 //   built, so each wave waits for HBM once.
+// * Packed variant (aqlm_pack_codes): the codes of a slice are stored as tiles
+//   of 8 rows x 64 groups, lane jl's 16 bytes holding the 8 rows' code pairs of
+//   group jl.  A wave then reads 1 KiB contiguous per load (instead of one
+//   128-byte row segment per load, half of which straddle two cache lines when
+//   rows are not 128-byte multiples), with one load and address per 8 rows.
+//   The group padding of the last slice holds code 0 and meets zero
+//   activations, so it adds nothing.
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -41,6 +48,50 @@ typedef _Float16 half4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float lds_f32(const char *base, uint32_t byte_addr) {
     return *reinterpret_cast<const float *>(base + byte_addr);
+}
+
+// Operands of the table build.  Wave w computes entries 32w .. 32w+31 for both
+// 32-group halves of the slice with v_mfma_f32_32x32x8_f16: lane l supplies
+// positions 4(l/32) .. 4(l/32)+3 of entry 32w + l%32 (A) and of the activations
+// of group j0 + 32h + l%32 (B, h = 0, 1), zero past the last group.
+// PLANAR: codebooks in the plane-major layout [K][8][256] of aqlm_pack_codebooks.
+template <bool PLANAR>
+__device__ __forceinline__ void load_build_operands(const uint16_t *__restrict__ cb,
+                                                    const uint16_t *__restrict__ x, int j0, int G,
+                                                    int wave, int lane, half4 &a, half4 (&bx)[2]) {
+    const int e = wave * 32 + (lane & 31);
+    const int kq = (lane >> 5) * 4;
+    if constexpr (PLANAR) {
+        const int k = e >> 8, c = e & 255;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            a[i] = __builtin_bit_cast(_Float16, cb[(k * 8 + kq + i) * 256 + c]);
+    } else {
+        a = *reinterpret_cast<const half4 *>(cb + size_t(e) * kGroup + kq);
+    }
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+        const int j = min(j0 + nb * 32 + (lane & 31), G - 1);
+        bx[nb] = *reinterpret_cast<const half4 *>(x + size_t(j) * kGroup + kq);
+        if (j0 + nb * 32 + (lane & 31) >= G) bx[nb] = half4{0, 0, 0, 0};
+    }
+}
+
+// L[e][jl] -> LDS byte (e * 64 + jl) * 4; result lane l, register r holds entry
+// 32w + 8(r/4) + 4(l/32) + r%4 of group 32h + l%32.
+__device__ __forceinline__ void store_tables(char *lut, const half4 &a, const half4 (&bx)[2],
+                                             int wave, int lane) {
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+        float16v d = {};
+        d = __builtin_amdgcn_mfma_f32_32x32x8f16(a, bx[nb], d, 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int m = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+            const int n = nb * 32 + (lane & 31);
+            *reinterpret_cast<float *>(lut + (wave * 32 + m) * 256 + n * 4) = d[r];
+        }
+    }
 }
 
 __global__ void __launch_bounds__(kLutWaves * kWave)
@@ -62,20 +113,11 @@ lut_kernel(const uint16_t *__restrict__ codes, const uint16_t *__restrict__ cb,
     const int w_begin = r_begin + wave * rpw;
     const int w_rows = max(0, min(rpw, r_end - w_begin));
 
-    // ---- build L[e][jl] = C[e] . x_{j0+jl} for the 512 entries e = k*256 + c
-    // wave w computes entries 32w .. 32w+31 for both 32-group halves of the slice.
+    // ---- build L[e][jl] = C[e] . x_{j0+jl} for the 512 entries e = k*256 + c.
     // Its (L2-resident) operands are loaded before the code stream: loads complete
     // in issue order, so the tables are built while the codes are still in flight.
-    const int e = wave * 32 + (lane & 31);
-    const int kq = (lane >> 5) * 4;              // this lane's 4 of the 8 vector positions
-    const half4 a = *reinterpret_cast<const half4 *>(cb + size_t(e) * kGroup + kq);
-    half4 bx[2];
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-        const int j = min(j0 + nb * 32 + (lane & 31), G - 1);
-        bx[nb] = *reinterpret_cast<const half4 *>(x + size_t(j) * kGroup + kq);
-        if (j0 + nb * 32 + (lane & 31) >= G) bx[nb] = half4{0, 0, 0, 0};
-    }
+    half4 a, bx[2];
+    load_build_operands<false>(cb, x, j0, G, wave, lane, a, bx);
 
     // then every code load of this wave (up to 32 rows): the wave waits for HBM once
     uint32_t code[kRowsPerWave];
@@ -85,17 +127,7 @@ lut_kernel(const uint16_t *__restrict__ codes, const uint16_t *__restrict__ cb,
         code[r] = uint32_t(__builtin_nontemporal_load(codes + size_t(row) * G + min(j0 + jl, G - 1)));
     }
 
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-        float16v d = {};
-        d = __builtin_amdgcn_mfma_f32_32x32x8f16(a, bx[nb], d, 0, 0, 0);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int m = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-            const int n = nb * 32 + (lane & 31);
-            *reinterpret_cast<float *>(lut + (wave * 32 + m) * 256 + n * 4) = d[r];
-        }
-    }
+    store_tables(lut, a, bx, wave, lane);
     __syncthreads();
 
     // byte-address template: byte0 = 4*jl, byte2 = 1 selects the second table half
@@ -115,6 +147,97 @@ lut_kernel(const uint16_t *__restrict__ codes, const uint16_t *__restrict__ cb,
         const float s = transpose_reduce<kReduceRows>(v, lane);
         const int r = h * kReduceRows + (lane >> 2);
         if ((lane & 3) == 0 && r < w_rows) partial[size_t(slice) * out + w_begin + r] = s;
+    }
+}
+
+// Same product from packed codes: tile (slice s, row octet q) is 64 lanes x 16 B at
+// byte ((s * NQ + q) * 64 + jl) * 16, NQ = ceil(out / 8); bytes 2r, 2r+1 of lane
+// jl's 16 B are the two codes of row 8q + r, group 64s + jl.  Codebooks are the
+// plane-major packed ones.  A workgroup's row range starts on an octet; wave w
+// takes the range's octets w, w + 16, w + 32, w + 48.
+constexpr int kOctetsPerWave = kRowsPerWave / 8;
+
+__global__ void __launch_bounds__(kLutWaves * kWave)
+lut_packed_kernel(const u32x4 *__restrict__ pcodes, const uint16_t *__restrict__ planes,
+                  const uint16_t *__restrict__ x, float *__restrict__ partial, int out, int G,
+                  int rows_per_block, int nslices) {
+    __shared__ __attribute__((aligned(16))) char lut[kLutBytes];
+
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int slice = blockIdx.x % nslices;
+    const int rblock = blockIdx.x / nslices;
+    const int j0 = slice * kSlice;
+    const int NQ = (out + 7) / 8;
+    const int r_begin = rblock * rows_per_block;             // a multiple of 8
+    const int r_end = min(out, r_begin + rows_per_block);
+    const int nq = (r_end - r_begin + 7) / 8;                 // >= 1
+
+    half4 a, bx[2];
+    load_build_operands<true>(planes, x, j0, G, wave, lane, a, bx);
+
+    // all code tiles of this wave (clamped into the range: always in bounds)
+    const u32x4 *tile = pcodes + (size_t(slice) * NQ + r_begin / 8) * kWave + lane;
+    u32x4 code[kOctetsPerWave];
+#pragma unroll
+    for (int i = 0; i < kOctetsPerWave; ++i)
+        code[i] = __builtin_nontemporal_load(tile + size_t(min(wave + kLutWaves * i, nq - 1)) * kWave);
+
+    store_tables(lut, a, bx, wave, lane);
+    __syncthreads();
+
+    const uint32_t lanebase = (uint32_t(lane) << 2) | (1u << 16);
+#pragma unroll
+    for (int i = 0; i < kOctetsPerWave; i += 2) {
+        if (wave + kLutWaves * i >= nq) break;               // wave-uniform
+        float v[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            // row r % 8 of octet i + r / 8: halfword r % 8 of the tile
+            const uint32_t w = code[i + r / 8][(r & 7) >> 1];
+            const bool hi = r & 1;
+            const uint32_t a0 = __builtin_amdgcn_perm(lanebase, w, hi ? 0x0C0C0204u : 0x0C0C0004u);
+            const uint32_t a1 = __builtin_amdgcn_perm(lanebase, w, hi ? 0x0C060304u : 0x0C060104u);
+            v[r] = lds_f32(lut, a0) + lds_f32(lut, a1);
+        }
+        const float sum = transpose_reduce<16>(v, lane);
+        const int vi = lane >> 2;                            // value index: octet i + vi/8, row vi%8
+        const int q = wave + kLutWaves * (i + (vi >> 3));
+        const int row = r_begin + 8 * q + (vi & 7);
+        if ((lane & 3) == 0 && q < nq && row < r_end) partial[size_t(slice) * out + row] = sum;
+    }
+}
+
+// codes [out][G] (two 8-bit codes per 16-bit word) -> packed tiles; padding is code 0
+__global__ void __launch_bounds__(256)
+pack_codes_kernel(const uint16_t *__restrict__ codes, uint16_t *__restrict__ packed, int out,
+                  int G, int nslices) {
+    const int NQ = (out + 7) / 8;
+    const int64_t lanes = int64_t(nslices) * NQ * kWave;
+    for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < lanes;
+         i += int64_t(gridDim.x) * blockDim.x) {
+        const int jl = int(i % kWave);
+        const int64_t t = i / kWave;
+        const int q = int(t % NQ), s = int(t / NQ);
+        const int j = s * kSlice + jl;
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            const int row = 8 * q + r;
+            packed[i * 8 + r] = (row < out && j < G) ? codes[size_t(row) * G + j] : uint16_t(0);
+        }
+    }
+}
+
+__global__ void __launch_bounds__(256)
+unpack_codes_kernel(const uint16_t *__restrict__ packed, uint16_t *__restrict__ codes, int out,
+                    int G, int nslices) {
+    const int64_t n = int64_t(out) * G;
+    const int NQ = (out + 7) / 8;
+    for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+         i += int64_t(gridDim.x) * blockDim.x) {
+        const int row = int(i / G), j = int(i % G);
+        const int s = j / kSlice, jl = j % kSlice;
+        codes[i] = packed[((size_t(s) * NQ + row / 8) * kWave + jl) * 8 + row % 8];
     }
 }
 
@@ -141,7 +264,7 @@ struct LutCfg {
     int nslices, nrblocks, rows_per_block;
 };
 
-LutCfg lut_cfg(const Problem &p) {
+LutCfg lut_cfg(const Problem &p, bool packed) {
     LutCfg c{};
     const int64_t G = p.in / kGroup;
     c.nslices = int((G + kSlice - 1) / kSlice);
@@ -152,7 +275,8 @@ LutCfg lut_cfg(const Problem &p) {
     const int64_t need = (p.out + max_rows - 1) / max_rows;
     if (nrb < need) nrb = need;
     int64_t rpb = (p.out + nrb - 1) / nrb;
-    rpb = (rpb + kLutWaves - 1) / kLutWaves * kLutWaves;   // whole rows per wave
+    if (packed) rpb = (rpb + 7) / 8 * 8;                      // ranges start on an octet
+    else rpb = (rpb + kLutWaves - 1) / kLutWaves * kLutWaves; // whole rows per wave
     if (rpb < kLutWaves) rpb = kLutWaves;
     c.rows_per_block = int(rpb);
     c.nrblocks = int((p.out + rpb - 1) / rpb);
@@ -171,13 +295,13 @@ bool lut_supported(const Problem &p) {
 }
 
 size_t lut_workspace_bytes(const Problem &p) {
-    const LutCfg c = lut_cfg(p);
+    const LutCfg c = lut_cfg(p, false);
     return size_t(c.nslices) * size_t(p.out) * sizeof(float);
 }
 
 // workspace: partial sums, nslices x out fp32 (no initial contents needed)
 hipError_t launch_lut(const Problem &p, void *workspace) {
-    const LutCfg c = lut_cfg(p);
+    const LutCfg c = lut_cfg(p, false);
     float *partial = static_cast<float *>(workspace);
     const int grid = c.nslices * c.nrblocks;
     hipLaunchKernelGGL(lut_kernel, dim3(grid), dim3(kLutWaves * kWave), 0, p.stream,
@@ -189,6 +313,59 @@ hipError_t launch_lut(const Problem &p, void *workspace) {
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(lut_reduce_kernel, dim3(unsigned((p.out + 255) / 256)), dim3(256), 0,
                        p.stream, partial, static_cast<uint16_t *>(p.y), int(p.out), c.nslices);
+    return hipGetLastError();
+}
+
+int64_t lut_packed_codes_bytes(int64_t out, int64_t in) {
+    const int64_t G = in / kGroup;
+    return (G + kSlice - 1) / kSlice * ((out + 7) / 8) * kWave * 16;
+}
+
+bool lut_packed_supported(const Problem &p) {
+    if (p.K != 2 || p.B != 8 || p.batch != 1) return false;
+    if (p.out > (1 << 30) || p.in > (1 << 30)) return false;
+    const uintptr_t a = reinterpret_cast<uintptr_t>(p.codes) |
+                        reinterpret_cast<uintptr_t>(p.codebooks) |
+                        reinterpret_cast<uintptr_t>(p.x);
+    return (a & 15u) == 0;
+}
+
+size_t lut_packed_workspace_bytes(const Problem &p) {
+    const LutCfg c = lut_cfg(p, true);
+    return size_t(c.nslices) * size_t(p.out) * sizeof(float);
+}
+
+// p.codes: packed tiles; p.codebooks: plane-major; workspace: nslices x out fp32
+hipError_t launch_lut_packed(const Problem &p, void *workspace) {
+    const LutCfg c = lut_cfg(p, true);
+    float *partial = static_cast<float *>(workspace);
+    hipLaunchKernelGGL(lut_packed_kernel, dim3(c.nslices * c.nrblocks), dim3(kLutWaves * kWave), 0,
+                       p.stream, static_cast<const u32x4 *>(p.codes),
+                       static_cast<const uint16_t *>(p.codebooks),
+                       static_cast<const uint16_t *>(p.x), partial, int(p.out),
+                       int(p.in / kGroup), c.rows_per_block, c.nslices);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(lut_reduce_kernel, dim3(unsigned((p.out + 255) / 256)), dim3(256), 0,
+                       p.stream, partial, static_cast<uint16_t *>(p.y), int(p.out), c.nslices);
+    return hipGetLastError();
+}
+
+// pack: src = codes [out][G] 16-bit words, dst = tiles; unpack: the reverse
+hipError_t launch_pack_codes_lut(const void *src, void *dst, int64_t out, int64_t in, bool pack,
+                                 hipStream_t s) {
+    const int G = int(in / kGroup);
+    const int nslices = (G + kSlice - 1) / kSlice;
+    const int64_t work = pack ? int64_t(nslices) * ((out + 7) / 8) * kWave : out * G;
+    const int blocks = int((work + 255) / 256 < 4096 ? (work + 255) / 256 : 4096);
+    if (pack)
+        hipLaunchKernelGGL(pack_codes_kernel, dim3(blocks), dim3(256), 0, s,
+                           static_cast<const uint16_t *>(src), static_cast<uint16_t *>(dst),
+                           int(out), G, nslices);
+    else
+        hipLaunchKernelGGL(unpack_codes_kernel, dim3(blocks), dim3(256), 0, s,
+                           static_cast<const uint16_t *>(src), static_cast<uint16_t *>(dst),
+                           int(out), G, nslices);
     return hipGetLastError();
 }
 

@@ -7,10 +7,10 @@ the 1x16 scheme (one 65536-entry codebook, 16-bit codes), 2 bits per weight,
 fp16 activations, batch 1.  Codes, codebooks and activations are seeded
 synthetic data (uniform codes, N(0, 0.02^2) codebooks, N(0, 1) activations).
 
-One step = the four products (2 shapes x 2 schemes).  The 1x16 products use the
-library's packed-codebook entry point (codebooks stored plane-major once, at
-load time, like any weight layout); the canonical-layout call is timed beside
-it.  Every launch reads a
+One step = the four products (2 shapes x 2 schemes), through the library's
+packed-weights entry point (codes and codebooks re-laid out once, at load time,
+like any weight layout: 2x8 codes in 8-row x 64-group tiles, 1x16 codebooks
+plane-major); the canonical-layout call is timed beside each.  Every launch reads a
 different copy of codes and codebooks from a rotation set larger than twice
 the 256 MB Infinity Cache, so weights stream from HBM as in a real decode step.
 Launches are replayed from captured HIP graphs; HIP events on the launch stream
@@ -45,7 +45,7 @@ WORKLOAD = [  # name, out, in, K, B
 SIGMA_CB = 0.02
 CONFIG_IDS = {8: 2, 16: 3}     # seed namespace per scheme (the 2x8 and 1x16 MLP workloads)
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "hbm_traffic.md")
-KERNEL_SOURCES = {"lut": "lut.hip", "lds": "gather.hip", "l2": "l2gather.hip", "mfma": "mfma.hip",
+KERNEL_SOURCES = {"lut": "lut.hip", "lut_packed": "lut.hip", "lds": "gather.hip", "l2": "l2gather.hip", "mfma": "mfma.hip",
                   "generic": "generic.hip", "split": "dimsplit.hip"}
 
 
@@ -79,7 +79,7 @@ def measured_traffic(config_name, variant):
 
 def build_inputs(torch, synth, aq, copies):
     """Device tensors: per copy, per workload entry (codes, codebooks, x, problem, packed
-    codebooks or None); plus y buffers."""
+    weights); plus y buffers."""
     import numpy as np
     dev = torch.device("cuda:0")
     sets = []
@@ -88,11 +88,10 @@ def build_inputs(torch, synth, aq, copies):
         for name, out, in_, K, B in WORKLOAD:
             p = synth.make_problem(out, in_, K, B, batch=1, sigma_cb=SIGMA_CB,
                                    config=CONFIG_IDS[B] * 10 + (0 if out > in_ else 1), copy=r)
-            codes = p["codes"] if B == 8 else p["codes"].view(np.int16)
+            codes = torch.from_numpy(p["codes"] if B == 8 else p["codes"].view(np.int16)).to(dev)
             cb = torch.from_numpy(p["codebooks"]).to(dev)
-            packed = aq.pack_codebooks(cb) if B == 16 else None
-            entry.append((torch.from_numpy(codes).to(dev), cb, torch.from_numpy(p["x"]).to(dev), p,
-                          packed))
+            packed = aq.pack_weights(codes, cb)
+            entry.append((codes, cb, torch.from_numpy(p["x"]).to(dev), p, packed))
         sets.append(entry)
     ys = [torch.empty((1, out), dtype=torch.float16, device=dev) for _, out, _, _, _ in WORKLOAD]
     return sets, ys
@@ -146,9 +145,11 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--warm", action="store_true", help="also time cache-resident (no rotation)")
-    ap.add_argument("--workload", default="mlp", choices=["mlp", "layer7b"],
+    ap.add_argument("--workload", default="mlp", choices=["mlp", "layer7b", "copy"],
                     help="mlp: the batch-1 MLP products (default, the headline line); "
-                         "layer7b: the seven linears of a Llama-2-7B layer through aqlm_gemm")
+                         "layer7b: the seven linears of a Llama-2-7B layer through aqlm_gemm; "
+                         "copy: device-to-device copies of 64 and 256 MiB (reference "
+                         "transfers that calibrate the FETCH_SIZE / WRITE_SIZE counters)")
     ap.add_argument("--batch", type=int, default=16, help="tokens for --workload layer7b")
     ap.add_argument("--scheme", default="2x8", choices=["2x8", "1x16"],
                     help="scheme for --workload layer7b")
@@ -173,6 +174,8 @@ def main():
 
     if args.workload == "layer7b":
         return layer_bench(args, torch, np, aq, synth)
+    if args.workload == "copy":
+        return copy_bench(args, torch)
 
     per_copy = sum(algorithmic_bytes(o, i, K, B) for _, o, i, K, B in WORKLOAD)
     copies = args.copies or max(2, math.ceil(2 * MALL_BYTES / per_copy))
@@ -184,13 +187,12 @@ def main():
 
     def call(entry_idx, r, canonical=False):
         codes, cb, x, _, packed = sets[r][entry_idx]
-        if packed is not None and not canonical:
-            aq.gemv_packed(codes, packed, x, out=ys[entry_idx])
+        if not canonical:
+            aq.gemv_packed(packed, x, out=ys[entry_idx])
         else:
             aq.gemv(codes, cb, x, out=ys[entry_idx])
 
-    variants = ["split" if sets[0][i][4] is not None else aq.selected_variant(*sets[0][i][:3])
-                for i in range(len(WORKLOAD))]
+    variants = ["split" if B == 16 else "lut_packed" for _, _, _, _, B in WORKLOAD]
     canonical_variants = [aq.selected_variant(*sets[0][i][:3]) for i in range(len(WORKLOAD))]
 
     # one stream for warmup, capture, replay and events: the warmup's eager calls
@@ -257,13 +259,13 @@ def _timed(args, torch, np, aq, sets, ys, copies, per_copy, call, variants, stre
             gw = capture_on(torch, stream, lambda i=i: [call(i, 0) for _ in range(copies)])
             dtw = time_graph(torch, gw, launches // copies) / ((launches // copies) * copies)
             rec["us_per_call_cache_resident"] = round(dtw * 1e6, 3)
-        if sets[0][i][4] is not None:       # also the canonical-layout call
-            gc = capture_on(torch, stream,
-                            lambda i=i: [call(i, r, canonical=True) for r in range(copies)])
-            dtc = time_graph(torch, gc, launches // copies) / ((launches // copies) * copies)
-            rec["canonical_layout"] = {"variant": canonical_variants[i],
-                                       "us_per_call": round(dtc * 1e6, 3),
-                                       "gbps": round(nbytes / dtc / 1e9, 1)}
+        # the same product from the canonical layout (aqlm_gemv), timed beside it
+        gc = capture_on(torch, stream,
+                        lambda i=i: [call(i, r, canonical=True) for r in range(copies)])
+        dtc = time_graph(torch, gc, launches // copies) / ((launches // copies) * copies)
+        rec["canonical_layout"] = {"variant": canonical_variants[i],
+                                   "us_per_call": round(dtc * 1e6, 3),
+                                   "gbps": round(nbytes / dtc / 1e9, 1)}
         per_call.append(rec)
         print(f"[bench] {name} ({variants[i]}): {rec['us_per_call']} us, {rec['gbps']} GB/s",
               file=sys.stderr, flush=True)
@@ -288,7 +290,7 @@ def _timed(args, torch, np, aq, sets, ys, copies, per_copy, call, variants, stre
                                "2x8 and 1x16 (2 bits/weight), batch 1",
                    "batch": 1, "rotation_copies": copies,
                    "rotation_bytes": per_copy * copies, "launch": "hip graph replay",
-                   "step": "4 products (2 shapes x 2 schemes); 1x16 with packed codebooks"},
+                   "step": "4 products (2 shapes x 2 schemes), packed weights"},
         "per_call": per_call,
         "roofline": roofline,
     }
@@ -300,6 +302,31 @@ def _timed(args, torch, np, aq, sets, ys, copies, per_copy, call, variants, stre
             ys_copy0.append(ys[i].float().cpu().numpy().astype(np.float64))
         result["cpu_baseline"] = cpu_baseline(sets, ys_copy0, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+def copy_bench(args, torch):
+    """Plain device-to-device copies of known size: the bytes a counter should report for
+    them calibrate that counter (FETCH_SIZE, WRITE_SIZE) on this machine."""
+    dev = torch.device("cuda:0")
+    res = []
+    for mib in (64, 256):
+        n = mib << 20
+        a = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        b = torch.empty_like(a)
+        reps = 4
+        torch.cuda.synchronize()
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record()
+        for _ in range(reps):
+            b.copy_(a)
+        end.record()
+        torch.cuda.synchronize()
+        dt = start.elapsed_time(end) * 1e-3 / reps
+        res.append({"mib": mib, "us_per_copy": round(dt * 1e6, 2),
+                    "gbps_read_plus_write": round(2 * n / dt / 1e9, 1)})
+        del a, b
+    print(json.dumps({"workload": "device copy (counter calibration)", "copies": res}),
+          flush=True)
 
 
 LAYER_7B = [("q", 4096, 4096), ("k", 4096, 4096), ("v", 4096, 4096), ("o", 4096, 4096),

@@ -136,18 +136,42 @@ aqlm_status_t aqlm_unpack_codebooks(const void *packed, void *codebooks, int K, 
                                     void *stream);
 
 /*
- * The product of aqlm_gemv with the codebooks given packed (aqlm_pack_codebooks).
- * For 16-bit codes with K in {1,2} and batch <= 4 it runs the position-split
- * kernel (AQLM_VARIANT_SPLIT): the K*8 codebook planes live in the LDS of K*8
- * workgroups per row range and a second kernel adds their partial sums.  Other
- * arguments are unpacked into the stream's workspace and run as aqlm_gemv.
- * Uses the per-(device, stream) workspace (K*8*batch*out fp32, or the unpacked
- * codebooks); on a capturing stream without a large enough workspace it
- * returns AQLM_ERR_UNSUPPORTED (make one call on the stream first).
+ * Packed code layout (a one-time change of the weights' layout, like
+ * aqlm_pack_codebooks; not part of the product).
+ * - K = 2, B = 8: tiles of 8 rows x 64 groups.  With G = in/8, NQ = ceil(out/8)
+ *   and S = ceil(G/64), tile (s, q) for s < S, q < NQ is 1024 bytes at byte
+ *   offset (s*NQ + q) * 1024; its bytes 16*jl + 2*r and 16*jl + 2*r + 1 are the
+ *   codes (codebook 0, codebook 1) of row 8q + r, group 64s + jl.  Rows >= out
+ *   and groups >= G hold code 0.  Size S * NQ * 1024 bytes.  codes and packed
+ *   must be 2-byte aligned.
+ * - every other (K, B): the canonical layout itself (a copy).
+ * aqlm_packed_codes_bytes returns the size, or -1 on bad arguments.  `packed`
+ * must not overlap `codes`.  Asynchronous on `stream`.
  */
-aqlm_status_t aqlm_gemv_packed(const void *codes, const void *packed_codebooks, const void *x,
-                               void *y, int64_t out_features, int64_t in_features, int K, int B,
-                               int batch, void *stream);
+int64_t aqlm_packed_codes_bytes(int64_t out_features, int64_t in_features, int K, int B);
+aqlm_status_t aqlm_pack_codes(const void *codes, void *packed, int64_t out_features,
+                              int64_t in_features, int K, int B, void *stream);
+/* Exact inverse of aqlm_pack_codes (padding is dropped). */
+aqlm_status_t aqlm_unpack_codes(const void *packed, void *codes, int64_t out_features,
+                                int64_t in_features, int K, int B, void *stream);
+
+/*
+ * The product of aqlm_gemv from packed weights: codes from aqlm_pack_codes,
+ * codebooks from aqlm_pack_codebooks.  Same y, same argument rules.
+ * - 16-bit codes, K in {1,2}, batch <= 4: the position-split kernel
+ *   (AQLM_VARIANT_SPLIT): the K*8 codebook planes live in the LDS of K*8
+ *   workgroups per row range and a second kernel adds their partial sums.
+ * - 2x8, batch 1, 16-byte aligned pointers: the lookup-table kernel reading
+ *   the code tiles (1 KiB contiguous per wave load).
+ * - otherwise the packed operands are unpacked into the stream's workspace and
+ *   the product runs as aqlm_gemv.
+ * Uses the per-(device, stream) workspace (partial sums, or the unpacked
+ * operands); on a capturing stream without a large enough workspace it returns
+ * AQLM_ERR_UNSUPPORTED (make one call on the stream first).
+ */
+aqlm_status_t aqlm_gemv_packed(const void *packed_codes, const void *packed_codebooks,
+                               const void *x, void *y, int64_t out_features, int64_t in_features,
+                               int K, int B, int batch, void *stream);
 
 /* K*B/group bits per weight (bitrate formula of the decode section). */
 double aqlm_bits_per_weight(int K, int B, int group);

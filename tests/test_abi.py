@@ -109,6 +109,32 @@ def test_pack_invalid(lib):
     assert lib.aqlm_gemv_packed(C, CB, X, Y, 16, 60, 1, 16, 1, None) == 1
 
 
+def test_packed_codes_sizes(lib):
+    # 2x8: ceil(G/64) slices x ceil(out/8) row octets x 1 KiB tiles
+    assert lib.aqlm_packed_codes_bytes(11008, 4096, 2, 8) == 8 * 1376 * 1024
+    assert lib.aqlm_packed_codes_bytes(4096, 11008, 2, 8) == 22 * 512 * 1024
+    assert lib.aqlm_packed_codes_bytes(65, 520, 2, 8) == 2 * 9 * 1024
+    assert lib.aqlm_packed_codes_bytes(1, 64, 2, 8) == 1024
+    # other schemes keep the canonical layout
+    assert lib.aqlm_packed_codes_bytes(4096, 4096, 1, 16) == 4096 * 512 * 2
+    assert lib.aqlm_packed_codes_bytes(10, 24, 3, 8) == 10 * 3 * 3
+    assert lib.aqlm_packed_codes_bytes(10, 12, 2, 8) == -1
+    assert lib.aqlm_packed_codes_bytes(10, 16, 2, 12) == -1
+
+
+def test_pack_codes_invalid(lib):
+    assert lib.aqlm_pack_codes(0, Y, 16, 64, 2, 8, None) == 1
+    assert lib.aqlm_pack_codes(C, 0, 16, 64, 2, 8, None) == 1
+    assert lib.aqlm_pack_codes(C, Y, 16, 60, 2, 8, None) == 1          # in % 8
+    assert lib.aqlm_pack_codes(C, C + 100, 16, 64, 2, 8, None) == 1    # overlapping
+    assert lib.aqlm_pack_codes(C + 1, Y, 16, 64, 2, 8, None) == 1      # 2x8 words misaligned
+    assert lib.aqlm_unpack_codes(C, Y + 1, 16, 64, 2, 8, None) == 1
+    # y inside the padded packed codes (beyond the canonical size) is rejected
+    n = lib.aqlm_packed_codes_bytes(9, 64, 2, 8)
+    assert n == 2 * 1024 and lib.aqlm_codes_bytes(9, 64, 2, 8) == 144
+    assert lib.aqlm_gemv_packed(C, CB, X, C + 512, 9, 64, 2, 8, 1, None) == 1
+
+
 def test_variant_choice_host_logic(lib):
     # pointers aligned to 256 B, shapes of the benchmark configurations
     def sel(gemm, out, in_, K, B, batch):

@@ -316,11 +316,45 @@ def test_pack_unpack_exact(aq, KB):
                           p["codebooks"].view(np.uint16))
 
 
+def _tiles_2x8(codes):
+    """Packed 2x8 code tiles as the header defines them, built with numpy."""
+    out, G, _ = codes.shape
+    w = np.ascontiguousarray(codes).view(np.uint16).reshape(out, G)   # byte 0 = c0, byte 1 = c1
+    S, NQ = -(-G // 64), -(-out // 8)
+    pad = np.zeros((NQ * 8, S * 64), np.uint16)
+    pad[:out, :G] = w
+    return np.ascontiguousarray(pad.reshape(NQ, 8, S, 64).transpose(2, 0, 3, 1)).view(np.uint8).ravel()
+
+
+@pytest.mark.parametrize("case", [(16, 512, 2, 8), (65, 520, 2, 8), (1, 64, 2, 8), (300, 11008, 2, 8),
+                                  (40, 512, 1, 16), (9, 64, 3, 8)],
+                         ids=lambda c: "x".join(map(str, c)))
+def test_pack_codes_exact(aq, case):
+    import torch
+    out, in_, K, B = case
+    p = synth.make_problem(out, in_, K, B, sigma_cb=0.02, config=1450 + out)
+    codes = _dev(p)[0]
+    P = aq.pack_codes(codes)
+    torch.cuda.synchronize()
+    got = P.cpu().numpy()
+    if (K, B) == (2, 8):
+        assert np.array_equal(got, _tiles_2x8(p["codes"]))
+    else:
+        assert np.array_equal(got, np.ascontiguousarray(p["codes"]).view(np.uint8).ravel())
+    back = aq.unpack_codes(P, out, in_, K, B)
+    assert np.array_equal(back.cpu().numpy().view(np.uint8),
+                          np.ascontiguousarray(p["codes"]).view(np.uint8))
+
+
 PACKED = [
     # out, in, K, B, batch
     (300, 4096, 1, 16, 1), (65, 520, 1, 16, 1), (1, 64, 1, 16, 1), (257, 11008, 1, 16, 1),
     (130, 2048, 1, 16, 2), (77, 1024, 1, 16, 3), (160, 8192, 1, 16, 4), (96, 512, 2, 16, 1),
-    (50, 1024, 2, 16, 4), (64, 512, 1, 16, 8), (40, 512, 2, 8, 1), (1000, 28672, 1, 16, 1),
+    (50, 1024, 2, 16, 4), (64, 512, 1, 16, 8), (1000, 28672, 1, 16, 1),
+    # 2x8: the tiled lookup-table kernel at batch 1 (ragged rows, partial slices), else unpacked
+    (40, 512, 2, 8, 1), (65, 520, 2, 8, 1), (1, 64, 2, 8, 1), (300, 4096, 2, 8, 1),
+    (257, 11008, 2, 8, 1), (1023, 4160, 2, 8, 1), (5000, 512, 2, 8, 1), (96, 512, 2, 8, 4),
+    (64, 512, 1, 8, 2),
 ]
 
 
@@ -329,16 +363,17 @@ def test_gemv_packed(aq, orc, case):
     out, in_, K, B, batch = case
     p = synth.make_problem(out, in_, K, B, batch=batch, sigma_cb=0.02, config=1500 + out + in_)
     codes, cb, x = _dev(p)
-    P = aq.pack_codebooks(cb)
+    W = aq.pack_weights(codes, cb)
     yref = orc.gemv(p["codes"], p["codebooks"], p["x"], K, B)
-    ys = [aq.gemv_packed(codes, P, x) for _ in range(2)]
+    ys = [aq.gemv_packed(W, x) for _ in range(2)]
     check_y(ys[0], yref, f"packed {case}")
-    assert bool((ys[0] == ys[1]).all())      # planes are summed in a fixed order
+    assert bool((ys[0] == ys[1]).all())      # partial sums are added in a fixed order
 
 
 @pytest.mark.parametrize("case", [("mlp_1x16_7b", 11008, 4096, 1), ("mlp_1x16_7b", 4096, 11008, 1),
                                   ("mlp_1x16_70b", 28672, 8192, 4), ("mlp_1x16_70b", 8192, 28672, 1),
-                                  ("proj_1x16_4096", 4096, 4096, 1)],
+                                  ("proj_1x16_4096", 4096, 4096, 1), ("mlp_2x8_7b", 11008, 4096, 1),
+                                  ("mlp_2x8_7b", 4096, 11008, 1)],
                          ids=lambda c: f"{c[0]}-{c[1]}x{c[2]}-b{c[3]}")
 def test_full_size_packed_sampled(aq, orc, case):
     import torch
@@ -348,7 +383,7 @@ def test_full_size_packed_sampled(aq, orc, case):
     p = synth.make_problem(out, in_, cfg["K"], cfg["B"], batch=batch, sigma_cb=cfg["sigma_cb"],
                            config=cid)
     codes, cb, x = _dev(p)
-    y = aq.gemv_packed(codes, aq.pack_codebooks(cb), x)
+    y = aq.gemv_packed(aq.pack_weights(codes, cb), x)
     torch.cuda.synchronize()
     rows = _sampled_rows(out, seed=cid)
     yref = orc.gemv_rows(p["codes"], p["codebooks"], p["x"], cfg["K"], cfg["B"], rows)
@@ -356,23 +391,25 @@ def test_full_size_packed_sampled(aq, orc, case):
     assert np.all(e <= TOL), f"{case}: {e.max():.3e}"
 
 
-def test_packed_graph_replay(aq, orc):
+@pytest.mark.parametrize("KB", [(1, 16), (2, 8)])
+def test_packed_graph_replay(aq, orc, KB):
     import torch
-    p = synth.make_problem(2000, 4096, 1, 16, batch=1, sigma_cb=0.02, config=1600)
+    K, B = KB
+    p = synth.make_problem(2000, 4096, K, B, batch=1, sigma_cb=0.02, config=1600 + K)
     codes, cb, x = _dev(p)
     stream = torch.cuda.Stream()
     with torch.cuda.stream(stream):
-        P = aq.pack_codebooks(cb)
-        eager = aq.gemv_packed(codes, P, x).clone()
+        W = aq.pack_weights(codes, cb)
+        eager = aq.gemv_packed(W, x).clone()
         y = torch.empty_like(eager)
         torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=stream):
-            aq.gemv_packed(codes, P, x, out=y)
+            aq.gemv_packed(W, x, out=y)
         for _ in range(3):
             y.fill_(3.0)
             torch.cuda.synchronize()
             g.replay()
             torch.cuda.synchronize()
             assert bool((y == eager).all())
-    check_y(eager, orc.gemv(p["codes"], p["codebooks"], p["x"], 1, 16), "packed eager")
+    check_y(eager, orc.gemv(p["codes"], p["codebooks"], p["x"], K, B), "packed eager")
