@@ -92,13 +92,10 @@ ds_kernel(const uint8_t *__restrict__ codes, const uint16_t *__restrict__ planes
         return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(rp + lane_off[sg]));
     };
 
-    // code loads first, so HBM latency overlaps with staging the plane
-    u32x4 ring[D];
-#pragma unroll
-    for (int q = 0; q < D; ++q) ring[q] = load_item(q, q % NSEG);
-
     {
-        // 128 KiB plane: every load of a thread issued before its LDS writes
+        // 128 KiB plane: every load of a thread issued before its LDS writes.  The
+        // plane gates all work, so it goes first; code loads issued with it would
+        // compete for the same bandwidth and delay it (about 2.5 us measured).
         const uint4 *src = reinterpret_cast<const uint4 *>(planes + size_t(p) * kEntries);
         uint4 *dst = reinterpret_cast<uint4 *>(tab);
         constexpr int PER = kEntries / 8 / (kDsWaves * kWave);
@@ -113,6 +110,10 @@ ds_kernel(const uint8_t *__restrict__ codes, const uint16_t *__restrict__ planes
     }
     __syncthreads();
     if (nitems == 0) return;
+
+    u32x4 ring[D];
+#pragma unroll
+    for (int q = 0; q < D; ++q) ring[q] = load_item(q, q % NSEG);
 
     // at batch 1 each lane's activations (GPC per chunk position) stay in registers
     constexpr bool XREG = NB == 1;

@@ -25,6 +25,14 @@
 //   inputs in a lane, so the product does not depend on how the hardware orders
 //   k inside a block.  Result (16x16): lane l, reg r -> row 4(l/16)+r, token l%16;
 //   (32x32): reg r -> row 8(r/4)+4(l/32)+(r%4), token l%32.
+//
+// Batch <= 32 uses a second kernel (mfma_kw_kernel): there a 16-row tile is too
+// little work to fill the chip with row tiles alone, so the 16 waves of a
+// workgroup take the same 16 rows and different 32-group units of the input
+// axis.  Each lane's A fragments are 8 consecutive groups of its row (one code
+// load), its B fragments the matching activations straight from global memory
+// (L2-resident), and the 16 partial tiles are added in LDS, in wave order, at
+// the end: no partial sums leave the workgroup.
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -282,6 +290,207 @@ hipError_t launch_kb(const Problem &p, const MfmaCfg &c, float *partial) {
     return launch_t<K, BITS, 32, 4>(p, c, partial);
 }
 
+
+// ---------------------------------------------------------------- batch <= 32
+constexpr int kKw = 16;                     // waves per workgroup, one share of the input each
+
+// the codes of 8 consecutive groups of one row: 8*K*BITS/32 dwords
+template <int K, int BITS> struct Seg {
+    static constexpr int NW = 8 * K * BITS / 32;
+};
+
+template <int K, int BITS>
+__device__ __forceinline__ void load_seg(const uint8_t *p, uint32_t (&w)[Seg<K, BITS>::NW]) {
+    constexpr int NW = Seg<K, BITS>::NW;
+    if constexpr (NW == 2) {
+        const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(p));
+        w[0] = v.x; w[1] = v.y;
+    } else {
+#pragma unroll
+        for (int h = 0; h < NW / 4; ++h) {
+            const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p) + h);
+            w[4 * h] = v.x; w[4 * h + 1] = v.y; w[4 * h + 2] = v.z; w[4 * h + 3] = v.w;
+        }
+    }
+}
+
+// code n of a segment (n = group * K + codebook, compile-time after unrolling)
+template <int BITS, int NW>
+__device__ __forceinline__ uint32_t seg_code(const uint32_t (&w)[NW], int n) {
+    if constexpr (BITS == 8) return (w[n >> 2] >> (8 * (n & 3))) & 0xFFu;
+    else return (w[n >> 1] >> (16 * (n & 1))) & 0xFFFFu;
+}
+
+// Persistent: one workgroup per CU walks 16-row tiles (tile, tile + grid, ...), with
+// the next tile's codes loaded while the current one is multiplied.  A wave owns
+// units wave, wave + 16, ... (at most MAXU); with a single unit its activations
+// are loaded once and kept in registers for every tile.
+template <int K, int BITS, int NT, int MAXU>
+__global__ void __launch_bounds__(kKw * kWave)
+mfma_kw_kernel(const uint8_t *__restrict__ codes, const uint16_t *__restrict__ cb,
+               const uint16_t *__restrict__ x, uint16_t *__restrict__ y, int out, int in,
+               int batch, int ntiles) {
+    constexpr int CBE = BITS == 8 ? K * 256 : 0;
+    constexpr int NW = Seg<K, BITS>::NW;
+    constexpr int CB = K * BITS / 8;                 // code bytes per group
+    __shared__ uint4 cbs[CBE > 0 ? CBE : 1];
+    __shared__ float red[2][kKw][NT * 4][kWave];     // double-buffered: one barrier per tile
+
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int G = in / kGroup;
+    const int U = (G + 31) / 32;                     // units of 32 groups
+    const int m = lane & 15, kb = lane >> 4;
+    const uint4 *cbg = reinterpret_cast<const uint4 *>(cb);
+
+    // lane (m, kb), unit u: groups g0 .. g0+7 of row m, g0 = 32u + 8kb; MFMA step s uses
+    // group g0 + s, so the 32 k of one step are groups {32u + 8kb + s : kb < 4}, in A
+    // and B alike.  Units past the last one are clamped for loading and masked in use.
+    auto seg_start = [&](int u) { return min(u * 32 + 8 * kb, G - 8); };
+    auto unit_of = [&](int i) { return wave + kKw * i; };
+    auto load_codes = [&](int tile, uint32_t (&cw)[MAXU][NW]) {
+        const int o = min(tile * 16 + m, out - 1);   // rows past the end: computed, not stored
+        const uint8_t *crow = codes + size_t(o) * size_t(G) * CB;
+#pragma unroll
+        for (int i = 0; i < MAXU; ++i)
+            load_seg<K, BITS>(crow + size_t(seg_start(min(unit_of(i), U - 1))) * CB, cw[i]);
+    };
+    auto load_x = [&](int u, half8 (&bx)[NT][8]) {
+        const bool ok = u * 32 + 8 * kb < G;
+        const int gc = seg_start(min(u, U - 1));
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            const int tok = t * 16 + m;
+            const bool okt = ok && tok < batch;
+            const uint16_t *xp = x + size_t(min(tok, batch - 1)) * in + size_t(gc) * kGroup;
+#pragma unroll
+            for (int s = 0; s < 8; ++s) {
+                const uint4 v = *reinterpret_cast<const uint4 *>(xp + s * kGroup);
+                bx[t][s] = okt ? __builtin_bit_cast(half8, v) : half8{};
+            }
+        }
+    };
+
+    // Every first load is issued before anything waits: the codebooks (one 16-byte
+    // vector per thread: K*256 <= 1024 threads), the first tile's codes and, with one
+    // unit per wave, the activations; the staging store then waits for the codebooks.
+    uint4 cbv{};
+    if constexpr (CBE > 0) cbv = cbg[min(int(threadIdx.x), CBE - 1)];
+    int tile = blockIdx.x;
+    uint32_t cw[MAXU][NW];
+    load_codes(tile, cw);
+    half8 bx[NT][8];
+    if constexpr (MAXU == 1) load_x(wave, bx);
+    if constexpr (CBE > 0) {
+        // unconditional (threads past the end rewrite the last vector with its own
+        // value), so the codebook load is not sunk behind the others
+        cbs[min(int(threadIdx.x), CBE - 1)] = cbv;
+        __syncthreads();
+    }
+
+    int buf = 0;
+    do {
+        // the next tile's codes replace each unit's codes as soon as they are decoded
+        // Past the last tile the reload is skipped (16-bit codes, whose codebook gathers
+        // share L2 with it) or repeats this tile's cached lines (8-bit codes: there the
+        // branch-free form measured faster).
+        const bool has_next = tile + int(gridDim.x) < ntiles;     // workgroup-uniform
+        const int next = has_next ? tile + int(gridDim.x) : tile;
+        const uint8_t *nrow = codes + size_t(min(next * 16 + m, out - 1)) * size_t(G) * CB;
+        float4v acc[NT];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) acc[t] = float4v{};
+#pragma unroll
+        for (int i = 0; i < MAXU; ++i) {
+            const int u = unit_of(i);
+            if (i > 0 && u >= U) break;              // wave-uniform; unit 0 always runs
+            if constexpr (MAXU > 1) load_x(u, bx);
+            const bool ok = u * 32 + 8 * kb < G;     // G is a multiple of 8
+            half8 a[8];
+#pragma unroll
+            for (int s = 0; s < 8; ++s) {
+                const uint32_t c0 = seg_code<BITS, NW>(cw[i], s * K);
+                half8 f = __builtin_bit_cast(half8, BITS == 8 ? cbs[c0] : cbg[c0]);
+                if constexpr (K == 2) {
+                    const uint32_t c1 = seg_code<BITS, NW>(cw[i], s * K + 1);
+                    f = f + __builtin_bit_cast(half8, BITS == 8 ? cbs[256 + c1]
+                                                                : cbg[(1u << 16) + c1]);
+                }
+                a[s] = ok ? f : half8{};
+            }
+            if (BITS == 8 || has_next)
+                load_seg<K, BITS>(nrow + size_t(seg_start(min(u, U - 1))) * CB, cw[i]);
+#pragma unroll
+            for (int s = 0; s < 8; ++s)
+#pragma unroll
+                for (int t = 0; t < NT; ++t)
+                    acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[s], bx[t][s], acc[t], 0, 0, 0);
+        }
+
+        // the 16 waves' tiles, added in wave order
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) red[buf][wave][t * 4 + r][lane] = acc[t][r];
+        __syncthreads();
+        const int row0 = tile * 16;
+        for (int e = threadIdx.x; e < NT * 4 * kWave; e += blockDim.x) {
+            const int tr = e / kWave, l = e % kWave;
+            float sum = 0.0f;
+#pragma unroll
+            for (int w = 0; w < kKw; ++w) sum += red[buf][w][tr][l];
+            const int t = tr >> 2, r = tr & 3;
+            const int row = row0 + 4 * (l >> 4) + r; // 16x16 result layout
+            const int tok = t * 16 + (l & 15);
+            if (row < out && tok < batch) y[size_t(tok) * out + row] = f2h_bits(sum);
+        }
+        buf ^= 1;
+        tile += gridDim.x;
+    } while (tile < ntiles);
+}
+
+// units per wave that fit the 128 registers of a 16-wave workgroup without spilling
+template <int K, int BITS>
+constexpr int kw_max_units(int nt) {
+    return nt > 1 ? 1 : (K * BITS > 16 ? 1 : 3);
+}
+
+template <int K, int BITS>
+hipError_t launch_kw(const Problem &p) {
+    const int G = int(p.in / kGroup);
+    const int U = (G + 31) / 32;
+    const int maxu = (U + kKw - 1) / kKw;
+    const int ntiles = int((p.out + 15) / 16);
+    const dim3 g(ntiles < 256 ? ntiles : 256), b(kKw * kWave);   // one workgroup per CU
+    const uint8_t *codes = static_cast<const uint8_t *>(p.codes);
+    const uint16_t *cb = static_cast<const uint16_t *>(p.codebooks);
+    const uint16_t *x = static_cast<const uint16_t *>(p.x);
+    uint16_t *y = static_cast<uint16_t *>(p.y);
+#define AQLM_KW(NT, MU)                                                                       \
+    hipLaunchKernelGGL((mfma_kw_kernel<K, BITS, NT, MU>), g, b, 0, p.stream, codes, cb, x, y, \
+                       int(p.out), int(p.in), p.batch, ntiles)
+    if (p.batch > 16) {
+        AQLM_KW(2, 1);
+    } else if (maxu <= 1) {
+        AQLM_KW(1, 1);
+    } else if constexpr (kw_max_units<K, BITS>(1) >= 3) {
+        if (maxu <= 2) AQLM_KW(1, 2);
+        else AQLM_KW(1, 3);
+    }
+#undef AQLM_KW
+    return hipGetLastError();
+}
+
+bool kw_fits(const Problem &p) {
+    const int64_t G = p.in / kGroup;
+    if (p.batch > 32 || G % 8) return false;
+    const int nt = p.batch > 16 ? 2 : 1;
+    const int64_t maxu = ((G + 31) / 32 + kKw - 1) / kKw;
+    const int lim = p.B == 8 ? (p.K == 1 ? kw_max_units<1, 8>(nt) : kw_max_units<2, 8>(nt))
+                             : (p.K == 1 ? kw_max_units<1, 16>(nt) : kw_max_units<2, 16>(nt));
+    return maxu <= lim;
+}
+
 }  // namespace
 
 bool mfma_supported(const Problem &p) {
@@ -298,12 +507,17 @@ bool mfma_supported(const Problem &p) {
 }
 
 size_t mfma_workspace_bytes(const Problem &p) {
+    if (kw_fits(p)) return 0;
     const MfmaCfg c = mfma_cfg(p);
     return c.ksplit > 1 ? size_t(c.ksplit) * size_t(p.batch) * size_t(p.out) * sizeof(float) : 0;
 }
 
 // workspace: KSPLIT x batch x out fp32 partial tiles (unused when KSPLIT = 1)
 hipError_t launch_mfma(const Problem &p, void *workspace) {
+    if (kw_fits(p)) {
+        if (p.B == 8) return p.K == 1 ? launch_kw<1, 8>(p) : launch_kw<2, 8>(p);
+        return p.K == 1 ? launch_kw<1, 16>(p) : launch_kw<2, 16>(p);
+    }
     const MfmaCfg c = mfma_cfg(p);
     float *partial = c.ksplit > 1 ? static_cast<float *>(workspace) : nullptr;
     hipError_t e;
