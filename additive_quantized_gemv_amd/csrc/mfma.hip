@@ -257,11 +257,10 @@ MfmaCfg mfma_cfg(const Problem &p) {
     c.grid_y = (p.batch + c.ms * c.nt - 1) / (c.ms * c.nt);
     const int64_t tiles = int64_t(c.grid_x) * c.grid_y;
     const int64_t nchunks = (G + chg - 1) / chg;
-    int64_t ks = (512 + tiles - 1) / tiles;          // about two workgroups per CU
-    // each split writes and re-reads batch*out fp32: keep that within twice the codes
-    const int64_t code_bytes_per_row = p.in / 4;     // 2 bits per weight
-    const int64_t cap = (2 * code_bytes_per_row) / (int64_t(p.batch) * 8);
-    if (ks > cap) ks = cap;
+    // About one workgroup per CU.  Measured on MI355X at batch 128 (4096 x 4096,
+    // 11008 x 4096, 4096 x 11008): fewer splits leave CUs idle, more cost more in the
+    // batch*out fp32 partial sums each split writes and the reduction re-reads.
+    int64_t ks = (256 + tiles - 1) / tiles;
     if (ks > nchunks) ks = nchunks;
     if (ks < 1) ks = 1;
     // whole chunks per split (multiples of 4 groups keep code blocks whole)
