@@ -153,6 +153,8 @@ def main():
     ap.add_argument("--batch", type=int, default=16, help="tokens for --workload layer7b")
     ap.add_argument("--scheme", default="2x8", choices=["2x8", "1x16"],
                     help="scheme for --workload layer7b")
+    ap.add_argument("--linears", default="q,k,v,o,gate,up,down",
+                    help="comma-separated subset of the layer's linears for --workload layer7b")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -339,21 +341,27 @@ def layer_bench(args, torch, np, aq, synth):
     (matrix cores from batch 16), rotating over copies larger than 2x the Infinity Cache."""
     K, B = (2, 8) if args.scheme == "2x8" else (1, 16)
     batch = args.batch
+    wanted = [n.strip() for n in args.linears.split(",") if n.strip()]
+    unknown = set(wanted) - {n for n, _, _ in LAYER_7B}
+    if unknown or not wanted:
+        print(f"unknown linears: {sorted(unknown)}", file=sys.stderr)
+        sys.exit(2)
+    layer = [e for e in LAYER_7B if e[0] in wanted]
     dev = torch.device("cuda:0")
-    per_copy = sum(algorithmic_bytes(o, i, K, B, batch) for _, o, i in LAYER_7B)
+    per_copy = sum(algorithmic_bytes(o, i, K, B, batch) for _, o, i in layer)
     copies = args.copies or max(2, math.ceil(2 * MALL_BYTES / per_copy))
     sets = []
     for r in range(copies):
         entry = []
-        for li, (name, out, in_) in enumerate(LAYER_7B):
+        for li, (name, out, in_) in enumerate(layer):
             p = synth.make_problem(out, in_, K, B, batch=batch, sigma_cb=SIGMA_CB,
                                    config=400 + li, copy=r)
             codes = p["codes"] if B == 8 else p["codes"].view(np.int16)
             entry.append((torch.from_numpy(codes).to(dev), torch.from_numpy(p["codebooks"]).to(dev),
                           torch.from_numpy(p["x"]).to(dev)))
         sets.append(entry)
-    ys = [torch.empty((batch, out), dtype=torch.float16, device=dev) for _, out, _ in LAYER_7B]
-    variants = [aq.selected_variant(*sets[0][i], gemm=True) for i in range(len(LAYER_7B))]
+    ys = [torch.empty((batch, out), dtype=torch.float16, device=dev) for _, out, _ in layer]
+    variants = [aq.selected_variant(*sets[0][i], gemm=True) for i in range(len(layer))]
     stream = torch.cuda.Stream()
 
     def call(i, r):
@@ -362,15 +370,15 @@ def layer_bench(args, torch, np, aq, synth):
     torch.cuda.synchronize()
     with torch.cuda.stream(stream):
         for w in range(max(2, args.warmup // 10)):
-            for i in range(len(LAYER_7B)):
+            for i in range(len(layer)):
                 call(i, w % copies)
         torch.cuda.synchronize()
-        layer = capture_on(torch, stream, lambda: [call(i, r) for r in range(copies)
-                                                   for i in range(len(LAYER_7B))])
+        layer_graph = capture_on(torch, stream, lambda: [call(i, r) for r in range(copies)
+                                                         for i in range(len(layer))])
         reps = max(1, args.steps // copies)
-        dt_layer = time_graph(torch, layer, reps) / (reps * copies)
+        dt_layer = time_graph(torch, layer_graph, reps) / (reps * copies)
         per = []
-        for i, (name, out, in_) in enumerate(LAYER_7B):
+        for i, (name, out, in_) in enumerate(layer):
             g = capture_on(torch, stream, lambda i=i: [call(i, r) for r in range(copies)])
             dt = time_graph(torch, g, reps) / (reps * copies)
             nbytes = algorithmic_bytes(out, in_, K, B, batch)
@@ -379,22 +387,22 @@ def layer_bench(args, torch, np, aq, synth):
                         "us_per_call": round(dt * 1e6, 3), "gbps": round(nbytes / dt / 1e9, 1),
                         "tflops": round(flops / dt / 1e12, 2)})
     layer_bytes = per_copy
-    layer_flops = sum(2.0 * o * i * batch for _, o, i in LAYER_7B)
+    layer_flops = sum(2.0 * o * i * batch for _, o, i in layer)
     dom = max(range(len(per)), key=lambda i: per[i]["us_per_call"])
     d = per[dom]
     mfma = batch >= 16
     if mfma:
-        achieved = 2.0 * LAYER_7B[dom][1] * LAYER_7B[dom][2] * batch / (d["us_per_call"] * 1e-6) / 1e12
+        achieved = 2.0 * layer[dom][1] * layer[dom][2] * batch / (d["us_per_call"] * 1e-6) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_PEAK_FP16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / MFMA_PEAK_FP16_TFLOPS, 4),
                 "traffic": None, "kernel": f"{d['variant']} ({d['linear']} {d['shape']})"}
     else:
-        achieved = algorithmic_bytes(LAYER_7B[dom][1], LAYER_7B[dom][2], K, B, batch) / (d["us_per_call"] * 1e-6) / 1e9
+        achieved = algorithmic_bytes(layer[dom][1], layer[dom][2], K, B, batch) / (d["us_per_call"] * 1e-6) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
                 "kernel": f"{d['variant']} ({d['linear']} {d['shape']})"}
-    result = {"metric": f"AQLM {args.scheme} Llama-2-7B layer (7 linears), batch {batch}: "
-                        "layer time and achieved rates",
+    result = {"metric": f"AQLM {args.scheme} Llama-2-7B layer ({','.join(n for n, _, _ in layer)}), "
+                        f"batch {batch}: layer time and achieved rates",
               "value": round(layer_bytes / dt_layer / 1e9, 1), "unit": "GB/s",
               "n_gpus": 1, "steps": reps * copies, "warmup": max(2, args.warmup // 10),
               "ms_per_step": round(dt_layer * 1e3, 5), "higher_is_better": True,
