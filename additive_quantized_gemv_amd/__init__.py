@@ -18,6 +18,7 @@ import os
 
 __all__ = ["gemv", "gemm", "gemv_variant", "gemv_packed", "pack_codebooks", "unpack_codebooks",
            "pack_codes", "unpack_codes", "packed_codes_bytes", "PackedWeights", "pack_weights",
+           "gemv_grouped", "gemm_grouped", "gemv_packed_grouped",
            "dequantize", "bits_per_weight", "codes_bytes",
            "codebooks_bytes", "variant_supported", "selected_variant", "VARIANTS", "library_path",
            "AqlmError", "version"]
@@ -65,6 +66,11 @@ def _load():
     lib.aqlm_selected_variant.restype = ci
     lib.aqlm_gemv_packed.argtypes = prod
     lib.aqlm_gemv_packed.restype = ci
+    grouped = [ci, ctypes.POINTER(vp), ctypes.POINTER(vp), vp, ctypes.POINTER(vp),
+               ctypes.POINTER(i64), i64, ci, ci, ci, vp]
+    for name in ("aqlm_gemv_grouped", "aqlm_gemm_grouped", "aqlm_gemv_packed_grouped"):
+        getattr(lib, name).argtypes = grouped
+        getattr(lib, name).restype = ci
     lib.aqlm_packed_codes_bytes.argtypes = [i64, i64, ci, ci]
     lib.aqlm_packed_codes_bytes.restype = i64
     for name in ("aqlm_pack_codes", "aqlm_unpack_codes"):
@@ -219,6 +225,63 @@ def gemv_packed(weights: PackedWeights, x, out=None):
                                 y.data_ptr(), w.out_features, w.in_features, w.K, w.B, batch,
                                 _stream()), "aqlm_gemv_packed")
     return y if x.dim() == 2 else y[0]
+
+
+def _grouped(fn_name, codes, codebooks, x, out_features, in_features, K, B, outs):
+    torch = _torch()
+    lib = _load()
+    n = len(codes)
+    if n < 1 or n > 4 or len(codebooks) != n:
+        raise ValueError("1 to 4 matrices, each with codes and codebooks")
+    if x.dtype != torch.float16:
+        raise TypeError("x must be float16")
+    x2 = x.unsqueeze(0) if x.dim() == 1 else x
+    if x2.dim() != 2 or x2.shape[1] != in_features or not x2.is_cuda or not x2.is_contiguous():
+        raise ValueError("x must be a contiguous device [batch][in] tensor")
+    batch = x2.shape[0]
+    ys = outs if outs is not None else [
+        torch.empty((batch, o), dtype=torch.float16, device=x2.device) for o in out_features]
+    for y, o in zip(ys, out_features):
+        if y.dtype != torch.float16 or tuple(y.shape) != (batch, o) or not y.is_contiguous():
+            raise ValueError("each out must be a contiguous float16 [batch][out] tensor")
+    vp = ctypes.c_void_p
+    arr = lambda ts: (vp * n)(*[t.data_ptr() for t in ts])
+    outs_arr = (ctypes.c_int64 * n)(*out_features)
+    _check(getattr(lib, fn_name)(n, arr(codes), arr(codebooks), x2.data_ptr(), arr(ys), outs_arr,
+                                 in_features, K, B, batch, _stream()), fn_name)
+    return ys if x.dim() == 2 else [y[0] for y in ys]
+
+
+def _grouped_canonical(fn_name, codes, codebooks, x, out):
+    K, B, x2 = _prep(codes[0], codebooks[0], x, None, None)
+    for c, cb in zip(codes, codebooks):
+        _prep(c, cb, x, K, B)
+    return _grouped(fn_name, codes, codebooks, x, [c.shape[0] for c in codes],
+                    codes[0].shape[1] * 8, K, B, out)
+
+
+def gemv_grouped(codes, codebooks, x, out=None):
+    """[W_m x for each m] in one launch: lists of codes and codebooks of matrices that share x."""
+    return _grouped_canonical("aqlm_gemv_grouped", codes, codebooks, x, out)
+
+
+def gemm_grouped(codes, codebooks, x, out=None):
+    """gemv_grouped with the matrix-core kernels from batch 16 (as gemm)."""
+    return _grouped_canonical("aqlm_gemm_grouped", codes, codebooks, x, out)
+
+
+def gemv_packed_grouped(weights, x, out=None):
+    """[W_m x for each m] in one launch from a list of PackedWeights that share x."""
+    w0 = weights[0]
+    for w in weights:
+        if (w.in_features, w.K, w.B) != (w0.in_features, w0.K, w0.B):
+            raise ValueError("grouped matrices must share in_features, K and B")
+        if w.codes.numel() * w.codes.element_size() != packed_codes_bytes(
+                w.out_features, w.in_features, w.K, w.B):
+            raise ValueError("packed codes have the wrong size")
+    return _grouped("aqlm_gemv_packed_grouped", [w.codes for w in weights],
+                    [w.codebooks for w in weights], x, [w.out_features for w in weights],
+                    w0.in_features, w0.K, w0.B, out)
 
 
 def packed_codes_bytes(out_features, in_features, K, B) -> int:

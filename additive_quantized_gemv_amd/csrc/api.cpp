@@ -94,8 +94,20 @@ aqlm_status_t check_args(const void *codes, const void *cb, const void *x, const
 
 aqlm::Problem make_problem(const void *codes, const void *cb, const void *x, void *y, int64_t out,
                            int64_t in, int K, int B, int batch, void *stream) {
-    return aqlm::Problem{codes, cb, x, y, out, in, K, B, batch,
-                         static_cast<hipStream_t>(stream)};
+    aqlm::Problem p{codes, cb, x, y, out, in, K, B, batch, static_cast<hipStream_t>(stream), {}};
+    p.segs.n = 1;
+    p.segs.row0[0] = 0;
+    p.segs.row0[1] = int(out);          // callers keep out <= 2^30 for the tuned kernels
+    p.segs.codes[0] = codes;
+    p.segs.cb[0] = cb;
+    p.segs.y[0] = y;
+    return p;
+}
+
+// Matrix m of a grouped problem as a problem of its own.
+aqlm::Problem segment(const aqlm::Problem &p, int m) {
+    return make_problem(p.segs.codes[m], p.segs.cb[m], p.x, p.segs.y[m],
+                        p.segs.row0[m + 1] - p.segs.row0[m], p.in, p.K, p.B, p.batch, p.stream);
 }
 
 // Packed codes: tiles of 8 rows x 64 groups for 2x8 (the lookup-table kernel's
@@ -110,7 +122,22 @@ int64_t packed_codes_size(int64_t out, int64_t in, int K, int B) {
     return aqlm::lut_packed_codes_bytes(out, in);
 }
 
+// f holds for the whole problem and for each of its matrices
+template <class F>
+bool all_segments(const aqlm::Problem &p, F f) {
+    if (!f(p)) return false;
+    for (int m = 0; p.segs.n > 1 && m < p.segs.n; ++m)
+        if (!f(segment(p, m))) return false;
+    return true;
+}
+
+bool supported_one(int variant, const aqlm::Problem &p);
+
 bool supported(int variant, const aqlm::Problem &p) {
+    return all_segments(p, [variant](const aqlm::Problem &q) { return supported_one(variant, q); });
+}
+
+bool supported_one(int variant, const aqlm::Problem &p) {
     switch (variant) {
         case AQLM_VARIANT_GENERIC: return true;
         case AQLM_VARIANT_LDS: return p.B == 8 && aqlm::gather_supported(p);
@@ -198,6 +225,14 @@ aqlm_status_t run(int variant, const aqlm::Problem &p) {
         std::fprintf(stderr, "[aqlm] %s out=%lld in=%lld K=%d B=%d batch=%d\n",
                      aqlm_variant_name(variant), (long long)p.out, (long long)p.in, p.K, p.B,
                      p.batch);
+    // kernels without a matrix table run once per matrix
+    if (p.segs.n > 1 && (variant == AQLM_VARIANT_LDS || variant == AQLM_VARIANT_GENERIC)) {
+        for (int m = 0; m < p.segs.n; ++m) {
+            const aqlm_status_t st = run(variant, segment(p, m));
+            if (st != AQLM_OK) return st;
+        }
+        return AQLM_OK;
+    }
     switch (variant) {
         case AQLM_VARIANT_LDS: e = aqlm::launch_gather(p); break;
         case AQLM_VARIANT_L2: e = aqlm::launch_l2(p); break;
@@ -212,7 +247,10 @@ aqlm_status_t run(int variant, const aqlm::Problem &p) {
                 if (log_enabled())
                     std::fprintf(stderr, "[aqlm] lut: no workspace on a capturing stream, "
                                          "using the gather kernel\n");
-                e = aqlm::gather_supported(p) ? aqlm::launch_gather(p) : aqlm::launch_generic(p);
+                for (int m = 0; m < p.segs.n && e == hipSuccess; ++m) {
+                    const aqlm::Problem q = segment(p, m);
+                    e = aqlm::gather_supported(q) ? aqlm::launch_gather(q) : aqlm::launch_generic(q);
+                }
             }
             break;
         }
@@ -224,19 +262,67 @@ aqlm_status_t run(int variant, const aqlm::Problem &p) {
                 if (e != hipSuccess) break;
                 if (!ws) {
                     // capturing stream without a workspace: same product, no workspace needed
-                    e = aqlm::launch_generic(p);
+                    for (int m = 0; m < p.segs.n && e == hipSuccess; ++m)
+                        e = aqlm::launch_generic(segment(p, m));
                     break;
                 }
             }
             e = aqlm::launch_mfma(p, ws);
             break;
         }
-        default: e = aqlm::launch_generic(p); break;
+        default:
+            for (int m = 0; m < p.segs.n && e == hipSuccess; ++m) e = aqlm::launch_generic(segment(p, m));
+            break;
     }
     if (e != hipSuccess) {
         set_error(aqlm_variant_name(variant), e);
         return AQLM_ERR_HIP;
     }
+    return AQLM_OK;
+}
+
+// Validates a grouped call and builds its problem (out = the total rows).  packed: the
+// codes are in the packed layout of aqlm_pack_codes.
+aqlm_status_t grouped_problem(int n, const void *const *codes, const void *const *codebooks,
+                              const void *x, void *const *y, const int64_t *out_features,
+                              int64_t in, int K, int B, int batch, void *stream, bool packed,
+                              aqlm::Problem *out) {
+    if (n < 1 || n > aqlm::kMaxSegs || !codes || !codebooks || !y || !out_features)
+        return AQLM_ERR_INVALID_ARGUMENT;
+    int64_t total = 0, code_bytes[aqlm::kMaxSegs];
+    Sizes s{};
+    for (int m = 0; m < n; ++m) {
+        const aqlm_status_t st =
+            check_args(codes[m], codebooks[m], x, y[m], out_features[m], in, K, B, batch, &s);
+        if (st != AQLM_OK) return st;
+        code_bytes[m] = packed ? packed_codes_size(out_features[m], in, K, B) : s.codes;
+        if (code_bytes[m] < 0) return AQLM_ERR_INVALID_ARGUMENT;
+        total += out_features[m];
+    }
+    if (total > (int64_t(1) << 30)) return AQLM_ERR_INVALID_ARGUMENT;
+    // no output may overlap any input or another output
+    for (int m = 0; m < n; ++m) {
+        const int64_t ym = int64_t(batch) * out_features[m] * 2;
+        for (int j = 0; j < n; ++j) {
+            if (overlaps(y[m], ym, codes[j], code_bytes[j]) ||
+                overlaps(y[m], ym, codebooks[j], s.codebooks))
+                return AQLM_ERR_INVALID_ARGUMENT;
+            if (j != m && overlaps(y[m], ym, y[j], int64_t(batch) * out_features[j] * 2))
+                return AQLM_ERR_INVALID_ARGUMENT;
+        }
+    }
+    aqlm::Problem p = make_problem(codes[0], codebooks[0], x, y[0], total, in, K, B, batch, stream);
+    p.segs.n = n;
+    int r = 0;
+    for (int m = 0; m < n; ++m) {
+        p.segs.row0[m] = r;
+        r += int(out_features[m]);
+        p.segs.codes[m] = codes[m];
+        p.segs.cb[m] = codebooks[m];
+        p.segs.y[m] = y[m];
+    }
+    p.segs.row0[n] = r;
+    *out = p;
     return AQLM_OK;
 }
 
@@ -415,29 +501,60 @@ aqlm_status_t aqlm_unpack_codes(const void *packed, void *codes, int64_t out_fea
 aqlm_status_t aqlm_gemv_packed(const void *packed_codes, const void *packed_codebooks,
                                const void *x, void *y, int64_t out_features, int64_t in_features,
                                int K, int B, int batch, void *stream) {
-    Sizes s;
-    aqlm_status_t st = check_args(packed_codes, packed_codebooks, x, y, out_features, in_features,
-                                  K, B, batch, &s);
+    const void *c[1] = {packed_codes}, *cb[1] = {packed_codebooks};
+    void *yy[1] = {y};
+    const int64_t o[1] = {out_features};
+    return aqlm_gemv_packed_grouped(1, c, cb, x, yy, o, in_features, K, B, batch, stream);
+}
+
+aqlm_status_t aqlm_gemv_grouped(int n, const void *const *codes, const void *const *codebooks,
+                                const void *x, void *const *y, const int64_t *out_features,
+                                int64_t in_features, int K, int B, int batch, void *stream) {
+    aqlm::Problem p;
+    const aqlm_status_t st = grouped_problem(n, codes, codebooks, x, y, out_features, in_features,
+                                             K, B, batch, stream, false, &p);
+    return st != AQLM_OK ? st : run(choose(false, p), p);
+}
+
+aqlm_status_t aqlm_gemm_grouped(int n, const void *const *codes, const void *const *codebooks,
+                                const void *x, void *const *y, const int64_t *out_features,
+                                int64_t in_features, int K, int B, int batch, void *stream) {
+    aqlm::Problem p;
+    const aqlm_status_t st = grouped_problem(n, codes, codebooks, x, y, out_features, in_features,
+                                             K, B, batch, stream, false, &p);
+    return st != AQLM_OK ? st : run(choose(true, p), p);
+}
+
+aqlm_status_t aqlm_gemv_packed_grouped(int n, const void *const *packed_codes,
+                                       const void *const *packed_codebooks, const void *x,
+                                       void *const *y, const int64_t *out_features,
+                                       int64_t in_features, int K, int B, int batch,
+                                       void *stream) {
+    aqlm::Problem p;
+    aqlm_status_t st = grouped_problem(n, packed_codes, packed_codebooks, x, y, out_features,
+                                       in_features, K, B, batch, stream, true, &p);
     if (st != AQLM_OK) return st;
-    const int64_t pbytes = packed_codes_size(out_features, in_features, K, B);
-    if (pbytes < 0 || overlaps(y, s.y, packed_codes, pbytes)) return AQLM_ERR_INVALID_ARGUMENT;
-    aqlm::Problem p = make_problem(packed_codes, packed_codebooks, x, y, out_features, in_features,
-                                   K, B, batch, stream);
     const bool generic = forced_variant() == AQLM_VARIANT_GENERIC;
     const bool tiled = tiled_codes(K, B);
-    int path;  // 0: split kernel, 1: packed lookup-table kernel, 2: unpack into the workspace
-    size_t need;
-    const size_t cb_off = (size_t(s.codes) + 255) / 256 * 256;
-    if (!generic && !tiled && aqlm::ds_supported(p)) {
-        path = 0;
-        need = aqlm::ds_workspace_bytes(p);
-    } else if (!generic && tiled && aqlm::lut_packed_supported(p)) {
-        path = 1;
-        need = aqlm::lut_packed_workspace_bytes(p);
-    } else {
-        path = 2;
-        need = tiled ? cb_off + size_t(s.codebooks) : size_t(s.codebooks);
+    const bool split = !generic && !tiled &&
+                       all_segments(p, [](const aqlm::Problem &q) { return aqlm::ds_supported(q); });
+    const bool lutp = !generic && tiled &&
+                      all_segments(p, [](const aqlm::Problem &q) { return aqlm::lut_packed_supported(q); });
+    if (!split && !lutp && n > 1) {
+        // unpacked one matrix at a time through the workspace (stream order keeps them apart)
+        for (int m = 0; m < n; ++m) {
+            st = aqlm_gemv_packed_grouped(1, packed_codes + m, packed_codebooks + m, x, y + m,
+                                          out_features + m, in_features, K, B, batch, stream);
+            if (st != AQLM_OK) return st;
+        }
+        return AQLM_OK;
     }
+    const int64_t cbytes = out_features[0] * (in_features / kGroup) * K * (B / 8);
+    const int64_t cbbytes = int64_t(K) * (int64_t(1) << B) * kGroup * 2;
+    const size_t cb_off = (size_t(cbytes) + 255) / 256 * 256;
+    const size_t need = split  ? aqlm::ds_workspace_bytes(p)
+                        : lutp ? aqlm::lut_packed_workspace_bytes(p)
+                        : tiled ? cb_off + size_t(cbbytes) : size_t(cbbytes);
     void *ws = nullptr;
     hipError_t e = get_workspace(p.stream, need, &ws);
     if (e != hipSuccess) {
@@ -446,40 +563,40 @@ aqlm_status_t aqlm_gemv_packed(const void *packed_codes, const void *packed_code
     }
     if (!ws) return AQLM_ERR_UNSUPPORTED;   // capturing stream without a workspace
     if (log_enabled())
-        std::fprintf(stderr, "[aqlm] packed %s out=%lld in=%lld K=%d B=%d batch=%d\n",
-                     path == 0 ? "split" : path == 1 ? "lut_packed" : "unpack+auto",
-                     (long long)p.out, (long long)p.in, K, B, batch);
-    if (path == 0 || path == 1) {
-        e = path == 0 ? aqlm::launch_ds(p, ws) : aqlm::launch_lut_packed(p, ws);
+        std::fprintf(stderr, "[aqlm] packed %s n=%d rows=%lld in=%lld K=%d B=%d batch=%d\n",
+                     split ? "split" : lutp ? "lut_packed" : "unpack+auto", n, (long long)p.out,
+                     (long long)p.in, K, B, batch);
+    if (split || lutp) {
+        e = split ? aqlm::launch_ds(p, ws) : aqlm::launch_lut_packed(p, ws);
         if (e != hipSuccess) {
-            set_error(path == 0 ? "split" : "lut_packed", e);
+            set_error(split ? "split" : "lut_packed", e);
             return AQLM_ERR_HIP;
         }
         return AQLM_OK;
     }
+    // one matrix: unpack into the workspace and run as aqlm_gemv
     char *wsb = static_cast<char *>(ws);
     if (tiled) {
-        e = aqlm::launch_pack_codes_lut(packed_codes, wsb, out_features, in_features, false,
-                                        p.stream);
+        e = aqlm::launch_pack_codes_lut(p.codes, wsb, p.out, p.in, false, p.stream);
         if (e != hipSuccess) {
             set_error("unpack_codes", e);
             return AQLM_ERR_HIP;
         }
-        p.codes = wsb;
     }
     void *cbws = tiled ? wsb + cb_off : wsb;
-    e = aqlm::launch_unpack_codebooks(packed_codebooks, cbws, K, B, p.stream);
+    e = aqlm::launch_unpack_codebooks(p.codebooks, cbws, K, B, p.stream);
     if (e != hipSuccess) {
         set_error("unpack_codebooks", e);
         return AQLM_ERR_HIP;
     }
-    p.codebooks = cbws;
-    int v = choose(false, p);
+    aqlm::Problem q = make_problem(tiled ? wsb : p.codes, cbws, p.x, p.y, p.out, p.in, K, B,
+                                   batch, stream);
+    int v = choose(false, q);
     if (v == AQLM_VARIANT_LUT) v = AQLM_VARIANT_LDS;   // the workspace holds the operands
-    return run(v, p);
+    return run(v, q);
 }
 
-const char *aqlm_version(void) { return "0.3.0"; }
+const char *aqlm_version(void) { return "0.4.0"; }
 
 const char *aqlm_last_error(void) { return g_last_error; }
 

@@ -1,5 +1,6 @@
 // Device-side helpers shared by the gfx950 kernels of libaqlm_mi355x.
 #pragma once
+#define AQLM_DEVICE_COMMON
 
 #include <hip/hip_runtime.h>
 #include <hip/hip_fp16.h>
@@ -150,6 +151,46 @@ __device__ __forceinline__ float transpose_reduce(float *v, int lane) {
     static_assert((1 << LOG) == R, "R must be a power of two");
     butterfly_levels<R, 0>(v, lane);
     return allreduce_levels<LOG>(v[0]);
+}
+
+// The index m (< n <= 4) with bounds[m] <= v < bounds[m + 1]; bounds ascending.
+__device__ __forceinline__ int range_of(int n, const int *bounds, int v) {
+    int m = 0;
+#pragma unroll
+    for (int i = 1; i < 4; ++i) m += (i < n && v >= bounds[i]) ? 1 : 0;
+    return m;
+}
+
+// a[m] for a uniform m (a matrix-table lookup).
+template <class T, int N>
+__device__ __forceinline__ T pick(const T (&a)[N], int m) {
+    T r = a[0];
+#pragma unroll
+    for (int i = 1; i < N; ++i) r = (m == i) ? a[i] : r;
+    return r;
+}
+
+
+// Makes the (wave-uniform) kernel arguments given live in scalar registers at this point,
+// so their loads are issued together and waited for once, before what follows.
+// Matrix-table lookups of a kernel compiled for NS matrices: with NS = 1 the index is the
+// constant 0 and the table's other entries are never read.
+template <int NS, int N>
+__device__ __forceinline__ int seg_of(int n, const int (&bounds)[N], int v) {
+    return NS == 1 ? 0 : range_of(n, bounds, v);
+}
+template <int NS, int N>
+__device__ __forceinline__ int seg_total(int n, const int (&row0)[N]) {
+    return NS == 1 ? row0[1] : pick(row0, n);
+}
+
+template <class T>
+__device__ __forceinline__ void scalar_ready(const T &v) {
+    asm volatile("" ::"s"(v));
+}
+template <class... A>
+__device__ __forceinline__ void scalars_ready(const A &...a) {
+    (scalar_ready(a), ...);
 }
 
 __device__ __forceinline__ int lane_id() { return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)); }

@@ -41,11 +41,11 @@ struct DsShape {
     static constexpr int D = NSEG * RB;
 };
 
-template <int K, int NB, int NSEG>
+template <int K, int NB, int NSEG, int NS>
 __global__ void __launch_bounds__(kDsWaves * kWave)
-ds_kernel(const uint8_t *__restrict__ codes, const uint16_t *__restrict__ planes,
-          const uint16_t *__restrict__ x, float *__restrict__ partial, int out, int in,
-          int batch, int nranges, int rows_per_range) {
+ds_kernel(const uint8_t *__restrict__ codes1, const uint16_t *__restrict__ planes1,
+          const uint16_t *__restrict__ x, float *__restrict__ partial, int out1, int in,
+          int batch, int nranges, int rows_per_range, const Segs segs) {
     constexpr int P = K * 8;                 // planes
     constexpr int GPC = 8 / K;               // groups per 16-byte chunk
     constexpr int RB = DsShape<NSEG>::RB;
@@ -60,13 +60,24 @@ ds_kernel(const uint8_t *__restrict__ codes, const uint16_t *__restrict__ planes
     const int rr = grp * 8 + (rem & 7);
     if (rr >= nranges) return;
     const int k = p >> 3, t = p & 7;
+    // this range's matrix: the arguments for one matrix (NS == 1), else from segs
+    // (ranges of each matrix numbered consecutively, segs.aux0)
+    const int mi = seg_of<NS>(segs.n, segs.aux0, rr);
+    const int lrr = NS == 1 ? rr : rr - pick(segs.aux0, mi);
+    const int out = NS == 1 ? out1 : pick(segs.row0, mi + 1) - pick(segs.row0, mi);
+    const int T = NS == 1 ? out1 : segs.row0[segs.n];
+    const int orow0 = NS == 1 ? 0 : pick(segs.row0, mi);
+    const uint8_t *__restrict__ codes =
+        NS == 1 ? codes1 : static_cast<const uint8_t *>(pick(segs.codes, mi));
+    const uint16_t *__restrict__ planes =
+        NS == 1 ? planes1 : static_cast<const uint16_t *>(pick(segs.cb, mi));
 
     const int lane = threadIdx.x & (kWave - 1);
     // wave-uniform values live in scalar registers
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int G = in / kGroup;
     const int NC = G / GPC;                  // chunks per row
-    const int r_begin = rr * rows_per_range;
+    const int r_begin = lrr * rows_per_range;
     const int r_end = min(out, r_begin + rows_per_range);
     const int rpw = (rows_per_range + kDsWaves - 1) / kDsWaves;
     const int w_begin = r_begin + wave * rpw;
@@ -185,26 +196,10 @@ ds_kernel(const uint8_t *__restrict__ codes, const uint16_t *__restrict__ planes
                 const float s = transpose_reduce<RB>(v, lane);
                 const int row = row0 + lane / (kWave / RB);
                 if ((lane & (kWave / RB - 1)) == 0 && row < w_end)
-                    partial[(size_t(p) * batch + b) * out + row] = s;
+                    partial[(size_t(p) * batch + b) * T + orow0 + row] = s;
             }
         }
     }
-}
-
-// y[i] = sum over planes (in order) of partial[plane][i], i over batch * out
-__global__ void __launch_bounds__(256)
-ds_reduce_kernel(const float *__restrict__ partial, uint16_t *__restrict__ y, int n, int planes) {
-    const int i = blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= n) return;
-    float s = 0.0f;
-    for (int p0 = 0; p0 < planes; p0 += 8) {
-        float v[8];
-#pragma unroll
-        for (int q = 0; q < 8; ++q) v[q] = (p0 + q < planes) ? partial[size_t(p0 + q) * n + i] : 0.0f;
-#pragma unroll
-        for (int q = 0; q < 8; ++q) s += v[q];
-    }
-    y[i] = f2h_bits(s);
 }
 
 // planes[k][t][c] = codebooks[k][c][t]
@@ -235,7 +230,9 @@ struct DsCfg {
     int nseg, nranges, nranges_padded, rows_per_range, grid;
 };
 
-DsCfg ds_cfg(const Problem &p) {
+// Row ranges of rows_per_range rows, about max(8, 256 / planes) of them over all matrices
+// (one workgroup per CU); each matrix gets whole ranges of its own (segs.aux0).
+DsCfg ds_cfg(const Problem &p, Segs *segs = nullptr) {
     DsCfg c{};
     const int P = p.K * 8;
     const int64_t G = p.in / kGroup;
@@ -245,41 +242,54 @@ DsCfg ds_cfg(const Problem &p) {
     if (nr < 8) nr = 8;
     if (nr > p.out) nr = int(p.out);
     c.rows_per_range = int((p.out + nr - 1) / nr);
-    c.nranges = int((p.out + c.rows_per_range - 1) / c.rows_per_range);
+    int total = 0;
+    for (int m = 0; m < p.segs.n; ++m) {
+        if (segs) segs->aux0[m] = total;
+        total += (p.segs.row0[m + 1] - p.segs.row0[m] + c.rows_per_range - 1) / c.rows_per_range;
+    }
+    if (segs) segs->aux0[p.segs.n] = total;
+    c.nranges = total;
     c.nranges_padded = (c.nranges + 7) / 8 * 8;
     c.grid = P * c.nranges_padded;
     return c;
 }
 
 template <int K, int NB, int NSEG>
-hipError_t launch3(const Problem &p, const DsCfg &c, float *partial) {
-    hipLaunchKernelGGL((ds_kernel<K, NB, NSEG>), dim3(c.grid), dim3(kDsWaves * kWave), 0, p.stream,
-                       static_cast<const uint8_t *>(p.codes),
-                       static_cast<const uint16_t *>(p.codebooks),
-                       static_cast<const uint16_t *>(p.x), partial, int(p.out), int(p.in), p.batch,
-                       c.nranges, c.rows_per_range);
+hipError_t launch3(const Problem &p, const DsCfg &c, const Segs &segs, float *partial) {
+    const dim3 g(c.grid), b(kDsWaves * kWave);
+    const uint16_t *x = static_cast<const uint16_t *>(p.x);
+    const uint8_t *codes = static_cast<const uint8_t *>(segs.codes[0]);
+    const uint16_t *planes = static_cast<const uint16_t *>(segs.cb[0]);
+    const int out = segs.row0[1];
+    if (segs.n == 1)
+        hipLaunchKernelGGL((ds_kernel<K, NB, NSEG, 1>), g, b, 0, p.stream, codes, planes, x,
+                           partial, out, int(p.in), p.batch, c.nranges, c.rows_per_range, segs);
+    else
+        hipLaunchKernelGGL((ds_kernel<K, NB, NSEG, kMaxSegs>), g, b, 0, p.stream, codes, planes,
+                           x, partial, out, int(p.in), p.batch, c.nranges, c.rows_per_range,
+                           segs);
     return hipGetLastError();
 }
 
 template <int K, int NB>
-hipError_t launch2(const Problem &p, const DsCfg &c, float *partial) {
+hipError_t launch2(const Problem &p, const DsCfg &c, const Segs &segs, float *partial) {
     switch (c.nseg) {
-        case 1: return launch3<K, NB, 1>(p, c, partial);
-        case 2: return launch3<K, NB, 2>(p, c, partial);
-        case 3: return launch3<K, NB, 3>(p, c, partial);
-        case 4: return launch3<K, NB, 4>(p, c, partial);
-        case 5: return launch3<K, NB, 5>(p, c, partial);
-        case 6: return launch3<K, NB, 6>(p, c, partial);
-        case 7: return launch3<K, NB, 7>(p, c, partial);
-        default: return launch3<K, NB, 8>(p, c, partial);
+        case 1: return launch3<K, NB, 1>(p, c, segs, partial);
+        case 2: return launch3<K, NB, 2>(p, c, segs, partial);
+        case 3: return launch3<K, NB, 3>(p, c, segs, partial);
+        case 4: return launch3<K, NB, 4>(p, c, segs, partial);
+        case 5: return launch3<K, NB, 5>(p, c, segs, partial);
+        case 6: return launch3<K, NB, 6>(p, c, segs, partial);
+        case 7: return launch3<K, NB, 7>(p, c, segs, partial);
+        default: return launch3<K, NB, 8>(p, c, segs, partial);
     }
 }
 
 template <int K>
-hipError_t launch1(const Problem &p, const DsCfg &c, float *partial) {
-    if (p.batch <= 1) return launch2<K, 1>(p, c, partial);
-    if (p.batch <= 2) return launch2<K, 2>(p, c, partial);
-    return launch2<K, 4>(p, c, partial);
+hipError_t launch1(const Problem &p, const DsCfg &c, const Segs &segs, float *partial) {
+    if (p.batch <= 1) return launch2<K, 1>(p, c, segs, partial);
+    if (p.batch <= 2) return launch2<K, 2>(p, c, segs, partial);
+    return launch2<K, 4>(p, c, segs, partial);
 }
 
 }  // namespace
@@ -302,16 +312,14 @@ size_t ds_workspace_bytes(const Problem &p) {
     return size_t(p.K) * 8 * size_t(p.batch) * size_t(p.out) * sizeof(float);
 }
 
-// p.codebooks holds the packed planes [K][8][65536]; workspace: K*8 x batch x out fp32
+// segs.cb holds the packed planes [K][8][65536]; workspace: K*8 x batch x T fp32
 hipError_t launch_ds(const Problem &p, void *workspace) {
-    const DsCfg c = ds_cfg(p);
+    Segs segs = p.segs;
+    const DsCfg c = ds_cfg(p, &segs);
     float *partial = static_cast<float *>(workspace);
-    hipError_t e = p.K == 1 ? launch1<1>(p, c, partial) : launch1<2>(p, c, partial);
+    hipError_t e = p.K == 1 ? launch1<1>(p, c, segs, partial) : launch1<2>(p, c, segs, partial);
     if (e != hipSuccess) return e;
-    const int n = int(p.batch * p.out);
-    hipLaunchKernelGGL(ds_reduce_kernel, dim3(unsigned((n + 255) / 256)), dim3(256), 0, p.stream,
-                       partial, static_cast<uint16_t *>(p.y), n, p.K * 8);
-    return hipGetLastError();
+    return launch_partial_sum_segs(partial, segs, p.batch, p.K * 8, p.stream);
 }
 
 hipError_t launch_pack_codebooks(const void *cb, void *planes, int K, int B, hipStream_t s) {

@@ -94,13 +94,17 @@ dequantize_kernel(const void *__restrict__ codes, const uint16_t *__restrict__ c
     }
 }
 
-// y[i] = sum over parts (in order) of partial[part][i], rounded to fp16; the
-// loads are issued eight parts at a time.
+// y_m[b][g - row0[m]] = fp16(sum over parts, in order, of partial[part][b][g]) for every
+// global row g < T of matrix m and token b; partial is [parts][batch][T].
+template <int NS>
 __global__ void __launch_bounds__(256)
-partial_sum_kernel(const float *__restrict__ partial, uint16_t *__restrict__ y, int64_t n,
-                   int parts) {
-    const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-    if (i >= n) return;
+partial_sum_segs_kernel(const float *__restrict__ partial, int batch, int parts, const Segs segs) {
+    const int T = seg_total<NS>(segs.n, segs.row0);
+    const int64_t n = int64_t(batch) * T;
+    const int g = blockIdx.x * blockDim.x + threadIdx.x;   // global row; token b = blockIdx.y
+    const int b = blockIdx.y;
+    if (g >= T) return;
+    const int64_t i = int64_t(b) * T + g;
     float s = 0.0f;
     for (int p0 = 0; p0 < parts; p0 += 8) {
         float v[8];
@@ -109,10 +113,45 @@ partial_sum_kernel(const float *__restrict__ partial, uint16_t *__restrict__ y, 
 #pragma unroll
         for (int q = 0; q < 8; ++q) s += v[q];
     }
+    const int m = seg_of<NS>(segs.n, segs.row0, g);
+    const int out_m = pick(segs.row0, m + 1) - pick(segs.row0, m);
+    static_cast<uint16_t *>(pick(segs.y, m))[int64_t(b) * out_m + (g - pick(segs.row0, m))] = f2h_bits(s);
+}
+
+// One matrix: y[i] = fp16(sum over parts, in order, of partial[part][i]), i < n = batch * out.
+__global__ void __launch_bounds__(256)
+partial_sum_kernel(const float *__restrict__ partial, uint16_t *__restrict__ y, int n, int parts) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    float s = 0.0f;
+    for (int p0 = 0; p0 < parts; p0 += 8) {
+        float v[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) v[q] = (p0 + q < parts) ? partial[size_t(p0 + q) * n + i] : 0.0f;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) s += v[q];
+    }
     y[i] = f2h_bits(s);
 }
 
 }  // namespace
+
+hipError_t launch_partial_sum_segs(const float *partial, const Segs &segs, int batch, int parts,
+                                   hipStream_t s) {
+    const int T = segs.row0[segs.n];
+    const dim3 grid(unsigned((T + 255) / 256), unsigned(batch));
+    if (segs.n == 1 && int64_t(batch) * T <= INT32_MAX - 255) {
+        const int n = batch * T;   // [batch][out] is one flat range
+        hipLaunchKernelGGL(partial_sum_kernel, dim3(unsigned((n + 255) / 256)), dim3(256), 0, s,
+                           partial, static_cast<uint16_t *>(segs.y[0]), n, parts);
+    } else if (segs.n == 1)
+        hipLaunchKernelGGL(partial_sum_segs_kernel<1>, grid, dim3(256), 0, s, partial, batch,
+                           parts, segs);
+    else
+        hipLaunchKernelGGL(partial_sum_segs_kernel<kMaxSegs>, grid, dim3(256), 0, s, partial,
+                           batch, parts, segs);
+    return hipGetLastError();
+}
 
 // byte copy, 16 bytes per thread where both pointers allow it
 __global__ void __launch_bounds__(256)
@@ -131,12 +170,6 @@ hipError_t launch_copy_bytes(const void *src, void *dst, int64_t n, hipStream_t 
     const int blocks = int((units + 255) / 256 < 4096 ? (units + 255) / 256 : 4096);
     hipLaunchKernelGGL(copy_bytes_kernel, dim3(blocks > 0 ? blocks : 1), dim3(256), 0, s,
                        static_cast<const uint8_t *>(src), static_cast<uint8_t *>(dst), n);
-    return hipGetLastError();
-}
-
-hipError_t launch_partial_sum(const float *partial, void *y, int64_t n, int parts, hipStream_t s) {
-    hipLaunchKernelGGL(partial_sum_kernel, dim3(unsigned((n + 255) / 256)), dim3(256), 0, s,
-                       partial, static_cast<uint16_t *>(y), n, parts);
     return hipGetLastError();
 }
 

@@ -6,17 +6,33 @@
 
 namespace aqlm {
 
+// Up to kMaxSegs matrices that share x, in, K, B and batch, computed in one launch:
+// matrix m owns global rows [row0[m], row0[m+1]) of the concatenated output.  A single
+// product is a table of one.  aux0 is scratch for launchers: the first work unit
+// (workgroup, row range or tile) of each matrix in the launch's own decomposition.
+constexpr int kMaxSegs = 4;
+struct Segs {
+    int n;
+    int row0[kMaxSegs + 1];
+    int aux0[kMaxSegs + 1];
+    const void *codes[kMaxSegs];
+    const void *cb[kMaxSegs];
+    void *y[kMaxSegs];
+};
+
+
 struct Problem {
-    const void *codes;
+    const void *codes;        // matrix 0 (the only one unless segs.n > 1)
     const void *codebooks;
     const void *x;
     void *y;
-    int64_t out;
+    int64_t out;              // total rows over all matrices
     int64_t in;
     int K;
     int B;
     int batch;
     hipStream_t stream;
+    Segs segs;
 };
 
 // Every launcher returns the hipError_t of its launch (hipSuccess when queued).
@@ -24,8 +40,10 @@ struct Problem {
 // Generic: any K in 1..8, B in {8,16}, any batch, any in % 8 == 0.
 hipError_t launch_generic(const Problem &p);
 
-// y[i] = fp16(sum over parts of partial[part][i]) for i < n (parts summed in order).
-hipError_t launch_partial_sum(const float *partial, void *y, int64_t n, int parts, hipStream_t s);
+// Same over matrices: partial is [parts][batch][T] (T = segs.row0[segs.n]); for global row g of
+// matrix m, y_m[b][g - row0[m]] = fp16(sum over parts, in order).
+hipError_t launch_partial_sum_segs(const float *partial, const Segs &segs, int batch, int parts,
+                                   hipStream_t s);
 hipError_t launch_copy_bytes(const void *src, void *dst, int64_t n, hipStream_t s);
 
 // Dense W (fp32 when w_fp16 == 0, fp16 otherwise).

@@ -22,10 +22,9 @@ namespace {
 
 constexpr int kL2Waves = 4;
 
-template <int K, int NB, bool XLDS>
+template <int K, int NB, bool XLDS, int NS>
 __global__ void __launch_bounds__(kL2Waves * kWave)
-l2_kernel(const uint8_t *__restrict__ codes, const uint4 *__restrict__ cb,
-          const uint16_t *__restrict__ x, uint16_t *__restrict__ y, int out, int in, int batch) {
+l2_kernel(const uint16_t *__restrict__ x, int in, int batch, const Segs segs) {
     constexpr int GPC = 8 / K;                 // groups per 16-byte chunk
     extern __shared__ uint4 xs[];              // [batch][G] when XLDS
     const int G = in / kGroup;
@@ -38,15 +37,19 @@ l2_kernel(const uint8_t *__restrict__ codes, const uint4 *__restrict__ cb,
     }
     const int lane = threadIdx.x & (kWave - 1);
     const int nwaves = gridDim.x * kL2Waves;
+    const int out = seg_total<NS>(segs.n, segs.row0);         // rows over all matrices
     int o = blockIdx.x * kL2Waves + threadIdx.x / kWave;
     if (o >= out) return;
 
     // Branch-free (the chunk index is clamped into the row; clamped lanes are masked
     // where the chunk is used): a conditional load would be waited for at once.
+    // Global row -> its matrix's codes (wave-uniform).
     auto load_chunk = [&](int row, int it) -> u32x4 {
+        const int mi = seg_of<NS>(segs.n, segs.row0, row);
+        const uint8_t *codes = static_cast<const uint8_t *>(pick(segs.codes, mi));
         const int c = min(lane + kWave * it, NC - 1);
-        return __builtin_nontemporal_load(
-            reinterpret_cast<const u32x4 *>(codes + (size_t(row) * NC + c) * 16u));
+        return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(
+            codes + (size_t(row - pick(segs.row0, mi)) * NC + c) * 16u));
     };
 
     int it = 0;
@@ -64,6 +67,8 @@ l2_kernel(const uint8_t *__restrict__ codes, const uint4 *__restrict__ cb,
         const u32x4 nxt = load_chunk(min(o_n, out - 1), it_n);
 
         const int c = lane + kWave * it;
+        const int mi = seg_of<NS>(segs.n, segs.row0, o);
+        const uint4 *__restrict__ cb = static_cast<const uint4 *>(pick(segs.cb, mi));
         if (c < NC) {
             uint4 v[8];
 #pragma unroll
@@ -91,7 +96,11 @@ l2_kernel(const uint8_t *__restrict__ codes, const uint4 *__restrict__ cb,
 #pragma unroll
             for (int b = 0; b < NB; ++b) {
                 const float s = wave_sum(acc[b]);
-                if (lane == 0 && b < batch) y[size_t(b) * out + o] = f2h_bits(s);
+                if (lane == 0 && b < batch) {
+                    const int out_m = pick(segs.row0, mi + 1) - pick(segs.row0, mi);
+                    static_cast<uint16_t *>(pick(segs.y, mi))[size_t(b) * out_m + (o - pick(segs.row0, mi))] =
+                        f2h_bits(s);
+                }
                 acc[b] = 0.0f;
             }
         }
@@ -114,16 +123,21 @@ hipError_t launch_nb(const Problem &p) {
     }
     const int64_t need = (p.out + kL2Waves - 1) / kL2Waves;
     const int grid = int(need < int64_t(256) * per_cu ? need : int64_t(256) * per_cu);
-    const uint8_t *codes = static_cast<const uint8_t *>(p.codes);
-    const uint4 *cb = static_cast<const uint4 *>(p.codebooks);
     const uint16_t *x = static_cast<const uint16_t *>(p.x);
-    uint16_t *y = static_cast<uint16_t *>(p.y);
-    if (xlds)
-        hipLaunchKernelGGL((l2_kernel<K, NB, true>), dim3(grid), dim3(kL2Waves * kWave), xbytes,
-                           p.stream, codes, cb, x, y, int(p.out), int(p.in), p.batch);
+    const dim3 g(grid), b(kL2Waves * kWave);
+    const bool one = p.segs.n == 1;
+    if (xlds && one)
+        hipLaunchKernelGGL((l2_kernel<K, NB, true, 1>), g, b, xbytes, p.stream, x, int(p.in),
+                           p.batch, p.segs);
+    else if (xlds)
+        hipLaunchKernelGGL((l2_kernel<K, NB, true, kMaxSegs>), g, b, xbytes, p.stream, x,
+                           int(p.in), p.batch, p.segs);
+    else if (one)
+        hipLaunchKernelGGL((l2_kernel<K, NB, false, 1>), g, b, 0, p.stream, x, int(p.in),
+                           p.batch, p.segs);
     else
-        hipLaunchKernelGGL((l2_kernel<K, NB, false>), dim3(grid), dim3(kL2Waves * kWave), 0,
-                           p.stream, codes, cb, x, y, int(p.out), int(p.in), p.batch);
+        hipLaunchKernelGGL((l2_kernel<K, NB, false, kMaxSegs>), g, b, 0, p.stream, x,
+                           int(p.in), p.batch, p.segs);
     return hipGetLastError();
 }
 

@@ -94,16 +94,25 @@ __device__ __forceinline__ void store_tables(char *lut, const half4 &a, const ha
     }
 }
 
+// Row blocks of each matrix are numbered consecutively (segs.aux0); a workgroup works
+// on one matrix, whose rows it indexes locally; partial sums go to global row
+// segs.row0[m] + local row of a [slice][T] workspace.
+template <int NS>
 __global__ void __launch_bounds__(kLutWaves * kWave)
-lut_kernel(const uint16_t *__restrict__ codes, const uint16_t *__restrict__ cb,
-           const uint16_t *__restrict__ x, float *__restrict__ partial, int out, int G,
-           int rows_per_block, int nslices) {
+lut_kernel(const uint16_t *__restrict__ x, float *__restrict__ partial, int G,
+           int rows_per_block, int nslices, const Segs segs) {
     __shared__ __attribute__((aligned(16))) char lut[kLutBytes];
 
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
     const int slice = blockIdx.x % nslices;
-    const int rblock = blockIdx.x / nslices;
+    const int rb = blockIdx.x / nslices;
+    const int mi = seg_of<NS>(segs.n, segs.aux0, rb);
+    const int rblock = rb - pick(segs.aux0, mi);
+    const int out = pick(segs.row0, mi + 1) - pick(segs.row0, mi);
+    const uint16_t *__restrict__ codes = static_cast<const uint16_t *>(pick(segs.codes, mi));
+    const uint16_t *__restrict__ cb = static_cast<const uint16_t *>(pick(segs.cb, mi));
+    float *__restrict__ part = partial + size_t(slice) * seg_total<NS>(segs.n, segs.row0) + pick(segs.row0, mi);
     const int j0 = slice * kSlice;
     const int jl = lane;
     const int r_begin = rblock * rows_per_block;
@@ -146,7 +155,7 @@ lut_kernel(const uint16_t *__restrict__ codes, const uint16_t *__restrict__ cb,
         }
         const float s = transpose_reduce<kReduceRows>(v, lane);
         const int r = h * kReduceRows + (lane >> 2);
-        if ((lane & 3) == 0 && r < w_rows) partial[size_t(slice) * out + w_begin + r] = s;
+        if ((lane & 3) == 0 && r < w_rows) part[w_begin + r] = s;
     }
 }
 
@@ -157,16 +166,22 @@ lut_kernel(const uint16_t *__restrict__ codes, const uint16_t *__restrict__ cb,
 // takes the range's octets w, w + 16, w + 32, w + 48.
 constexpr int kOctetsPerWave = kRowsPerWave / 8;
 
+template <int NS>
 __global__ void __launch_bounds__(kLutWaves * kWave)
-lut_packed_kernel(const u32x4 *__restrict__ pcodes, const uint16_t *__restrict__ planes,
-                  const uint16_t *__restrict__ x, float *__restrict__ partial, int out, int G,
-                  int rows_per_block, int nslices) {
+lut_packed_kernel(const uint16_t *__restrict__ x, float *__restrict__ partial,
+                  int G, int rows_per_block, int nslices, const Segs segs) {
     __shared__ __attribute__((aligned(16))) char lut[kLutBytes];
 
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int slice = blockIdx.x % nslices;
-    const int rblock = blockIdx.x / nslices;
+    const int rb = blockIdx.x / nslices;
+    const int mi = seg_of<NS>(segs.n, segs.aux0, rb);
+    const int rblock = rb - pick(segs.aux0, mi);
+    const int out = pick(segs.row0, mi + 1) - pick(segs.row0, mi);
+    const u32x4 *__restrict__ pcodes = static_cast<const u32x4 *>(pick(segs.codes, mi));
+    const uint16_t *__restrict__ planes = static_cast<const uint16_t *>(pick(segs.cb, mi));
+    float *__restrict__ part = partial + size_t(slice) * seg_total<NS>(segs.n, segs.row0) + pick(segs.row0, mi);
     const int j0 = slice * kSlice;
     const int NQ = (out + 7) / 8;
     const int r_begin = rblock * rows_per_block;             // a multiple of 8
@@ -204,7 +219,7 @@ lut_packed_kernel(const u32x4 *__restrict__ pcodes, const uint16_t *__restrict__
         const int vi = lane >> 2;                            // value index: octet i + vi/8, row vi%8
         const int q = wave + kLutWaves * (i + (vi >> 3));
         const int row = r_begin + 8 * q + (vi & 7);
-        if ((lane & 3) == 0 && q < nq && row < r_end) partial[size_t(slice) * out + row] = sum;
+        if ((lane & 3) == 0 && q < nq && row < r_end) part[row] = sum;
     }
 }
 
@@ -241,35 +256,17 @@ unpack_codes_kernel(const uint16_t *__restrict__ packed, uint16_t *__restrict__ 
     }
 }
 
-// y[row] = sum over slices (in slice order) of the partial sums, rounded to fp16.
-// Loads are issued eight at a time so that a row waits for memory ceil(n/8) times.
-__global__ void __launch_bounds__(256)
-lut_reduce_kernel(const float *__restrict__ partial, uint16_t *__restrict__ y, int out,
-                  int nslices) {
-    const int row = blockIdx.x * blockDim.x + threadIdx.x;
-    if (row >= out) return;
-    float s = 0.0f;
-    for (int s0 = 0; s0 < nslices; s0 += 8) {
-        float t[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-            t[i] = (s0 + i < nslices) ? partial[size_t(s0 + i) * out + row] : 0.0f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) s += t[i];
-    }
-    y[row] = f2h_bits(s);
-}
-
 struct LutCfg {
     int nslices, nrblocks, rows_per_block;
 };
 
-LutCfg lut_cfg(const Problem &p, bool packed) {
+// Row blocks of at most kLutWaves * kRowsPerWave rows (a wave's rows are all loaded at
+// once), about 256 / nslices of them over all matrices (one workgroup per CU); each
+// matrix gets whole blocks of its own (segs.aux0 is filled here).
+LutCfg lut_cfg(const Problem &p, bool packed, Segs *segs = nullptr) {
     LutCfg c{};
     const int64_t G = p.in / kGroup;
     c.nslices = int((G + kSlice - 1) / kSlice);
-    // one workgroup per CU: about 256 / nslices row ranges, each at most
-    // kLutWaves * kRowsPerWave rows (a wave's rows are all loaded at once)
     const int64_t max_rows = int64_t(kLutWaves) * kRowsPerWave;
     int64_t nrb = c.nslices >= 256 ? 1 : 256 / c.nslices;
     const int64_t need = (p.out + max_rows - 1) / max_rows;
@@ -278,8 +275,15 @@ LutCfg lut_cfg(const Problem &p, bool packed) {
     if (packed) rpb = (rpb + 7) / 8 * 8;                      // ranges start on an octet
     else rpb = (rpb + kLutWaves - 1) / kLutWaves * kLutWaves; // whole rows per wave
     if (rpb < kLutWaves) rpb = kLutWaves;
+    if (rpb > max_rows) rpb = max_rows;
     c.rows_per_block = int(rpb);
-    c.nrblocks = int((p.out + rpb - 1) / rpb);
+    int64_t total = 0;
+    for (int m = 0; m < p.segs.n; ++m) {
+        if (segs) segs->aux0[m] = int(total);
+        total += (p.segs.row0[m + 1] - p.segs.row0[m] + rpb - 1) / rpb;
+    }
+    if (segs) segs->aux0[p.segs.n] = int(total);
+    c.nrblocks = int(total);
     return c;
 }
 
@@ -299,21 +303,23 @@ size_t lut_workspace_bytes(const Problem &p) {
     return size_t(c.nslices) * size_t(p.out) * sizeof(float);
 }
 
-// workspace: partial sums, nslices x out fp32 (no initial contents needed)
+// workspace: partial sums, nslices x T fp32 (no initial contents needed)
 hipError_t launch_lut(const Problem &p, void *workspace) {
-    const LutCfg c = lut_cfg(p, false);
+    Segs segs = p.segs;
+    const LutCfg c = lut_cfg(p, false, &segs);
     float *partial = static_cast<float *>(workspace);
-    const int grid = c.nslices * c.nrblocks;
-    hipLaunchKernelGGL(lut_kernel, dim3(grid), dim3(kLutWaves * kWave), 0, p.stream,
-                       static_cast<const uint16_t *>(p.codes),
-                       static_cast<const uint16_t *>(p.codebooks),
-                       static_cast<const uint16_t *>(p.x), partial, int(p.out),
-                       int(p.in / kGroup), c.rows_per_block, c.nslices);
+    if (segs.n == 1)
+        hipLaunchKernelGGL(lut_kernel<1>, dim3(c.nslices * c.nrblocks), dim3(kLutWaves * kWave), 0,
+                           p.stream, static_cast<const uint16_t *>(p.x), partial,
+                           int(p.in / kGroup), c.rows_per_block, c.nslices, segs);
+    else
+        hipLaunchKernelGGL(lut_kernel<kMaxSegs>, dim3(c.nslices * c.nrblocks),
+                           dim3(kLutWaves * kWave), 0, p.stream,
+                           static_cast<const uint16_t *>(p.x), partial, int(p.in / kGroup),
+                           c.rows_per_block, c.nslices, segs);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(lut_reduce_kernel, dim3(unsigned((p.out + 255) / 256)), dim3(256), 0,
-                       p.stream, partial, static_cast<uint16_t *>(p.y), int(p.out), c.nslices);
-    return hipGetLastError();
+    return launch_partial_sum_segs(partial, segs, 1, c.nslices, p.stream);
 }
 
 int64_t lut_packed_codes_bytes(int64_t out, int64_t in) {
@@ -335,20 +341,24 @@ size_t lut_packed_workspace_bytes(const Problem &p) {
     return size_t(c.nslices) * size_t(p.out) * sizeof(float);
 }
 
-// p.codes: packed tiles; p.codebooks: plane-major; workspace: nslices x out fp32
+// segs.codes: packed tiles; segs.cb: plane-major; workspace: nslices x T fp32
 hipError_t launch_lut_packed(const Problem &p, void *workspace) {
-    const LutCfg c = lut_cfg(p, true);
+    Segs segs = p.segs;
+    const LutCfg c = lut_cfg(p, true, &segs);
     float *partial = static_cast<float *>(workspace);
-    hipLaunchKernelGGL(lut_packed_kernel, dim3(c.nslices * c.nrblocks), dim3(kLutWaves * kWave), 0,
-                       p.stream, static_cast<const u32x4 *>(p.codes),
-                       static_cast<const uint16_t *>(p.codebooks),
-                       static_cast<const uint16_t *>(p.x), partial, int(p.out),
-                       int(p.in / kGroup), c.rows_per_block, c.nslices);
+    if (segs.n == 1)
+        hipLaunchKernelGGL(lut_packed_kernel<1>, dim3(c.nslices * c.nrblocks),
+                           dim3(kLutWaves * kWave), 0, p.stream,
+                           static_cast<const uint16_t *>(p.x), partial, int(p.in / kGroup),
+                           c.rows_per_block, c.nslices, segs);
+    else
+        hipLaunchKernelGGL(lut_packed_kernel<kMaxSegs>, dim3(c.nslices * c.nrblocks),
+                           dim3(kLutWaves * kWave), 0, p.stream,
+                           static_cast<const uint16_t *>(p.x), partial, int(p.in / kGroup),
+                           c.rows_per_block, c.nslices, segs);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(lut_reduce_kernel, dim3(unsigned((p.out + 255) / 256)), dim3(256), 0,
-                       p.stream, partial, static_cast<uint16_t *>(p.y), int(p.out), c.nslices);
-    return hipGetLastError();
+    return launch_partial_sum_segs(partial, segs, 1, c.nslices, p.stream);
 }
 
 // pack: src = codes [out][G] 16-bit words, dst = tiles; unpack: the reverse

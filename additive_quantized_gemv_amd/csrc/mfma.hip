@@ -92,11 +92,10 @@ template <int MS, int NT> struct Tile {
     static constexpr int XLOADS = BN * CHG / (kMfmaWaves * kWave);   // 16-B loads per thread
 };
 
-template <int K, int BITS, int MS, int NT>
+template <int K, int BITS, int MS, int NT, int NS>
 __global__ void __launch_bounds__(kMfmaWaves * kWave)
-mfma_kernel(const uint8_t *__restrict__ codes, const uint16_t *__restrict__ cb,
-            const uint16_t *__restrict__ x, uint16_t *__restrict__ y, float *__restrict__ partial,
-            int out, int in, int batch, int groups_per_split) {
+mfma_kernel(const uint16_t *__restrict__ x, float *__restrict__ partial, int in,
+            int batch, int groups_per_split, const Segs segs) {
     typedef Tile<MS, NT> T;
     typedef typename Acc<MS>::type acc_t;
     typedef typename CodeBlock<K, BITS>::type cblock_t;
@@ -109,7 +108,14 @@ mfma_kernel(const uint8_t *__restrict__ codes, const uint16_t *__restrict__ cb,
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int G = in / kGroup;
-    const int row0 = blockIdx.x * (kMfmaWaves * MS) + wave * MS;
+    // row tiles of each matrix are numbered consecutively (segs.aux0)
+    const int mi = seg_of<NS>(segs.n, segs.aux0, blockIdx.x);
+    const int out = pick(segs.row0, mi + 1) - pick(segs.row0, mi);
+    const int rows_all = seg_total<NS>(segs.n, segs.row0);
+    const uint8_t *__restrict__ codes = static_cast<const uint8_t *>(pick(segs.codes, mi));
+    const uint16_t *__restrict__ cb = static_cast<const uint16_t *>(pick(segs.cb, mi));
+    uint16_t *__restrict__ y = static_cast<uint16_t *>(pick(segs.y, mi));
+    const int row0 = (blockIdx.x - pick(segs.aux0, mi)) * (kMfmaWaves * MS) + wave * MS;
     const int tok0 = blockIdx.y * T::BN;
     const int split = blockIdx.z;
     const int g_begin = split * groups_per_split;
@@ -233,7 +239,7 @@ mfma_kernel(const uint8_t *__restrict__ codes, const uint16_t *__restrict__ cb,
             const int n = tok0 + t * MS + (lane % MS);
             if (row < out && n < batch) {
                 if (partial)
-                    partial[(size_t(split) * batch + n) * out + row] = acc[t][r];
+                    partial[(size_t(split) * batch + n) * rows_all + pick(segs.row0, mi) + row] = acc[t][r];
                 else
                     y[size_t(n) * out + row] = f2h_bits(acc[t][r]);
             }
@@ -245,7 +251,7 @@ struct MfmaCfg {
     int ms, nt, ksplit, groups_per_split, grid_x, grid_y;
 };
 
-MfmaCfg mfma_cfg(const Problem &p) {
+MfmaCfg mfma_cfg(const Problem &p, Segs *segs = nullptr) {
     MfmaCfg c{};
     if (p.batch <= 16) { c.ms = 16; c.nt = 1; }
     else if (p.batch <= 32) { c.ms = 32; c.nt = 1; }
@@ -253,7 +259,14 @@ MfmaCfg mfma_cfg(const Problem &p) {
     else { c.ms = 32; c.nt = 4; }
     const int64_t G = p.in / kGroup;
     const int chg = c.ms == 16 ? 32 : 16;
-    c.grid_x = int((p.out + kMfmaWaves * c.ms - 1) / (kMfmaWaves * c.ms));
+    const int rows_per_tile = kMfmaWaves * c.ms;
+    int gx = 0;                                      // row tiles, whole ones per matrix
+    for (int m = 0; m < p.segs.n; ++m) {
+        if (segs) segs->aux0[m] = gx;
+        gx += (p.segs.row0[m + 1] - p.segs.row0[m] + rows_per_tile - 1) / rows_per_tile;
+    }
+    if (segs) segs->aux0[p.segs.n] = gx;
+    c.grid_x = gx;
     c.grid_y = (p.batch + c.ms * c.nt - 1) / (c.ms * c.nt);
     const int64_t tiles = int64_t(c.grid_x) * c.grid_y;
     const int64_t nchunks = (G + chg - 1) / chg;
@@ -271,22 +284,24 @@ MfmaCfg mfma_cfg(const Problem &p) {
 }
 
 template <int K, int BITS, int MS, int NT>
-hipError_t launch_t(const Problem &p, const MfmaCfg &c, float *partial) {
-    hipLaunchKernelGGL((mfma_kernel<K, BITS, MS, NT>), dim3(c.grid_x, c.grid_y, c.ksplit),
-                       dim3(kMfmaWaves * kWave), 0, p.stream,
-                       static_cast<const uint8_t *>(p.codes),
-                       static_cast<const uint16_t *>(p.codebooks),
-                       static_cast<const uint16_t *>(p.x), static_cast<uint16_t *>(p.y), partial,
-                       int(p.out), int(p.in), p.batch, c.groups_per_split);
+hipError_t launch_t(const Problem &p, const MfmaCfg &c, const Segs &segs, float *partial) {
+    const dim3 g(c.grid_x, c.grid_y, c.ksplit), b(kMfmaWaves * kWave);
+    const uint16_t *x = static_cast<const uint16_t *>(p.x);
+    if (segs.n == 1)
+        hipLaunchKernelGGL((mfma_kernel<K, BITS, MS, NT, 1>), g, b, 0, p.stream, x, partial,
+                           int(p.in), p.batch, c.groups_per_split, segs);
+    else
+        hipLaunchKernelGGL((mfma_kernel<K, BITS, MS, NT, kMaxSegs>), g, b, 0, p.stream, x,
+                           partial, int(p.in), p.batch, c.groups_per_split, segs);
     return hipGetLastError();
 }
 
 template <int K, int BITS>
-hipError_t launch_kb(const Problem &p, const MfmaCfg &c, float *partial) {
-    if (c.ms == 16) return launch_t<K, BITS, 16, 1>(p, c, partial);
-    if (c.nt == 1) return launch_t<K, BITS, 32, 1>(p, c, partial);
-    if (c.nt == 2) return launch_t<K, BITS, 32, 2>(p, c, partial);
-    return launch_t<K, BITS, 32, 4>(p, c, partial);
+hipError_t launch_kb(const Problem &p, const MfmaCfg &c, const Segs &segs, float *partial) {
+    if (c.ms == 16) return launch_t<K, BITS, 16, 1>(p, c, segs, partial);
+    if (c.nt == 1) return launch_t<K, BITS, 32, 1>(p, c, segs, partial);
+    if (c.nt == 2) return launch_t<K, BITS, 32, 2>(p, c, segs, partial);
+    return launch_t<K, BITS, 32, 4>(p, c, segs, partial);
 }
 
 
@@ -324,15 +339,17 @@ __device__ __forceinline__ uint32_t seg_code(const uint32_t (&w)[NW], int n) {
 // the next tile's codes loaded while the current one is multiplied.  A wave owns
 // units wave, wave + 16, ... (at most MAXU); with a single unit its activations
 // are loaded once and kept in registers for every tile.
-template <int K, int BITS, int NT, int MAXU>
+template <int K, int BITS, int NT, int MAXU, int NSEGS>
 __global__ void __launch_bounds__(kKw * kWave)
 mfma_kw_kernel(const uint8_t *__restrict__ codes, const uint16_t *__restrict__ cb,
                const uint16_t *__restrict__ x, uint16_t *__restrict__ y, int out, int in,
-               int batch, int ntiles) {
+               int batch, int ntiles, const Segs segs) {
+    // codes / cb / y / out describe the one matrix when NSEGS == 1; with NSEGS > 1 the
+    // matrices come from segs (tiles of each matrix numbered consecutively, segs.aux0)
     constexpr int CBE = BITS == 8 ? K * 256 : 0;
     constexpr int NW = Seg<K, BITS>::NW;
     constexpr int CB = K * BITS / 8;                 // code bytes per group
-    __shared__ uint4 cbs[CBE > 0 ? CBE : 1];
+    __shared__ uint4 cbs[CBE > 0 ? NSEGS * CBE : 1];
     __shared__ float red[2][kKw][NT * 4][kWave];     // double-buffered: one barrier per tile
 
     const int lane = threadIdx.x & (kWave - 1);
@@ -347,9 +364,20 @@ mfma_kw_kernel(const uint8_t *__restrict__ codes, const uint16_t *__restrict__ c
     // and B alike.  Units past the last one are clamped for loading and masked in use.
     auto seg_start = [&](int u) { return min(u * 32 + 8 * kb, G - 8); };
     auto unit_of = [&](int i) { return wave + kKw * i; };
+    // this lane's code row in global tile `tile` (rows past the matrix end: computed,
+    // not stored)
+    auto code_row = [&](int tile) -> const uint8_t * {
+        if constexpr (NSEGS == 1) {
+            return codes + size_t(min(tile * 16 + m, out - 1)) * size_t(G) * CB;
+        } else {
+            const int mi = range_of(segs.n, segs.aux0, tile);
+            const int out_m = segs.row0[mi + 1] - segs.row0[mi];
+            const int o = min((tile - segs.aux0[mi]) * 16 + m, out_m - 1);
+            return static_cast<const uint8_t *>(segs.codes[mi]) + size_t(o) * size_t(G) * CB;
+        }
+    };
     auto load_codes = [&](int tile, uint32_t (&cw)[MAXU][NW]) {
-        const int o = min(tile * 16 + m, out - 1);   // rows past the end: computed, not stored
-        const uint8_t *crow = codes + size_t(o) * size_t(G) * CB;
+        const uint8_t *crow = code_row(tile);
 #pragma unroll
         for (int i = 0; i < MAXU; ++i)
             load_seg<K, BITS>(crow + size_t(seg_start(min(unit_of(i), U - 1))) * CB, cw[i]);
@@ -371,10 +399,17 @@ mfma_kw_kernel(const uint8_t *__restrict__ codes, const uint16_t *__restrict__ c
     };
 
     // Every first load is issued before anything waits: the codebooks (one 16-byte
-    // vector per thread: K*256 <= 1024 threads), the first tile's codes and, with one
-    // unit per wave, the activations; the staging store then waits for the codebooks.
-    uint4 cbv{};
-    if constexpr (CBE > 0) cbv = cbg[min(int(threadIdx.x), CBE - 1)];
+    // vector per thread and matrix: K*256 <= 1024 threads), the first tile's codes and,
+    // with one unit per wave, the activations; the staging store then waits for the
+    // codebooks.
+    uint4 cbv[NSEGS];
+    if constexpr (CBE > 0) {
+#pragma unroll
+        for (int q = 0; q < NSEGS; ++q) {
+            const uint4 *src = NSEGS == 1 ? cbg : static_cast<const uint4 *>(segs.cb[min(q, segs.n - 1)]);
+            cbv[q] = src[min(int(threadIdx.x), CBE - 1)];
+        }
+    }
     int tile = blockIdx.x;
     uint32_t cw[MAXU][NW];
     load_codes(tile, cw);
@@ -383,7 +418,8 @@ mfma_kw_kernel(const uint8_t *__restrict__ codes, const uint16_t *__restrict__ c
     if constexpr (CBE > 0) {
         // unconditional (threads past the end rewrite the last vector with its own
         // value), so the codebook load is not sunk behind the others
-        cbs[min(int(threadIdx.x), CBE - 1)] = cbv;
+#pragma unroll
+        for (int q = 0; q < NSEGS; ++q) cbs[q * CBE + min(int(threadIdx.x), CBE - 1)] = cbv[q];
         __syncthreads();
     }
 
@@ -395,7 +431,12 @@ mfma_kw_kernel(const uint8_t *__restrict__ codes, const uint16_t *__restrict__ c
         // branch-free form measured faster).
         const bool has_next = tile + int(gridDim.x) < ntiles;     // workgroup-uniform
         const int next = has_next ? tile + int(gridDim.x) : tile;
-        const uint8_t *nrow = codes + size_t(min(next * 16 + m, out - 1)) * size_t(G) * CB;
+        const uint8_t *nrow = code_row(next);
+        // this tile's matrix: codebooks, output
+        const int mi = NSEGS == 1 ? 0 : range_of(segs.n, segs.aux0, tile);
+        const uint4 *cbm;
+        if constexpr (NSEGS == 1) cbm = BITS == 8 ? cbs : cbg;
+        else cbm = BITS == 8 ? cbs + mi * CBE : static_cast<const uint4 *>(segs.cb[mi]);
         float4v acc[NT];
 #pragma unroll
         for (int t = 0; t < NT; ++t) acc[t] = float4v{};
@@ -409,11 +450,10 @@ mfma_kw_kernel(const uint8_t *__restrict__ codes, const uint16_t *__restrict__ c
 #pragma unroll
             for (int s = 0; s < 8; ++s) {
                 const uint32_t c0 = seg_code<BITS, NW>(cw[i], s * K);
-                half8 f = __builtin_bit_cast(half8, BITS == 8 ? cbs[c0] : cbg[c0]);
+                half8 f = __builtin_bit_cast(half8, cbm[c0]);
                 if constexpr (K == 2) {
                     const uint32_t c1 = seg_code<BITS, NW>(cw[i], s * K + 1);
-                    f = f + __builtin_bit_cast(half8, BITS == 8 ? cbs[256 + c1]
-                                                                : cbg[(1u << 16) + c1]);
+                    f = f + __builtin_bit_cast(half8, cbm[(1u << BITS) + c1]);
                 }
                 a[s] = ok ? f : half8{};
             }
@@ -432,7 +472,13 @@ mfma_kw_kernel(const uint8_t *__restrict__ codes, const uint16_t *__restrict__ c
 #pragma unroll
             for (int r = 0; r < 4; ++r) red[buf][wave][t * 4 + r][lane] = acc[t][r];
         __syncthreads();
-        const int row0 = tile * 16;
+        int out_m = out, row0 = tile * 16;
+        uint16_t *ym = y;
+        if constexpr (NSEGS > 1) {
+            out_m = segs.row0[mi + 1] - segs.row0[mi];
+            row0 = (tile - segs.aux0[mi]) * 16;
+            ym = static_cast<uint16_t *>(segs.y[mi]);
+        }
         for (int e = threadIdx.x; e < NT * 4 * kWave; e += blockDim.x) {
             const int tr = e / kWave, l = e % kWave;
             float sum = 0.0f;
@@ -441,7 +487,7 @@ mfma_kw_kernel(const uint8_t *__restrict__ codes, const uint16_t *__restrict__ c
             const int t = tr >> 2, r = tr & 3;
             const int row = row0 + 4 * (l >> 4) + r; // 16x16 result layout
             const int tok = t * 16 + (l & 15);
-            if (row < out && tok < batch) y[size_t(tok) * out + row] = f2h_bits(sum);
+            if (row < out_m && tok < batch) ym[size_t(tok) * out_m + row] = f2h_bits(sum);
         }
         buf ^= 1;
         tile += gridDim.x;
@@ -451,7 +497,8 @@ mfma_kw_kernel(const uint8_t *__restrict__ codes, const uint16_t *__restrict__ c
 // units per wave that fit the 128 registers of a 16-wave workgroup without spilling
 template <int K, int BITS>
 constexpr int kw_max_units(int nt) {
-    return nt > 1 ? 1 : (K * BITS > 16 ? 1 : 3);
+    if (K * BITS > 16) return nt > 1 ? 0 : 1;        // 32-bit code words: one unit, one token tile
+    return nt > 1 ? 1 : 3;
 }
 
 template <int K, int BITS>
@@ -459,17 +506,29 @@ hipError_t launch_kw(const Problem &p) {
     const int G = int(p.in / kGroup);
     const int U = (G + 31) / 32;
     const int maxu = (U + kKw - 1) / kKw;
-    const int ntiles = int((p.out + 15) / 16);
+    Segs segs = p.segs;
+    int ntiles = 0;
+    for (int m = 0; m < segs.n; ++m) {
+        segs.aux0[m] = ntiles;
+        ntiles += (segs.row0[m + 1] - segs.row0[m] + 15) / 16;
+    }
+    segs.aux0[segs.n] = ntiles;
     const dim3 g(ntiles < 256 ? ntiles : 256), b(kKw * kWave);   // one workgroup per CU
     const uint8_t *codes = static_cast<const uint8_t *>(p.codes);
     const uint16_t *cb = static_cast<const uint16_t *>(p.codebooks);
     const uint16_t *x = static_cast<const uint16_t *>(p.x);
     uint16_t *y = static_cast<uint16_t *>(p.y);
-#define AQLM_KW(NT, MU)                                                                       \
-    hipLaunchKernelGGL((mfma_kw_kernel<K, BITS, NT, MU>), g, b, 0, p.stream, codes, cb, x, y, \
-                       int(p.out), int(p.in), p.batch, ntiles)
+#define AQLM_KW(NT, MU)                                                                        \
+    do {                                                                                       \
+        if (segs.n == 1)                                                                       \
+            hipLaunchKernelGGL((mfma_kw_kernel<K, BITS, NT, MU, 1>), g, b, 0, p.stream, codes, \
+                               cb, x, y, int(p.out), int(p.in), p.batch, ntiles, segs);        \
+        else                                                                                   \
+            hipLaunchKernelGGL((mfma_kw_kernel<K, BITS, NT, MU, kMaxSegs>), g, b, 0, p.stream, \
+                               codes, cb, x, y, int(p.out), int(p.in), p.batch, ntiles, segs); \
+    } while (0)
     if (p.batch > 16) {
-        AQLM_KW(2, 1);
+        if constexpr (kw_max_units<K, BITS>(2) >= 1) AQLM_KW(2, 1);
     } else if (maxu <= 1) {
         AQLM_KW(1, 1);
     } else if constexpr (kw_max_units<K, BITS>(1) >= 3) {
@@ -511,19 +570,22 @@ size_t mfma_workspace_bytes(const Problem &p) {
     return c.ksplit > 1 ? size_t(c.ksplit) * size_t(p.batch) * size_t(p.out) * sizeof(float) : 0;
 }
 
-// workspace: KSPLIT x batch x out fp32 partial tiles (unused when KSPLIT = 1)
+// workspace: KSPLIT x batch x T fp32 partial tiles (unused when KSPLIT = 1)
 hipError_t launch_mfma(const Problem &p, void *workspace) {
     if (kw_fits(p)) {
         if (p.B == 8) return p.K == 1 ? launch_kw<1, 8>(p) : launch_kw<2, 8>(p);
         return p.K == 1 ? launch_kw<1, 16>(p) : launch_kw<2, 16>(p);
     }
-    const MfmaCfg c = mfma_cfg(p);
+    Segs segs = p.segs;
+    const MfmaCfg c = mfma_cfg(p, &segs);
     float *partial = c.ksplit > 1 ? static_cast<float *>(workspace) : nullptr;
     hipError_t e;
-    if (p.B == 8) e = p.K == 1 ? launch_kb<1, 8>(p, c, partial) : launch_kb<2, 8>(p, c, partial);
-    else e = p.K == 1 ? launch_kb<1, 16>(p, c, partial) : launch_kb<2, 16>(p, c, partial);
+    if (p.B == 8)
+        e = p.K == 1 ? launch_kb<1, 8>(p, c, segs, partial) : launch_kb<2, 8>(p, c, segs, partial);
+    else
+        e = p.K == 1 ? launch_kb<1, 16>(p, c, segs, partial) : launch_kb<2, 16>(p, c, segs, partial);
     if (e != hipSuccess || c.ksplit == 1) return e;
-    return launch_partial_sum(partial, p.y, p.batch * p.out, c.ksplit, p.stream);
+    return launch_partial_sum_segs(partial, segs, p.batch, c.ksplit, p.stream);
 }
 
 }  // namespace aqlm

@@ -173,6 +173,30 @@ aqlm_status_t aqlm_gemv_packed(const void *packed_codes, const void *packed_code
                                const void *x, void *y, int64_t out_features, int64_t in_features,
                                int K, int B, int batch, void *stream);
 
+/*
+ * Several products that read the same activations, in one launch: the linears of a
+ * layer that share x (q, k, v; gate, up).  y_m = W_m x for m < n, 1 <= n <= 4, where
+ * W_m has out_features[m] rows, codes codes[m] and codebooks codebooks[m]; in_features,
+ * K, B and batch are common.  codes, codebooks, y and out_features are host arrays of n
+ * entries (read during the call only); each y[m] is [batch][out_features[m]] fp16.
+ * Each matrix follows the argument rules of aqlm_gemv; no y[m] may overlap x, any codes,
+ * any codebooks or another y; the out_features must add up to at most 2^30.  The result
+ * equals n separate calls; launches (and their fixed start-up time) are shared.
+ * aqlm_gemv_grouped chooses kernels as aqlm_gemv does, aqlm_gemm_grouped as aqlm_gemm,
+ * aqlm_gemv_packed_grouped as aqlm_gemv_packed (packed codes and codebooks).
+ */
+aqlm_status_t aqlm_gemv_grouped(int n, const void *const *codes, const void *const *codebooks,
+                                const void *x, void *const *y, const int64_t *out_features,
+                                int64_t in_features, int K, int B, int batch, void *stream);
+aqlm_status_t aqlm_gemm_grouped(int n, const void *const *codes, const void *const *codebooks,
+                                const void *x, void *const *y, const int64_t *out_features,
+                                int64_t in_features, int K, int B, int batch, void *stream);
+aqlm_status_t aqlm_gemv_packed_grouped(int n, const void *const *packed_codes,
+                                       const void *const *packed_codebooks, const void *x,
+                                       void *const *y, const int64_t *out_features,
+                                       int64_t in_features, int K, int B, int batch,
+                                       void *stream);
+
 /* K*B/group bits per weight (bitrate formula of the decode section). */
 double aqlm_bits_per_weight(int K, int B, int group);
 

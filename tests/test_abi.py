@@ -135,6 +135,36 @@ def test_pack_codes_invalid(lib):
     assert lib.aqlm_gemv_packed(C, CB, X, C + 512, 9, 64, 2, 8, 1, None) == 1
 
 
+def _grouped_args(n, outs, ys, codes=None):
+    vp, k = ctypes.c_void_p, max(n, 4)
+    codes = codes or [C + 0x100000 * i for i in range(k)]
+    return (n, (vp * k)(*codes), (vp * k)(*[CB + 0x100000 * i for i in range(k)]), X,
+            (vp * k)(*(ys + [Y + 0x800000] * (k - len(ys)))),
+            (ctypes.c_int64 * k)(*(outs + [16] * (k - len(outs)))))
+
+
+@pytest.mark.parametrize("fn", ["aqlm_gemv_grouped", "aqlm_gemm_grouped", "aqlm_gemv_packed_grouped"])
+def test_grouped_invalid(lib, fn):
+    f = getattr(lib, fn)
+    f.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                  ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                  ctypes.c_void_p]
+    ys = [Y, Y + 0x100000, Y + 0x200000, Y + 0x300000]
+    def call(n, outs, ys_, in_=64, K=2, B=8, batch=1, codes=None):
+        a = _grouped_args(n, outs, ys_, codes)
+        return f(a[0], ctypes.cast(a[1], ctypes.c_void_p), ctypes.cast(a[2], ctypes.c_void_p), a[3],
+                 ctypes.cast(a[4], ctypes.c_void_p), ctypes.cast(a[5], ctypes.c_void_p), in_, K, B,
+                 batch, None)
+    assert call(0, [16] * 4, ys) == 1                       # no matrices
+    assert call(5, [16] * 4, ys) == 1                       # more than 4
+    assert call(2, [16, 0, 0, 0], ys) == 1                  # empty matrix
+    assert call(2, [16, 16, 0, 0], ys, in_=60) == 1         # in % 8
+    assert call(2, [16, 16, 0, 0], [Y, Y + 16, 0, 0]) == 1  # y_0 overlaps y_1
+    assert call(2, [16, 16, 0, 0], [Y, C + 8, 0, 0]) == 1   # y_1 overlaps codes_0
+    assert call(2, [16, 16, 0, 0], [Y, X, 0, 0]) == 1       # y_1 overlaps x
+    assert call(2, [1 << 29, 1 << 29 + 1, 0, 0], ys, in_=8) == 1   # more than 2^30 rows
+
+
 def test_variant_choice_host_logic(lib):
     # pointers aligned to 256 B, shapes of the benchmark configurations
     def sel(gemm, out, in_, K, B, batch):

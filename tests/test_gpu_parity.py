@@ -413,3 +413,123 @@ def test_packed_graph_replay(aq, orc, KB):
             torch.cuda.synchronize()
             assert bool((y == eager).all())
     check_y(eager, orc.gemv(p["codes"], p["codebooks"], p["x"], K, B), "packed eager")
+
+
+# ------------------------------------------------------------ grouped calls (shared x)
+
+def _group(outs, in_, K, B, batch, cfg):
+    """Matrices that share one x: problems with their own codes/codebooks, x from the first."""
+    ps = [synth.make_problem(o, in_, K, B, batch=batch, sigma_cb=0.02, config=cfg + i)
+          for i, o in enumerate(outs)]
+    for p in ps[1:]:
+        p["x"] = ps[0]["x"]
+    return ps
+
+
+GROUPED = [
+    # outs, in, K, B, batch
+    ((100, 257, 64), 512, 2, 8, 1),          # lookup tables, ragged matrices
+    ((65, 33), 520, 2, 8, 1),                # partial 64-group slice
+    ((300, 17, 1), 1024, 1, 16, 1),          # L2 gathers
+    ((96, 64), 512, 2, 8, 4),                # per-matrix kernels
+    ((130, 200, 50), 2048, 1, 16, 3),
+    ((100, 257, 64), 512, 2, 8, 16),         # matrix cores, input split over waves
+    ((300, 17), 1024, 1, 16, 16),
+    ((120, 40, 64, 8), 4096, 2, 8, 32),      # four matrices, two token tiles
+    ((200, 33, 100), 11008, 2, 8, 16),       # three units per wave
+    ((130, 70), 512, 2, 8, 128),             # tiled, split partial sums
+    ((129, 300), 2048, 1, 16, 64),
+]
+
+
+@pytest.mark.parametrize("case", GROUPED, ids=lambda c: "-".join(map(str, c[0])) + "x" + "x".join(map(str, c[1:])))
+def test_grouped(aq, orc, case):
+    outs, in_, K, B, batch = case
+    ps = _group(outs, in_, K, B, batch, 1700 + sum(outs) + in_ + batch)
+    dev = [_dev(p) for p in ps]
+    x = dev[0][2]
+    refs = [orc.gemv(p["codes"], p["codebooks"], p["x"], K, B) for p in ps]
+    for fn in (aq.gemv_grouped, aq.gemm_grouped):
+        ys = fn([d[0] for d in dev], [d[1] for d in dev], x)
+        for m, (y, r) in enumerate(zip(ys, refs)):
+            check_y(y, r, f"{fn.__name__} {case} matrix {m}")
+
+
+PACKED_GROUPED = [
+    ((100, 257, 64), 4096, 2, 8, 1),         # tiled lookup-table kernel
+    ((65, 33, 8), 520, 2, 8, 1),
+    ((300, 17, 1), 4096, 1, 16, 1),          # position-split kernel
+    ((130, 50), 2048, 1, 16, 3),
+    ((96, 64), 512, 2, 8, 2),                # unpacked matrix by matrix
+    ((40, 24), 512, 2, 16, 1),
+]
+
+
+@pytest.mark.parametrize("case", PACKED_GROUPED, ids=lambda c: "-".join(map(str, c[0])) + "x" + "x".join(map(str, c[1:])))
+def test_packed_grouped(aq, orc, case):
+    outs, in_, K, B, batch = case
+    ps = _group(outs, in_, K, B, batch, 1800 + sum(outs) + in_ + batch)
+    dev = [_dev(p) for p in ps]
+    W = [aq.pack_weights(d[0], d[1]) for d in dev]
+    ys = aq.gemv_packed_grouped(W, dev[0][2])
+    for m, (y, p) in enumerate(zip(ys, ps)):
+        check_y(y, orc.gemv(p["codes"], p["codebooks"], p["x"], K, B), f"packed grouped {case} {m}")
+    again = aq.gemv_packed_grouped(W, dev[0][2])
+    assert all(bool((a == b).all()) for a, b in zip(ys, again))
+
+
+@pytest.mark.parametrize("case", [
+    ("qkv 2x8", (4096, 4096, 4096), 4096, 2, 8, 1), ("qkv 2x8", (4096, 4096, 4096), 4096, 2, 8, 16),
+    ("qkv 2x8", (4096, 4096, 4096), 4096, 2, 8, 128), ("gate|up 2x8", (11008, 11008), 4096, 2, 8, 1),
+    ("gate|up 2x8", (11008, 11008), 4096, 2, 8, 16), ("qkv 1x16", (4096, 4096, 4096), 4096, 1, 16, 1),
+    ("qkv 1x16", (4096, 4096, 4096), 4096, 1, 16, 16), ("gate|up 1x16", (11008, 11008), 4096, 1, 16, 1)],
+    ids=lambda c: f"{c[0].replace(' ', '-')}-b{c[5]}")
+def test_grouped_full_size_sampled(aq, orc, case):
+    """The 7B layer's shared-x groups at full size, through aqlm_gemm_grouped and (batch 1)
+    aqlm_gemv_packed_grouped, checked on sampled rows."""
+    import torch
+    name, outs, in_, K, B, batch = case
+    ps = _group(outs, in_, K, B, batch, 1900 + len(outs) * 10 + K * 100 + batch)
+    dev = [_dev(p) for p in ps]
+    x = dev[0][2]
+    runs = [aq.gemm_grouped([d[0] for d in dev], [d[1] for d in dev], x)]
+    if batch == 1:
+        runs.append(aq.gemv_packed_grouped([aq.pack_weights(d[0], d[1]) for d in dev], x))
+    torch.cuda.synchronize()
+    for ys in runs:
+        for m, (y, p) in enumerate(zip(ys, ps)):
+            rows = _sampled_rows(outs[m], seed=m + batch)
+            yref = orc.gemv_rows(p["codes"], p["codebooks"], p["x"], K, B, rows)
+            e = rel_err(y.float().cpu().numpy()[:, rows], yref)
+            assert np.all(e <= TOL), f"{case} matrix {m}: {e.max():.3e}"
+
+
+@pytest.mark.parametrize("mode", ["gemm b16", "packed b1"])
+def test_grouped_graph_replay(aq, orc, mode):
+    import torch
+    batch = 16 if mode == "gemm b16" else 1
+    ps = _group((500, 300, 64), 2048, 2, 8, batch, 2000 + batch)
+    dev = [_dev(p) for p in ps]
+    x = dev[0][2]
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        if batch == 1:
+            W = [aq.pack_weights(d[0], d[1]) for d in dev]
+            fn = lambda out=None: aq.gemv_packed_grouped(W, x, out=out)
+        else:
+            fn = lambda out=None: aq.gemm_grouped([d[0] for d in dev], [d[1] for d in dev], x, out=out)
+        eager = [y.clone() for y in fn()]
+        ys = [torch.empty_like(y) for y in eager]
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            fn(out=ys)
+        for _ in range(3):
+            for y in ys:
+                y.fill_(3.0)
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            assert all(bool((a == b).all()) for a, b in zip(ys, eager))
+    for m, p in enumerate(ps):
+        check_y(eager[m], orc.gemv(p["codes"], p["codebooks"], p["x"], 2, 8), f"graph {mode} {m}")
