@@ -242,6 +242,13 @@ aqlm_status_t run(int variant, const aqlm::Problem &p) {
             if (e != hipSuccess) break;
             if (ws) {
                 e = aqlm::launch_lut(p, ws);
+            } else if (p.segs.n > 1) {
+                // capturing stream whose workspace fits the matrices one at a time only
+                for (int m = 0; m < p.segs.n; ++m) {
+                    const aqlm_status_t st = run(variant, segment(p, m));
+                    if (st != AQLM_OK) return st;
+                }
+                return AQLM_OK;
             } else {
                 // capturing stream without a workspace: same product, no workspace needed
                 if (log_enabled())
@@ -260,6 +267,14 @@ aqlm_status_t run(int variant, const aqlm::Problem &p) {
             if (need) {
                 e = get_workspace(p.stream, need, &ws);
                 if (e != hipSuccess) break;
+                if (!ws && p.segs.n > 1) {
+                    // capturing stream whose workspace may fit the matrices one at a time
+                    for (int m = 0; m < p.segs.n; ++m) {
+                        const aqlm_status_t st = run(variant, segment(p, m));
+                        if (st != AQLM_OK) return st;
+                    }
+                    return AQLM_OK;
+                }
                 if (!ws) {
                     // capturing stream without a workspace: same product, no workspace needed
                     for (int m = 0; m < p.segs.n && e == hipSuccess; ++m)

@@ -155,6 +155,9 @@ def main():
                     help="scheme for --workload layer7b")
     ap.add_argument("--linears", default="q,k,v,o,gate,up,down",
                     help="comma-separated subset of the layer's linears for --workload layer7b")
+    ap.add_argument("--grouped", action="store_true",
+                    help="--workload layer7b: q|k|v and gate|up as one grouped call each "
+                         "(members share the input); the separate calls are timed beside")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -363,20 +366,56 @@ def layer_bench(args, torch, np, aq, synth):
     ys = [torch.empty((batch, out), dtype=torch.float16, device=dev) for _, out, _ in layer]
     variants = [aq.selected_variant(*sets[0][i], gemm=True) for i in range(len(layer))]
     stream = torch.cuda.Stream()
+    # launch units: runs of linears that read the same activations (q|k|v, gate|up) become
+    # one grouped call with the first member's input; otherwise one call per linear
+    names = [n for n, _, _ in layer]
+    units = []
+    for i, n in enumerate(names):
+        fused = args.grouped and units and (
+            (n in ("k", "v") and names[units[-1][-1]] in ("q", "k")) or
+            (n == "up" and names[units[-1][-1]] == "gate"))
+        if fused:
+            units[-1].append(i)
+        else:
+            units.append([i])
 
     def call(i, r):
         aq.gemm(*sets[r][i], out=ys[i])
 
+    def call_unit(u, r):
+        if len(u) == 1:
+            call(u[0], r)
+        else:
+            aq.gemm_grouped([sets[r][i][0] for i in u], [sets[r][i][1] for i in u],
+                            sets[r][u[0]][2], out=[ys[i] for i in u])
+
     torch.cuda.synchronize()
     with torch.cuda.stream(stream):
+        # warm-up also sizes the stream's workspace for every call the graphs capture
         for w in range(max(2, args.warmup // 10)):
             for i in range(len(layer)):
                 call(i, w % copies)
+            for u in units:
+                call_unit(u, w % copies)
         torch.cuda.synchronize()
-        layer_graph = capture_on(torch, stream, lambda: [call(i, r) for r in range(copies)
-                                                         for i in range(len(layer))])
+        layer_graph = capture_on(torch, stream, lambda: [call_unit(u, r) for r in range(copies)
+                                                         for u in units])
         reps = max(1, args.steps // copies)
         dt_layer = time_graph(torch, layer_graph, reps) / (reps * copies)
+        dt_sep = None
+        if any(len(u) > 1 for u in units):
+            sep_graph = capture_on(torch, stream, lambda: [call(i, r) for r in range(copies)
+                                                           for i in range(len(layer))])
+            dt_sep = time_graph(torch, sep_graph, reps) / (reps * copies)
+        groups = []
+        for u in units:
+            if len(u) == 1:
+                continue
+            g = capture_on(torch, stream, lambda u=u: [call_unit(u, r) for r in range(copies)])
+            dt = time_graph(torch, g, reps) / (reps * copies)
+            nbytes = sum(algorithmic_bytes(layer[i][1], layer[i][2], K, B, batch) for i in u)
+            groups.append({"linears": "|".join(names[i] for i in u),
+                           "us_per_call": round(dt * 1e6, 3), "gbps": round(nbytes / dt / 1e9, 1)})
         per = []
         for i, (name, out, in_) in enumerate(layer):
             g = capture_on(torch, stream, lambda i=i: [call(i, r) for r in range(copies)])
@@ -402,7 +441,8 @@ def layer_bench(args, torch, np, aq, synth):
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
                 "kernel": f"{d['variant']} ({d['linear']} {d['shape']})"}
     result = {"metric": f"AQLM {args.scheme} Llama-2-7B layer ({','.join(n for n, _, _ in layer)}), "
-                        f"batch {batch}: layer time and achieved rates",
+                        f"batch {batch}{', grouped q|k|v and gate|up' if args.grouped else ''}: "
+                        f"layer time and achieved rates",
               "value": round(layer_bytes / dt_layer / 1e9, 1), "unit": "GB/s",
               "n_gpus": 1, "steps": reps * copies, "warmup": max(2, args.warmup // 10),
               "ms_per_step": round(dt_layer * 1e3, 5), "higher_is_better": True,
@@ -412,6 +452,10 @@ def layer_bench(args, torch, np, aq, synth):
                                      f"11008x4096; down 4096x11008; {args.scheme}, batch {batch}",
                          "batch": batch, "rotation_copies": copies, "launch": "hip graph replay"},
               "layer_us": round(dt_layer * 1e6, 2),
+              "grouped": [names[u[0]] if len(u) == 1 else "|".join(names[i] for i in u)
+                          for u in units] if args.grouped else None,
+              "layer_us_separate_calls": round(dt_sep * 1e6, 2) if dt_sep else None,
+              "per_group": groups or None,
               "layer_tflops": round(layer_flops / dt_layer / 1e12, 2),
               "per_linear": per, "roofline": roof}
     print(json.dumps(result), flush=True)

@@ -31,13 +31,15 @@
  * keeps no pointer to caller memory after a call returns.  Memory: the only
  * allocation is one workspace per (device, stream) for kernels that sum partial
  * results in a second pass (the batch-1 2x8 lookup-table kernel: out x
- * ceil(in/512) fp32; aqlm_gemv_packed: K*8 x batch x out fp32), made on the
- * first such call on that stream, grown when a larger shape needs it and kept
- * until the process exits.  Calls on different streams may run
- * concurrently.  On a stream that is being captured into a HIP graph and has no
- * workspace yet, that product runs on the workspace-free gather kernel instead
- * (same result within the stated tolerance); make one call on the stream
- * before capturing to get the lookup-table kernel in the graph.
+ * ceil(in/512) fp32; the matrix-core kernel above batch 32: splits x batch x out
+ * fp32; aqlm_gemv_packed: K*8 x batch x out fp32), made on the first such call on
+ * that stream, grown when a larger shape needs it and kept until the process
+ * exits.  Calls on different streams may run concurrently.  On a stream that is
+ * being captured into a HIP graph and has no large enough workspace, a grouped
+ * call runs its matrices one at a time, and a product that still does not fit
+ * runs on a workspace-free kernel instead (gather, else the generic kernel: same
+ * result within the stated tolerance, much slower); make the same calls on the
+ * stream once before capturing to get the fast kernels in the graph.
  *
  * Errors: argument errors are reported synchronously, before any device work:
  * a null pointer, a size < 1, in_features not a multiple of 8, K outside

@@ -533,3 +533,33 @@ def test_grouped_graph_replay(aq, orc, mode):
             assert all(bool((a == b).all()) for a, b in zip(ys, eager))
     for m, p in enumerate(ps):
         check_y(eager[m], orc.gemv(p["codes"], p["codebooks"], p["x"], 2, 8), f"graph {mode} {m}")
+
+
+@pytest.mark.parametrize("warm", ["one matrix", "cold"])
+def test_grouped_capture_small_workspace(aq, orc, warm):
+    """A grouped batch-128 product captured on a stream whose workspace fits one matrix
+    (or none): the graph runs the matrices one at a time (or workspace-free) and still
+    computes every product."""
+    import torch
+    ps = _group((500, 300, 64), 2048, 2, 8, 128, 2300)
+    dev = [_dev(p) for p in ps]
+    x = dev[0][2]
+    stream = torch.cuda.Stream()
+    ys = [torch.empty((128, p["codes"].shape[0]), dtype=torch.float16, device="cuda")
+          for p in ps]
+    with torch.cuda.stream(stream):
+        if warm == "one matrix":
+            aq.gemm(dev[0][0], dev[0][1], x)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            aq.gemm_grouped([d[0] for d in dev], [d[1] for d in dev], x, out=ys)
+        for _ in range(2):
+            for y in ys:
+                y.fill_(3.0)
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            for m, p in enumerate(ps):
+                check_y(ys[m], orc.gemv(p["codes"], p["codebooks"], p["x"], 2, 8),
+                        f"capture {warm} {m}")
