@@ -33,6 +33,8 @@
 // load), its B fragments the matching activations straight from global memory
 // (L2-resident), and the 16 partial tiles are added in LDS, in wave order, at
 // the end: no partial sums leave the workgroup.
+#include <type_traits>
+
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -93,7 +95,7 @@ template <int MS, int NT> struct Tile {
 };
 
 template <int K, int BITS, int MS, int NT, int NS>
-__global__ void __launch_bounds__(kMfmaWaves * kWave)
+__global__ void __launch_bounds__(kMfmaWaves * kWave) __attribute__((amdgpu_waves_per_eu(1, 1)))
 mfma_kernel(const uint16_t *__restrict__ x, float *__restrict__ partial, int in,
             int batch, int groups_per_split, const Segs segs) {
     typedef Tile<MS, NT> T;
@@ -132,55 +134,73 @@ mfma_kernel(const uint16_t *__restrict__ x, float *__restrict__ partial, int in,
     for (int i = threadIdx.x; i < CBE; i += blockDim.x)
         cbs[i] = reinterpret_cast<const uint4 *>(cb)[i];
 
+    // Software pipeline over chunks of CHG groups.  While the MFMAs of chunk c run,
+    // chunk c+1's A fragments are gathered (its codes arrived during chunk c-1) and its
+    // activations staged in LDS (loaded during chunk c-1); chunk c+2's codes and
+    // activations are loaded.  Every global load thus has a whole chunk of MFMAs to
+    // arrive.  Loads past the split are clamped into the matrix (always in bounds) and
+    // masked where used, so none is conditional.
+    //
     // activations of chunk c: token n, group g_begin + c*CHG + jj -> xs[buf][n*XROW + jj*8]
     auto load_x = [&](int c, uint4 (&r)[T::XLOADS]) {
 #pragma unroll
         for (int i = 0; i < T::XLOADS; ++i) {
             const int e = threadIdx.x + i * (kMfmaWaves * kWave);
             const int n = e / T::CHG, jj = e % T::CHG;
-            const int j = g_begin + c * T::CHG + jj;
-            const int tn = tok0 + n;
-            r[i] = make_uint4(0, 0, 0, 0);
-            if (tn < batch && j < g_end)
-                r[i] = *reinterpret_cast<const uint4 *>(x + size_t(tn) * in + size_t(j) * kGroup);
+            const int j = min(g_begin + c * T::CHG + jj, g_end - 1);
+            const int tn = min(tok0 + n, batch - 1);
+            r[i] = *reinterpret_cast<const uint4 *>(x + size_t(tn) * in + size_t(j) * kGroup);
         }
     };
-    auto store_x = [&](int buf, const uint4 (&r)[T::XLOADS]) {
+    // Groups past the split are zeroed (their A fragments are zero too; zeroing B as
+    // well keeps an inf or NaN of a clamped duplicate out of the sum).  Tokens past the
+    // batch are clamped duplicates whose outputs are never stored.  The mask is an AND
+    // with an opaque value: a select on the loaded vector would be turned into a branch
+    // that sinks the load to this point.
+    auto store_x = [&](int buf, int c, const uint4 (&r)[T::XLOADS]) {
 #pragma unroll
         for (int i = 0; i < T::XLOADS; ++i) {
             const int e = threadIdx.x + i * (kMfmaWaves * kWave);
             const int n = e / T::CHG, jj = e % T::CHG;
-            *reinterpret_cast<uint4 *>(&xs[buf][n * T::XROW + jj * 8]) = r[i];
+            uint32_t msk = g_begin + c * T::CHG + jj < g_end ? 0xFFFFFFFFu : 0u;
+            asm volatile("" : "+v"(msk));
+            *reinterpret_cast<uint4 *>(&xs[buf][n * T::XROW + jj * 8]) =
+                make_uint4(r[i].x & msk, r[i].y & msk, r[i].z & msk, r[i].w & msk);
         }
     };
-    // A fragments of chunk c: super-step q, k-step s -> group g_begin + c*CHG + q*SS + 4*kb + s.
-    // gather() only issues the codebook reads (raw vectors); fold() adds the K
-    // vectors and masks groups past the split, after the current chunk's MFMAs,
-    // so L2 latency of the 16-bit codebook overlaps with them.
-    auto gather = [&](int c, uint4 (&v0)[STEPS], uint4 (&v1)[STEPS], bool (&ok)[T::SPC]) {
+    // codes of chunk c, super-step q: the 4 groups g_begin + c*CHG + q*SS + 4*kb + (0..3)
+    auto load_codes = [&](int c, cblock_t (&cw)[T::SPC]) {
 #pragma unroll
         for (int q = 0; q < T::SPC; ++q) {
             const int jb = g_begin + c * T::CHG + q * T::SS + 4 * kb;
-            ok[q] = jb < g_end;                      // g_end - g_begin is a multiple of 4
-            const cblock_t cw = __builtin_nontemporal_load(crow + min(jb, G - 4) / 4);
+            cw[q] = __builtin_nontemporal_load(crow + min(jb, G - 4) / 4);
+        }
+    };
+    // A fragments: gather() only issues the codebook reads (raw vectors); fold() adds
+    // the K vectors and masks groups past the split after the current chunk's MFMAs,
+    // so the read latency (LDS, or L2 for the 16-bit codebook) overlaps with them.
+    auto gather = [&](const cblock_t (&cw)[T::SPC], uint4 (&v0)[STEPS], uint4 (&v1)[STEPS]) {
+#pragma unroll
+        for (int q = 0; q < T::SPC; ++q) {
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
-                const uint32_t c0 = block_code<K, BITS>(cw, s * K);
+                const uint32_t c0 = block_code<K, BITS>(cw[q], s * K);
                 v0[q * 4 + s] = BITS == 8 ? cbs[c0] : cbg[c0];
                 if constexpr (K == 2) {
-                    const uint32_t c1 = block_code<K, BITS>(cw, s * K + 1);
+                    const uint32_t c1 = block_code<K, BITS>(cw[q], s * K + 1);
                     v1[q * 4 + s] = BITS == 8 ? cbs[256 + c1] : cbg[(1u << 16) + c1];
                 }
             }
         }
     };
-    auto fold = [&](const uint4 (&v0)[STEPS], const uint4 (&v1)[STEPS], const bool (&ok)[T::SPC],
-                    half8 (&a)[STEPS]) {
+    auto fold = [&](int c, const uint4 (&v0)[STEPS], const uint4 (&v1)[STEPS], half8 (&a)[STEPS]) {
 #pragma unroll
         for (int st = 0; st < STEPS; ++st) {
+            // g_end - g_begin is a multiple of 4: a 4-group block is all in or all out
+            const bool ok = g_begin + c * T::CHG + (st / 4) * T::SS + 4 * kb < g_end;
             half8 f = __builtin_bit_cast(half8, v0[st]);
             if constexpr (K == 2) f = f + __builtin_bit_cast(half8, v1[st]);
-            a[st] = ok[st / 4] ? f : half8{};
+            a[st] = ok ? f : half8{};
         }
     };
 
@@ -188,61 +208,109 @@ mfma_kernel(const uint16_t *__restrict__ x, float *__restrict__ partial, int in,
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc[t] = acc_t{};
 
-    uint4 xr[T::XLOADS];
+    // Register slots: at chunk c (parity S = c & 1), cw[S] holds chunk c+1's codes
+    // and xr[S] its activations (both loaded two chunks earlier); slot S^1 holds chunk
+    // c+2's, still in flight.  After use, slot S is refilled with chunk c+3's.  The
+    // chunk loop is unrolled by two so that every slot index is a constant.
+    uint4 xr[2][T::XLOADS];
+    cblock_t cw[2][T::SPC];
     half8 acur[STEPS];
     uint4 g0[STEPS], g1[STEPS];                  // g1 only used when K = 2
-    bool gok[T::SPC];
-    if (nchunks > 0) {
-        load_x(0, xr);
-        if constexpr (BITS == 16) gather(0, g0, g1, gok);
-    }
-    if (CBE) __syncthreads();                        // codebooks staged
-    if (nchunks > 0) {
-        if constexpr (BITS == 8) gather(0, g0, g1, gok);   // LDS codebooks are ready only now
-        store_x(0, xr);
-        fold(g0, g1, gok, acur);
-    }
-    __syncthreads();
-
-    for (int c = 0; c < nchunks; ++c) {
-        const int buf = c & 1;
-        const bool more = c + 1 < nchunks;
-        if (more) {
-            load_x(c + 1, xr);
-            gather(c + 1, g0, g1, gok);
-        }
-        const uint16_t *xb = xs[buf];
-#pragma unroll
-        for (int st = 0; st < STEPS; ++st) {
-            const int q = st / 4, s = st % 4;
-            const int jj = q * T::SS + 4 * kb + s;   // group inside the chunk (same as A)
-#pragma unroll
-            for (int t = 0; t < NT; ++t) {
-                const half8 b = *reinterpret_cast<const half8 *>(
-                    &xb[(t * MS + m) * T::XROW + jj * 8]);
-                acc[t] = mfma<MS>(acur[st], b, acc[t]);
-            }
-        }
-        if (more) {
-            store_x(buf ^ 1, xr);
-            fold(g0, g1, gok, acur);
-        }
+    {
+        // prologue: chunk 0 decoded and staged; chunks 1 and 2 in flight.
+        // (Every split has at least one chunk.)
+        cblock_t cw0[T::SPC];
+        uint4 x0[T::XLOADS];
+        load_codes(0, cw0);
+        load_x(0, x0);
+        load_codes(1, cw[0]);
+        load_x(1, xr[0]);
+        load_codes(2, cw[1]);
+        load_x(2, xr[1]);
+        if constexpr (BITS == 16) gather(cw0, g0, g1);
+        if (CBE) __syncthreads();                    // codebooks staged
+        if constexpr (BITS == 8) gather(cw0, g0, g1);
+        store_x(0, 0, x0);
+        fold(0, g0, g1, acur);
         __syncthreads();
     }
 
-    // epilogue: partial tile (KSPLIT > 1) or y
+    // Nothing in a chunk is conditional: past the last chunk the loads are clamped
+    // duplicates and the staged values go unused (a conditional load would make the
+    // compiler wait for every load in flight where the paths join).
+    auto chunk = [&](int c, auto slot) {
+        constexpr int S = decltype(slot)::value;
+        gather(cw[S], g0, g1);                   // chunk c+1's codebook vectors
+        // B fragments of k-step st: token t*MS + m, group q*SS + 4*kb + s of the chunk
+        // (the same group as the A fragment).  Those of step st+1 are read while the
+        // MFMAs of step st run, so no MFMA waits for an LDS read of its own.
+        const uint16_t *xb = xs[S];
+        auto load_b = [&](int st, half8 (&b)[NT]) {
+            const int jj = (st / 4) * T::SS + 4 * kb + (st % 4);
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+                b[t] = *reinterpret_cast<const half8 *>(&xb[(t * MS + m) * T::XROW + jj * 8]);
+        };
+        half8 bq[2][NT];
+        load_b(0, bq[0]);
+#pragma unroll
+        for (int st = 0; st < STEPS; ++st) {
+            if (st + 1 < STEPS) load_b(st + 1, bq[(st + 1) & 1]);
+            // pinned order: left to itself the scheduler sinks each read to its MFMA
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int t = 0; t < NT; ++t) acc[t] = mfma<MS>(acur[st], bq[st & 1][t], acc[t]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        store_x(S ^ 1, c + 1, xr[S]);
+        fold(c + 1, g0, g1, acur);
+        load_x(c + 3, xr[S]);
+        load_codes(c + 3, cw[S]);
+        __syncthreads();
+    };
+    // Chunks go in pairs.  With an odd count the last one is past the split: its A and
+    // B fragments are all zero and it adds nothing (mfma_cfg makes the counts even where
+    // it can).  The first pair is unconditional (do-while), so that the prologue's loads
+    // stay above the barriers.
+    int c = 0;
+    do {
+        chunk(c, std::integral_constant<int, 0>{});
+        chunk(c + 1, std::integral_constant<int, 1>{});
+        c += 2;
+    } while (c < nchunks);
+
+    // Epilogue: the workgroup's tile goes through LDS (the activation buffers are free
+    // now) as [token][row], so that the stores to global memory are row-contiguous:
+    // one 4-byte (partial) or 2-byte (y) store per lane, consecutive lanes on
+    // consecutive rows.
+    constexpr int ROWS = kMfmaWaves * MS;            // rows per workgroup
+    constexpr int TROW = ROWS + 4;                   // floats per token row (+16 B pad)
+    static_assert(sizeof(float) * T::BN * TROW <= sizeof(xs), "output tile fits the LDS buffers");
+    float *tile = reinterpret_cast<float *>(&xs[0][0]);
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
 #pragma unroll
-        for (int r = 0; r < NACC; ++r) {
-            const int row = row0 + out_row<MS>(lane, r);
-            const int n = tok0 + t * MS + (lane % MS);
-            if (row < out && n < batch) {
-                if (partial)
-                    partial[(size_t(split) * batch + n) * rows_all + pick(segs.row0, mi) + row] = acc[t][r];
-                else
-                    y[size_t(n) * out + row] = f2h_bits(acc[t][r]);
-            }
+        for (int r4 = 0; r4 < NACC / 4; ++r4) {
+            // registers 4*r4 .. 4*r4+3 hold 4 consecutive rows of one token
+            const int rl = wave * MS + out_row<MS>(lane, 4 * r4);
+            const int tl = t * MS + (lane % MS);
+            const float4 v = make_float4(acc[t][4 * r4], acc[t][4 * r4 + 1], acc[t][4 * r4 + 2],
+                                         acc[t][4 * r4 + 3]);
+            *reinterpret_cast<float4 *>(&tile[tl * TROW + rl]) = v;
+        }
+    }
+    __syncthreads();
+    const int wg_row0 = (blockIdx.x - pick(segs.aux0, mi)) * ROWS;
+    const size_t prow0 = size_t(pick(segs.row0, mi)) + wg_row0;
+    for (int e = threadIdx.x; e < T::BN * ROWS; e += kMfmaWaves * kWave) {
+        const int tl = e / ROWS, rl = e % ROWS;
+        const int n = tok0 + tl, row = wg_row0 + rl;
+        if (row < out && n < batch) {
+            const float v = tile[tl * TROW + rl];
+            if (partial)
+                partial[(size_t(split) * batch + n) * rows_all + prow0 + rl] = v;
+            else
+                y[size_t(n) * out + row] = f2h_bits(v);
         }
     }
 }
@@ -276,8 +344,11 @@ MfmaCfg mfma_cfg(const Problem &p, Segs *segs = nullptr) {
     int64_t ks = (256 + tiles - 1) / tiles;
     if (ks > nchunks) ks = nchunks;
     if (ks < 1) ks = 1;
-    // whole chunks per split (multiples of 4 groups keep code blocks whole)
-    int64_t gps = (nchunks + ks - 1) / ks * chg;
+    // whole chunks per split (multiples of 4 groups keep code blocks whole), an even
+    // number of them (the kernel runs chunks in pairs)
+    int64_t cps = (nchunks + ks - 1) / ks;
+    cps += cps & 1;
+    int64_t gps = cps * chg;
     c.ksplit = int((G + gps - 1) / gps);
     c.groups_per_split = int(gps);
     return c;

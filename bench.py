@@ -155,6 +155,9 @@ def main():
                     help="scheme for --workload layer7b")
     ap.add_argument("--linears", default="q,k,v,o,gate,up,down",
                     help="comma-separated subset of the layer's linears for --workload layer7b")
+    ap.add_argument("--layers", type=int, default=0,
+                    help="--workload layer7b: a decode sweep over this many layers, each with its "
+                         "own weights, captured as one HIP graph (e.g. 32 for Llama-2-7B)")
     ap.add_argument("--grouped", action="store_true",
                     help="--workload layer7b: q|k|v and gate|up as one grouped call each "
                          "(members share the input); the separate calls are timed beside")
@@ -183,7 +186,7 @@ def main():
         return copy_bench(args, torch)
 
     per_copy = sum(algorithmic_bytes(o, i, K, B) for _, o, i, K, B in WORKLOAD)
-    copies = args.copies or max(2, math.ceil(2 * MALL_BYTES / per_copy))
+    copies = args.layers or args.copies or max(2, math.ceil(2 * MALL_BYTES / per_copy))
     t_gen = time.perf_counter()
     sets, ys = build_inputs(torch, synth, aq, copies)
     torch.cuda.synchronize()
@@ -352,7 +355,7 @@ def layer_bench(args, torch, np, aq, synth):
     layer = [e for e in LAYER_7B if e[0] in wanted]
     dev = torch.device("cuda:0")
     per_copy = sum(algorithmic_bytes(o, i, K, B, batch) for _, o, i in layer)
-    copies = args.copies or max(2, math.ceil(2 * MALL_BYTES / per_copy))
+    copies = args.layers or args.copies or max(2, math.ceil(2 * MALL_BYTES / per_copy))
     sets = []
     for r in range(copies):
         entry = []
@@ -456,6 +459,10 @@ def layer_bench(args, torch, np, aq, synth):
                           for u in units] if args.grouped else None,
               "layer_us_separate_calls": round(dt_sep * 1e6, 2) if dt_sep else None,
               "per_group": groups or None,
+              "decode_sweep": {"layers": copies, "us": round(dt_layer * copies * 1e6, 1),
+                               "tokens_per_s": round(batch / (dt_layer * copies), 1),
+                               "note": "linears only (no attention, norms or sampling)"}
+              if args.layers else None,
               "layer_tflops": round(layer_flops / dt_layer / 1e12, 2),
               "per_linear": per, "roofline": roof}
     print(json.dumps(result), flush=True)
