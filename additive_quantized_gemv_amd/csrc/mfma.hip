@@ -131,9 +131,6 @@ mfma_kernel(const uint16_t *__restrict__ x, float *__restrict__ partial, int in,
         codes + size_t(o) * size_t(G) * (K * BITS / 8));
     const uint4 *cbg = reinterpret_cast<const uint4 *>(cb);
 
-    for (int i = threadIdx.x; i < CBE; i += blockDim.x)
-        cbs[i] = reinterpret_cast<const uint4 *>(cb)[i];
-
     // Software pipeline over chunks of CHG groups.  While the MFMAs of chunk c run,
     // chunk c+1's A fragments are gathered (its codes arrived during chunk c-1) and its
     // activations staged in LDS (loaded during chunk c-1); chunk c+2's codes and
@@ -218,7 +215,13 @@ mfma_kernel(const uint16_t *__restrict__ x, float *__restrict__ partial, int in,
     uint4 g0[STEPS], g1[STEPS];                  // g1 only used when K = 2
     {
         // prologue: chunk 0 decoded and staged; chunks 1 and 2 in flight.
-        // (Every split has at least one chunk.)
+        // (Every split has at least one chunk.)  The codebook loads go first and
+        // every chunk load is issued before their LDS stores wait for them.
+        constexpr int CBPT = (CBE + kMfmaWaves * kWave - 1) / (kMfmaWaves * kWave);
+        uint4 cbv[CBPT > 0 ? CBPT : 1];
+#pragma unroll
+        for (int i = 0; i < CBPT; ++i)
+            cbv[i] = cbg[min(int(threadIdx.x) + i * kMfmaWaves * kWave, CBE - 1)];
         cblock_t cw0[T::SPC];
         uint4 x0[T::XLOADS];
         load_codes(0, cw0);
@@ -228,6 +231,11 @@ mfma_kernel(const uint16_t *__restrict__ x, float *__restrict__ partial, int in,
         load_codes(2, cw[1]);
         load_x(2, xr[1]);
         if constexpr (BITS == 16) gather(cw0, g0, g1);
+        // unconditional stores (clamped threads rewrite the last vector with its own
+        // value), so that the codebook loads are not sunk behind the others
+#pragma unroll
+        for (int i = 0; i < CBPT; ++i)
+            cbs[min(int(threadIdx.x) + i * kMfmaWaves * kWave, CBE - 1)] = cbv[i];
         if (CBE) __syncthreads();                    // codebooks staged
         if constexpr (BITS == 8) gather(cw0, g0, g1);
         store_x(0, 0, x0);
