@@ -58,7 +58,9 @@ def algorithmic_bytes(out, in_, K, B, batch=1):
 def source_sha(variant):
     path = os.path.join(ROOT, "additive_quantized_gemv_amd", "csrc", KERNEL_SOURCES[variant])
     h = hashlib.sha256()
-    for p in (path, os.path.join(ROOT, "additive_quantized_gemv_amd", "csrc", "device_common.hpp")):
+    # the kernel's own source, the shared device helpers and the partial-sum kernel
+    for p in (path, os.path.join(ROOT, "additive_quantized_gemv_amd", "csrc", "device_common.hpp"),
+              os.path.join(ROOT, "additive_quantized_gemv_amd", "csrc", "generic.hip")):
         with open(p, "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
