@@ -12,8 +12,10 @@
 //   fp16 rounding of the fp32 fold because fp32 carries more than 2*11+2 bits
 //   (double rounding through fp32 is innocuous for one fp16 addition).
 // * B = 8 codebooks are staged in LDS; the B = 16 codebook is read through L2.
-// * Workgroup = 4 waves on 4*MS consecutive rows x (MS*NT) tokens.  Waves own
-//   different rows and share the activations: chunks of CHG groups x all tokens
+// * Workgroup = 8 waves on 4*MS consecutive rows x (MS*NT) tokens.  Wave pairs own
+//   different rows (each wave of a pair one half of every chunk's input groups,
+//   their tiles added in LDS at the end: two waves per SIMD) and share the
+//   activations: chunks of CHG groups x all tokens
 //   are staged in LDS (double-buffered, rows padded by 16 B so the B-fragment
 //   reads of one instruction hit different banks).  While the MFMAs of chunk c
 //   run, the activations of chunk c+1 are loaded and its A fragments decoded.
@@ -41,7 +43,8 @@
 namespace aqlm {
 namespace {
 
-constexpr int kMfmaWaves = 4;
+constexpr int kMfmaWaves = 4;                  // row groups of a tiled workgroup
+constexpr int kTiledThreads = 2 * kMfmaWaves * kWave;   // two waves per row group
 
 template <int MS> struct Acc;
 template <> struct Acc<16> { typedef float4v type; static constexpr int n = 4; };
@@ -91,11 +94,13 @@ template <int MS, int NT> struct Tile {
     static constexpr int SPC = CHG / SS;             // super-steps per chunk
     static constexpr int XROW = CHG * 8 + 8;         // halves per staged token row (+16 B pad)
     static constexpr int XBUF = BN * XROW;           // halves per chunk buffer
-    static constexpr int XLOADS = BN * CHG / (kMfmaWaves * kWave);   // 16-B loads per thread
+    static constexpr int XLOADS = BN * CHG / kTiledThreads;   // 16-B loads per thread
+    static_assert(SPC == 2, "one super-step per wave of a row group");
+    static_assert(BN * CHG % kTiledThreads == 0, "whole activation loads per thread");
 };
 
 template <int K, int BITS, int MS, int NT, int NS>
-__global__ void __launch_bounds__(kMfmaWaves * kWave) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ void __launch_bounds__(kTiledThreads)
 mfma_kernel(const uint16_t *__restrict__ x, float *__restrict__ partial, int in,
             int batch, int groups_per_split, const Segs segs) {
     typedef Tile<MS, NT> T;
@@ -103,12 +108,16 @@ mfma_kernel(const uint16_t *__restrict__ x, float *__restrict__ partial, int in,
     typedef typename CodeBlock<K, BITS>::type cblock_t;
     constexpr int CBE = BITS == 8 ? K * 256 : 0;
     constexpr int NACC = Acc<MS>::n;
-    constexpr int STEPS = T::SPC * 4;                // MFMA k-steps per chunk
+    constexpr int STEPS = 4;                         // MFMA k-steps per chunk and wave
     __shared__ uint4 cbs[CBE > 0 ? CBE : 1];
     __shared__ __attribute__((aligned(16))) uint16_t xs[2][T::XBUF];
 
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    // Waves w and w+4 own row group w & 3 (MS rows) and take super-steps 0 and 1 of
+    // every chunk (h = w >> 2): two waves per SIMD, whose partial tiles are added in
+    // LDS at the end.
+    const int rg = wave & (kMfmaWaves - 1), h = wave >> 2;
     const int G = in / kGroup;
     // row tiles of each matrix are numbered consecutively (segs.aux0)
     const int mi = seg_of<NS>(segs.n, segs.aux0, blockIdx.x);
@@ -117,7 +126,7 @@ mfma_kernel(const uint16_t *__restrict__ x, float *__restrict__ partial, int in,
     const uint8_t *__restrict__ codes = static_cast<const uint8_t *>(pick(segs.codes, mi));
     const uint16_t *__restrict__ cb = static_cast<const uint16_t *>(pick(segs.cb, mi));
     uint16_t *__restrict__ y = static_cast<uint16_t *>(pick(segs.y, mi));
-    const int row0 = (blockIdx.x - pick(segs.aux0, mi)) * (kMfmaWaves * MS) + wave * MS;
+    const int row0 = (blockIdx.x - pick(segs.aux0, mi)) * (kMfmaWaves * MS) + rg * MS;
     const int tok0 = blockIdx.y * T::BN;
     const int split = blockIdx.z;
     const int g_begin = split * groups_per_split;
@@ -142,7 +151,7 @@ mfma_kernel(const uint16_t *__restrict__ x, float *__restrict__ partial, int in,
     auto load_x = [&](int c, uint4 (&r)[T::XLOADS]) {
 #pragma unroll
         for (int i = 0; i < T::XLOADS; ++i) {
-            const int e = threadIdx.x + i * (kMfmaWaves * kWave);
+            const int e = threadIdx.x + i * kTiledThreads;
             const int n = e / T::CHG, jj = e % T::CHG;
             const int j = min(g_begin + c * T::CHG + jj, g_end - 1);
             const int tn = min(tok0 + n, batch - 1);
@@ -157,7 +166,7 @@ mfma_kernel(const uint16_t *__restrict__ x, float *__restrict__ partial, int in,
     auto store_x = [&](int buf, int c, const uint4 (&r)[T::XLOADS]) {
 #pragma unroll
         for (int i = 0; i < T::XLOADS; ++i) {
-            const int e = threadIdx.x + i * (kMfmaWaves * kWave);
+            const int e = threadIdx.x + i * kTiledThreads;
             const int n = e / T::CHG, jj = e % T::CHG;
             uint32_t msk = g_begin + c * T::CHG + jj < g_end ? 0xFFFFFFFFu : 0u;
             asm volatile("" : "+v"(msk));
@@ -165,28 +174,22 @@ mfma_kernel(const uint16_t *__restrict__ x, float *__restrict__ partial, int in,
                 make_uint4(r[i].x & msk, r[i].y & msk, r[i].z & msk, r[i].w & msk);
         }
     };
-    // codes of chunk c, super-step q: the 4 groups g_begin + c*CHG + q*SS + 4*kb + (0..3)
-    auto load_codes = [&](int c, cblock_t (&cw)[T::SPC]) {
-#pragma unroll
-        for (int q = 0; q < T::SPC; ++q) {
-            const int jb = g_begin + c * T::CHG + q * T::SS + 4 * kb;
-            cw[q] = __builtin_nontemporal_load(crow + min(jb, G - 4) / 4);
-        }
+    // codes of chunk c, this wave's super-step h: groups g_begin + c*CHG + h*SS + 4*kb + (0..3)
+    auto load_codes = [&](int c, cblock_t &cw) {
+        const int jb = g_begin + c * T::CHG + h * T::SS + 4 * kb;
+        cw = __builtin_nontemporal_load(crow + min(jb, G - 4) / 4);
     };
     // A fragments: gather() only issues the codebook reads (raw vectors); fold() adds
     // the K vectors and masks groups past the split after the current chunk's MFMAs,
     // so the read latency (LDS, or L2 for the 16-bit codebook) overlaps with them.
-    auto gather = [&](const cblock_t (&cw)[T::SPC], uint4 (&v0)[STEPS], uint4 (&v1)[STEPS]) {
+    auto gather = [&](const cblock_t &cw, uint4 (&v0)[STEPS], uint4 (&v1)[STEPS]) {
 #pragma unroll
-        for (int q = 0; q < T::SPC; ++q) {
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const uint32_t c0 = block_code<K, BITS>(cw[q], s * K);
-                v0[q * 4 + s] = BITS == 8 ? cbs[c0] : cbg[c0];
-                if constexpr (K == 2) {
-                    const uint32_t c1 = block_code<K, BITS>(cw[q], s * K + 1);
-                    v1[q * 4 + s] = BITS == 8 ? cbs[256 + c1] : cbg[(1u << 16) + c1];
-                }
+        for (int s = 0; s < STEPS; ++s) {
+            const uint32_t c0 = block_code<K, BITS>(cw, s * K);
+            v0[s] = BITS == 8 ? cbs[c0] : cbg[c0];
+            if constexpr (K == 2) {
+                const uint32_t c1 = block_code<K, BITS>(cw, s * K + 1);
+                v1[s] = BITS == 8 ? cbs[256 + c1] : cbg[(1u << 16) + c1];
             }
         }
     };
@@ -194,7 +197,7 @@ mfma_kernel(const uint16_t *__restrict__ x, float *__restrict__ partial, int in,
 #pragma unroll
         for (int st = 0; st < STEPS; ++st) {
             // g_end - g_begin is a multiple of 4: a 4-group block is all in or all out
-            const bool ok = g_begin + c * T::CHG + (st / 4) * T::SS + 4 * kb < g_end;
+            const bool ok = g_begin + c * T::CHG + h * T::SS + 4 * kb < g_end;
             half8 f = __builtin_bit_cast(half8, v0[st]);
             if constexpr (K == 2) f = f + __builtin_bit_cast(half8, v1[st]);
             a[st] = ok ? f : half8{};
@@ -210,19 +213,19 @@ mfma_kernel(const uint16_t *__restrict__ x, float *__restrict__ partial, int in,
     // c+2's, still in flight.  After use, slot S is refilled with chunk c+3's.  The
     // chunk loop is unrolled by two so that every slot index is a constant.
     uint4 xr[2][T::XLOADS];
-    cblock_t cw[2][T::SPC];
+    cblock_t cw[2];
     half8 acur[STEPS];
     uint4 g0[STEPS], g1[STEPS];                  // g1 only used when K = 2
     {
         // prologue: chunk 0 decoded and staged; chunks 1 and 2 in flight.
         // (Every split has at least one chunk.)  The codebook loads go first and
         // every chunk load is issued before their LDS stores wait for them.
-        constexpr int CBPT = (CBE + kMfmaWaves * kWave - 1) / (kMfmaWaves * kWave);
+        constexpr int CBPT = (CBE + kTiledThreads - 1) / kTiledThreads;
         uint4 cbv[CBPT > 0 ? CBPT : 1];
 #pragma unroll
         for (int i = 0; i < CBPT; ++i)
-            cbv[i] = cbg[min(int(threadIdx.x) + i * kMfmaWaves * kWave, CBE - 1)];
-        cblock_t cw0[T::SPC];
+            cbv[i] = cbg[min(int(threadIdx.x) + i * kTiledThreads, CBE - 1)];
+        cblock_t cw0;
         uint4 x0[T::XLOADS];
         load_codes(0, cw0);
         load_x(0, x0);
@@ -235,7 +238,7 @@ mfma_kernel(const uint16_t *__restrict__ x, float *__restrict__ partial, int in,
         // value), so that the codebook loads are not sunk behind the others
 #pragma unroll
         for (int i = 0; i < CBPT; ++i)
-            cbs[min(int(threadIdx.x) + i * kMfmaWaves * kWave, CBE - 1)] = cbv[i];
+            cbs[min(int(threadIdx.x) + i * kTiledThreads, CBE - 1)] = cbv[i];
         if (CBE) __syncthreads();                    // codebooks staged
         if constexpr (BITS == 8) gather(cw0, g0, g1);
         store_x(0, 0, x0);
@@ -249,12 +252,12 @@ mfma_kernel(const uint16_t *__restrict__ x, float *__restrict__ partial, int in,
     auto chunk = [&](int c, auto slot) {
         constexpr int S = decltype(slot)::value;
         gather(cw[S], g0, g1);                   // chunk c+1's codebook vectors
-        // B fragments of k-step st: token t*MS + m, group q*SS + 4*kb + s of the chunk
+        // B fragments of k-step st: token t*MS + m, group h*SS + 4*kb + st of the chunk
         // (the same group as the A fragment).  Those of step st+1 are read while the
         // MFMAs of step st run, so no MFMA waits for an LDS read of its own.
         const uint16_t *xb = xs[S];
         auto load_b = [&](int st, half8 (&b)[NT]) {
-            const int jj = (st / 4) * T::SS + 4 * kb + (st % 4);
+            const int jj = h * T::SS + 4 * kb + st;
 #pragma unroll
             for (int t = 0; t < NT; ++t)
                 b[t] = *reinterpret_cast<const half8 *>(&xb[(t * MS + m) * T::XROW + jj * 8]);
@@ -290,27 +293,38 @@ mfma_kernel(const uint16_t *__restrict__ x, float *__restrict__ partial, int in,
     // Epilogue: the workgroup's tile goes through LDS (the activation buffers are free
     // now) as [token][row], so that the stores to global memory are row-contiguous:
     // one 4-byte (partial) or 2-byte (y) store per lane, consecutive lanes on
-    // consecutive rows.
+    // consecutive rows.  The super-step-1 waves write their tiles, then the
+    // super-step-0 waves add theirs (sum = h0 + h1, in that order).
     constexpr int ROWS = kMfmaWaves * MS;            // rows per workgroup
     constexpr int TROW = ROWS + 4;                   // floats per token row (+16 B pad)
     static_assert(sizeof(float) * T::BN * TROW <= sizeof(xs), "output tile fits the LDS buffers");
     float *tile = reinterpret_cast<float *>(&xs[0][0]);
+    auto tile_pass = [&](bool add) {
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
+        for (int t = 0; t < NT; ++t) {
 #pragma unroll
-        for (int r4 = 0; r4 < NACC / 4; ++r4) {
-            // registers 4*r4 .. 4*r4+3 hold 4 consecutive rows of one token
-            const int rl = wave * MS + out_row<MS>(lane, 4 * r4);
-            const int tl = t * MS + (lane % MS);
-            const float4 v = make_float4(acc[t][4 * r4], acc[t][4 * r4 + 1], acc[t][4 * r4 + 2],
-                                         acc[t][4 * r4 + 3]);
-            *reinterpret_cast<float4 *>(&tile[tl * TROW + rl]) = v;
+            for (int r4 = 0; r4 < NACC / 4; ++r4) {
+                // registers 4*r4 .. 4*r4+3 hold 4 consecutive rows of one token
+                const int rl = rg * MS + out_row<MS>(lane, 4 * r4);
+                const int tl = t * MS + (lane % MS);
+                float4 *q = reinterpret_cast<float4 *>(&tile[tl * TROW + rl]);
+                float4 v = make_float4(acc[t][4 * r4], acc[t][4 * r4 + 1], acc[t][4 * r4 + 2],
+                                       acc[t][4 * r4 + 3]);
+                if (add) {
+                    const float4 u = *q;
+                    v = make_float4(v.x + u.x, v.y + u.y, v.z + u.z, v.w + u.w);
+                }
+                *q = v;
+            }
         }
-    }
+    };
+    if (h == 1) tile_pass(false);
+    __syncthreads();
+    if (h == 0) tile_pass(true);
     __syncthreads();
     const int wg_row0 = (blockIdx.x - pick(segs.aux0, mi)) * ROWS;
     const size_t prow0 = size_t(pick(segs.row0, mi)) + wg_row0;
-    for (int e = threadIdx.x; e < T::BN * ROWS; e += kMfmaWaves * kWave) {
+    for (int e = threadIdx.x; e < T::BN * ROWS; e += kTiledThreads) {
         const int tl = e / ROWS, rl = e % ROWS;
         const int n = tok0 + tl, row = wg_row0 + rl;
         if (row < out && n < batch) {
@@ -367,7 +381,7 @@ MfmaCfg mfma_cfg(const Problem &p, Segs *segs = nullptr) {
 
 template <int K, int BITS, int MS, int NT>
 hipError_t launch_t(const Problem &p, const MfmaCfg &c, const Segs &segs, float *partial) {
-    const dim3 g(c.grid_x, c.grid_y, c.ksplit), b(kMfmaWaves * kWave);
+    const dim3 g(c.grid_x, c.grid_y, c.ksplit), b(kTiledThreads);
     const uint16_t *x = static_cast<const uint16_t *>(p.x);
     if (segs.n == 1)
         hipLaunchKernelGGL((mfma_kernel<K, BITS, MS, NT, 1>), g, b, 0, p.stream, x, partial,
