@@ -360,13 +360,14 @@ MfmaCfg mfma_cfg(const Problem &p, Segs *segs = nullptr) {
     c.grid_y = (p.batch + c.ms * c.nt - 1) / (c.ms * c.nt);
     const int64_t tiles = int64_t(c.grid_x) * c.grid_y;
     const int64_t nchunks = (G + chg - 1) / chg;
-    // About one workgroup per CU, but at least 2*NT chunks per split.  Measured on
-    // MI355X at batch 128 (splits 2/4/8/16): fewer splits leave CUs idle, more cost more
-    // in the batch*out fp32 partial sums each split writes and the reduction re-reads,
-    // and a split of few chunks does not amortise its start-up (4096 x 4096: 4 splits
-    // of 8 chunks beat 8 of 4; 4096 x 11008: 8 splits of 12 chunks beat 4 of 22 and 16
-    // of 6).  At batch 64 (half the MFMAs per chunk) 8 splits of 4 chunks beat 4 of 8.
-    int64_t ks = (256 + tiles - 1) / tiles;
+    // At most one workgroup per CU (one workgroup fills a CU's registers: a 257th
+    // would run in a second round), and at least 2*NT chunks per split.  Measured on
+    // MI355X at batches 64 and 128 (splits 1..8): fewer splits leave CUs idle, more
+    // cost more in the batch*out fp32 partial sums each split writes and the reduction
+    // re-reads, and a split of few chunks does not amortise its start-up (4096 x 4096
+    // at batch 128: 4 splits of 8 chunks beat 8 of 4; 11008 x 4096: 2 splits (172
+    // workgroups) beat 3 (258); 4096 x 11008: 8 splits of 12 chunks beat fewer).
+    int64_t ks = 256 / tiles;
     if (ks > nchunks / (2 * c.nt)) ks = nchunks / (2 * c.nt);
     if (ks < 1) ks = 1;
     // whole chunks per split (multiples of 4 groups keep code blocks whole), an even
