@@ -241,7 +241,16 @@ DsCfg ds_cfg(const Problem &p, Segs *segs = nullptr) {
     int nr = 256 / P;                           // one workgroup per CU
     if (nr < 8) nr = 8;
     if (nr > p.out) nr = int(p.out);
-    c.rows_per_range = int((p.out + nr - 1) / nr);
+    // each matrix of a grouped call gets whole ranges of its own; they may not outnumber
+    // nr (one workgroup fills a CU's LDS), so the range grows until they fit
+    int64_t rpr = (p.out + nr - 1) / nr;
+    auto ranges = [&](int64_t r) {
+        int64_t t = 0;
+        for (int m = 0; m < p.segs.n; ++m) t += (p.segs.row0[m + 1] - p.segs.row0[m] + r - 1) / r;
+        return t;
+    };
+    while (ranges(rpr) > nr) ++rpr;
+    c.rows_per_range = int(rpr);
     int total = 0;
     for (int m = 0; m < p.segs.n; ++m) {
         if (segs) segs->aux0[m] = total;

@@ -276,6 +276,16 @@ LutCfg lut_cfg(const Problem &p, bool packed, Segs *segs = nullptr) {
     else rpb = (rpb + kLutWaves - 1) / kLutWaves * kLutWaves; // whole rows per wave
     if (rpb < kLutWaves) rpb = kLutWaves;
     if (rpb > max_rows) rpb = max_rows;
+    // Each matrix of a grouped call gets whole blocks of its own; the blocks may not
+    // outnumber nrb (a workgroup fills a CU's LDS: one more block column would run in
+    // a second round), so the block grows until they fit.
+    const int64_t unit = packed ? 8 : kLutWaves;
+    auto blocks = [&](int64_t r) {
+        int64_t t = 0;
+        for (int m = 0; m < p.segs.n; ++m) t += (p.segs.row0[m + 1] - p.segs.row0[m] + r - 1) / r;
+        return t;
+    };
+    while (blocks(rpb) > nrb && rpb + unit <= max_rows) rpb += unit;
     c.rows_per_block = int(rpb);
     int64_t total = 0;
     for (int m = 0; m < p.segs.n; ++m) {
