@@ -553,9 +553,13 @@ aqlm_status_t aqlm_gemv_packed_grouped(int n, const void *const *packed_codes,
     const bool tiled = tiled_codes(K, B);
     const bool split = !generic && !tiled &&
                        all_segments(p, [](const aqlm::Problem &q) { return aqlm::ds_supported(q); });
+    // batches the LDS-plane dot-product kernel does not take: the same planes on the
+    // matrix cores
+    const bool splitm = !generic && !tiled && !split &&
+                        all_segments(p, [](const aqlm::Problem &q) { return aqlm::dsm_supported(q); });
     const bool lutp = !generic && tiled &&
                       all_segments(p, [](const aqlm::Problem &q) { return aqlm::lut_packed_supported(q); });
-    if (!split && !lutp && n > 1) {
+    if (!split && !splitm && !lutp && n > 1) {
         // unpacked one matrix at a time through the workspace (stream order keeps them apart)
         for (int m = 0; m < n; ++m) {
             st = aqlm_gemv_packed_grouped(1, packed_codes + m, packed_codebooks + m, x, y + m,
@@ -567,9 +571,21 @@ aqlm_status_t aqlm_gemv_packed_grouped(int n, const void *const *packed_codes,
     const int64_t cbytes = out_features[0] * (in_features / kGroup) * K * (B / 8);
     const int64_t cbbytes = int64_t(K) * (int64_t(1) << B) * kGroup * 2;
     const size_t cb_off = (size_t(cbytes) + 255) / 256 * 256;
-    const size_t need = split  ? aqlm::ds_workspace_bytes(p)
-                        : lutp ? aqlm::lut_packed_workspace_bytes(p)
-                        : tiled ? cb_off + size_t(cbbytes) : size_t(cbbytes);
+    // unpacked operands, then (matrix cores) that kernel's own workspace
+    const size_t unpacked = tiled ? cb_off + size_t(cbbytes) : size_t(cbbytes);
+    const size_t ops_off = (unpacked + 255) / 256 * 256;
+    const bool gemm = !generic && batch >= mfma_min_batch();
+    size_t mfma_ws = 0;
+    if (!split && !splitm && !lutp && gemm) {
+        const aqlm::Problem shape = make_problem(p.codes, p.codebooks, p.x, p.y, p.out, p.in, K,
+                                                 B, batch, stream);
+        // sized on the shape alone (the kernel's own pointers are checked at launch)
+        if (aqlm::mfma_supported(shape)) mfma_ws = aqlm::mfma_workspace_bytes(shape);
+    }
+    const size_t need = split    ? aqlm::ds_workspace_bytes(p)
+                        : splitm ? aqlm::dsm_workspace_bytes(p)
+                        : lutp   ? aqlm::lut_packed_workspace_bytes(p)
+                                 : ops_off + mfma_ws;
     void *ws = nullptr;
     hipError_t e = get_workspace(p.stream, need, &ws);
     if (e != hipSuccess) {
@@ -579,12 +595,13 @@ aqlm_status_t aqlm_gemv_packed_grouped(int n, const void *const *packed_codes,
     if (!ws) return AQLM_ERR_UNSUPPORTED;   // capturing stream without a workspace
     if (log_enabled())
         std::fprintf(stderr, "[aqlm] packed %s n=%d rows=%lld in=%lld K=%d B=%d batch=%d\n",
-                     split ? "split" : lutp ? "lut_packed" : "unpack+auto", n, (long long)p.out,
+                     split ? "split" : splitm ? "split-mfma" : lutp ? "lut_packed" : "unpack+auto", n,
+                     (long long)p.out,
                      (long long)p.in, K, B, batch);
-    if (split || lutp) {
-        e = split ? aqlm::launch_ds(p, ws) : aqlm::launch_lut_packed(p, ws);
+    if (split || splitm || lutp) {
+        e = split ? aqlm::launch_ds(p, ws) : splitm ? aqlm::launch_dsm(p, ws) : aqlm::launch_lut_packed(p, ws);
         if (e != hipSuccess) {
-            set_error(split ? "split" : "lut_packed", e);
+            set_error(split ? "split" : splitm ? "split-mfma" : "lut_packed", e);
             return AQLM_ERR_HIP;
         }
         return AQLM_OK;
@@ -606,8 +623,19 @@ aqlm_status_t aqlm_gemv_packed_grouped(int n, const void *const *packed_codes,
     }
     aqlm::Problem q = make_problem(tiled ? wsb : p.codes, cbws, p.x, p.y, p.out, p.in, K, B,
                                    batch, stream);
+    if (gemm && aqlm::mfma_supported(q) && aqlm::mfma_workspace_bytes(q) <= mfma_ws) {
+        // matrix cores, with their partial sums after the unpacked operands
+        e = aqlm::launch_mfma(q, mfma_ws ? wsb + ops_off : nullptr);
+        if (e != hipSuccess) {
+            set_error("mfma", e);
+            return AQLM_ERR_HIP;
+        }
+        return AQLM_OK;
+    }
     int v = choose(false, q);
-    if (v == AQLM_VARIANT_LUT) v = AQLM_VARIANT_LDS;   // the workspace holds the operands
+    // the workspace holds the operands: no kernel that needs one of its own
+    if (v == AQLM_VARIANT_LUT || v == AQLM_VARIANT_MFMA) v = AQLM_VARIANT_LDS;
+    if (v == AQLM_VARIANT_LDS && !supported(v, q)) v = AQLM_VARIANT_GENERIC;
     return run(v, q);
 }
 

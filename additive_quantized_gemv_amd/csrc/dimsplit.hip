@@ -31,6 +31,9 @@ namespace {
 constexpr int kDsWaves = 16;
 constexpr int kEntries = 65536;
 constexpr int kXPlaneHalves = 14336;   // batch * in/8 activations of one position
+// tokens of the matrix-core form: one 16-token tile (measured on MI355X against unpacking
+// and the canonical kernels: 1.3-6x faster at batches 5..8, even at 16, slower from 32)
+constexpr int kDsmMaxBatch = 16;
 
 typedef _Float16 hf;
 
@@ -202,6 +205,189 @@ ds_kernel(const uint8_t *__restrict__ codes1, const uint16_t *__restrict__ plane
     }
 }
 
+// ------------------------------------------------------------------ batch 5 .. 128
+// The same position split on the matrix cores.  Workgroups are laid out as for
+// ds_kernel (one plane (k, t) x one row range, the planes of a range on one XCD);
+// a wave takes 16-row tiles of the range and runs each over the whole input axis
+// with v_mfma_f32_16x16x32_f16, 16 tokens per token tile:
+// * weight operand (B): lane (row j, k-block kb) holds the plane values of groups
+//   32s + 8kb .. +7 of its row: one 16-byte code load (K = 1; two for K = 2) and 8
+//   LDS lookups;
+// * activation operand (A): the position-t activations of the same 8 groups, one
+//   16-byte load from xT[t][token][group], a transposed copy that xt_kernel writes
+//   first (the activations are the A operand so that a result register holds 16
+//   consecutive weight rows of one token: row-contiguous partial-sum stores);
+// * D steps of codes and activations are in flight per lane (a ring, as in
+//   ds_kernel);
+// * up to 16 tokens (one token tile).  Measured on MI355X the kernel is bound by the
+//   L2 request rate of its loads, not by the lookups: the MFMA operand layout puts 16
+//   rows in every load instruction, 64 bytes each, for the codes and likewise for the
+//   activations.
+// Per-plane partial sums go to the workspace and partial_sum adds the K*8 planes.
+
+// xT[t][b][j] = x[b][8j + t]
+__global__ void __launch_bounds__(256)
+xt_kernel(const uint16_t *__restrict__ x, uint16_t *__restrict__ xT, int batch, int G) {
+    const int64_t n = int64_t(batch) * G;
+    for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < n;
+         i += int64_t(gridDim.x) * 256) {
+        // x[b][8j .. 8j+7] with i = b*G + j (in = 8G)
+        const uint4 v = *reinterpret_cast<const uint4 *>(x + i * kGroup);
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+            xT[int64_t(t) * n + i] = uint16_t(w[t >> 1] >> (16 * (t & 1)));
+    }
+}
+
+// k-steps of codes and activations in flight per lane (4K + 4NT registers each)
+template <int K, int NT> constexpr int dsm_ring() { return K * NT >= 4 ? 3 : 4; }
+
+template <int K, int NT, int NS>
+__global__ void __launch_bounds__(kDsWaves * kWave)
+dsm_kernel(const uint8_t *__restrict__ codes1, const uint16_t *__restrict__ planes1,
+           const uint16_t *__restrict__ xT, float *__restrict__ partial, int out1, int in,
+           int batch, int tb, int nranges, int rows_per_range, const Segs segs) {
+    // tokens tb .. tb + 16*NT - 1 (a token block; larger batches launch once per block)
+    constexpr int P = K * 8;
+    constexpr int D = dsm_ring<K, NT>();
+    __shared__ __attribute__((aligned(16))) hf tab[kEntries];
+
+    // block -> (plane, row range), as in ds_kernel
+    const int id = blockIdx.x;
+    const int grp = id / (P * 8), rem = id - grp * (P * 8);
+    const int p = rem >> 3;
+    const int rr = grp * 8 + (rem & 7);
+    if (rr >= nranges) return;
+    const int k = p >> 3, t = p & 7;
+    const int mi = seg_of<NS>(segs.n, segs.aux0, rr);
+    const int lrr = NS == 1 ? rr : rr - pick(segs.aux0, mi);
+    const int out = NS == 1 ? out1 : pick(segs.row0, mi + 1) - pick(segs.row0, mi);
+    const int T = NS == 1 ? out1 : segs.row0[segs.n];
+    const int orow0 = NS == 1 ? 0 : pick(segs.row0, mi);
+    const uint8_t *__restrict__ codes =
+        NS == 1 ? codes1 : static_cast<const uint8_t *>(pick(segs.codes, mi));
+    const uint16_t *__restrict__ planes =
+        NS == 1 ? planes1 : static_cast<const uint16_t *>(pick(segs.cb, mi));
+
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int G = in / kGroup;
+    const int r_begin = lrr * rows_per_range;
+    const int r_end = min(out, r_begin + rows_per_range);
+
+    {
+        // 128 KiB plane: every load of a thread issued before its LDS writes
+        const uint4 *src = reinterpret_cast<const uint4 *>(planes + size_t(p) * kEntries);
+        uint4 *dst = reinterpret_cast<uint4 *>(tab);
+        constexpr int PER = kEntries / 8 / (kDsWaves * kWave);
+        uint4 tmp[PER];
+#pragma unroll
+        for (int i = 0; i < PER; ++i) tmp[i] = src[threadIdx.x + i * kDsWaves * kWave];
+#pragma unroll
+        for (int i = 0; i < PER; ++i) dst[threadIdx.x + i * kDsWaves * kWave] = tmp[i];
+    }
+    __syncthreads();
+
+    const int ntiles = (r_end - r_begin + 15) / 16;   // <= 0: nothing to do
+    const int nsteps = (G + 31) / 32;
+    const int i16 = lane & 15, kb = lane >> 4;
+    const uint16_t *xp = xT + size_t(t) * batch * G;  // plane t: [batch][G]
+    const size_t row_bytes = size_t(G) * K * 2;
+
+    // (one token block per launch: a loop over blocks here would let the compiler hoist
+    // the loads that do not depend on it, and change the ring's load order, see below)
+    for (int tile = wave; tile < ntiles; tile += kDsWaves) {
+        const int row = min(r_begin + tile * 16 + i16, r_end - 1);  // past the end: not stored
+        const uint8_t *crow = codes + size_t(row) * row_bytes;
+        // the activation loads do not depend on the tile: an opaque zero in their
+        // address keeps them in this loop, in the ring's order (hoisted out of it,
+        // every wait in the k-step loop would become a wait for most of the ring)
+        int tz = tile;
+        asm volatile("" : "+s"(tz));
+        const uint16_t *xq = xp + (tz - tile);
+        {
+            // codes and activations of k-step s (clamped into the row: always in bounds)
+            auto load = [&](int s, u32x4 (&cw)[K], half8 (&xa)[NT]) {
+                const int jb = min(s * 32 + 8 * kb, G - 8);
+#pragma unroll
+                for (int kk = 0; kk < K; ++kk)
+                    cw[kk] = __builtin_nontemporal_load(
+                        reinterpret_cast<const u32x4 *>(crow + size_t(jb) * K * 2) + kk);
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) {
+                    const int tok = min(tb + nt * 16 + i16, batch - 1);
+                    xa[nt] = *reinterpret_cast<const half8 *>(xq + size_t(tok) * G + jb);
+                }
+            };
+            u32x4 rc[D][K];
+            half8 rx[D][NT];
+            // issued slot by slot in the loop's own order (codes, then activations):
+            // the waits in the loop are counted against this order too, so a reordered
+            // prologue would make every wait there a wait for the whole ring
+#pragma unroll
+            for (int q = 0; q < D; ++q) {
+                load(q, rc[q], rx[q]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            float4v acc[NT];
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) acc[nt] = float4v{};
+            for (int base = 0; base < nsteps; base += D) {
+#pragma unroll
+                for (int q = 0; q < D; ++q) {
+                    const int s = base + q;
+                    const u32x4 (&cw)[K] = rc[q];
+                    const half8 (&xa)[NT] = rx[q];
+                    // groups past the row (a clamped block, or a step past the last) add
+                    // nothing: both operands are zeroed (an AND with an opaque mask, so
+                    // that the loads are not turned into branches)
+                    uint32_t msk = s * 32 + 8 * kb < G ? 0xFFFFFFFFu : 0u;
+                    asm volatile("" : "+v"(msk));
+                    half8 w;
+#pragma unroll
+                    for (int g = 0; g < 8; ++g) {
+                        uint32_t code;
+                        if constexpr (K == 1) {
+                            const uint32_t v = cw[0][g >> 1];
+                            code = (g & 1) ? (v >> 16) : (v & 0xFFFFu);
+                        } else {
+                            // 32 bytes: group g's two codes are word g (codebook k in half k)
+                            code = (cw[g >> 2][g & 3] >> (16 * k)) & 0xFFFFu;
+                        }
+                        w[g] = tab[code];
+                    }
+                    u32x4 wb = __builtin_bit_cast(u32x4, w);
+                    wb &= msk;
+                    w = __builtin_bit_cast(half8, wb);
+#pragma unroll
+                    for (int nt = 0; nt < NT; ++nt) {
+                        u32x4 xb = __builtin_bit_cast(u32x4, xa[nt]);
+                        xb &= msk;
+                        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                            __builtin_bit_cast(half8, xb), w, acc[nt], 0, 0, 0);
+                    }
+                    // the slot is consumed: refill it D steps ahead (loaded in place,
+                    // so the ring needs no register copies)
+                    __builtin_amdgcn_sched_barrier(0);
+                    load(s + D, rc[q], rx[q]);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+            // result lane l, register r: token 4(l/16) + r of the token tile, row l % 16
+            const int rowo = r_begin + tile * 16 + i16;
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int tok = tb + nt * 16 + 4 * kb + r;
+                    if (tok < batch && rowo < r_end)
+                        partial[(size_t(p) * batch + tok) * T + orow0 + rowo] = acc[nt][r];
+                }
+        }
+    }
+}
+
 // planes[k][t][c] = codebooks[k][c][t]
 __global__ void __launch_bounds__(256)
 pack_kernel(const uint16_t *__restrict__ cb, uint16_t *__restrict__ planes, int K, int entries) {
@@ -301,7 +487,73 @@ hipError_t launch1(const Problem &p, const DsCfg &c, const Segs &segs, float *pa
     return launch2<K, 4>(p, c, segs, partial);
 }
 
+template <int K, int NT>
+hipError_t launch_m2(const Problem &p, const DsCfg &c, const Segs &segs, const uint16_t *xT,
+                     float *partial) {
+    const dim3 g(c.grid), b(kDsWaves * kWave);
+    const uint8_t *codes = static_cast<const uint8_t *>(segs.codes[0]);
+    const uint16_t *planes = static_cast<const uint16_t *>(segs.cb[0]);
+    const int out = segs.row0[1];
+    for (int tb = 0; tb < p.batch; tb += 16 * NT) {
+        if (segs.n == 1)
+            hipLaunchKernelGGL((dsm_kernel<K, NT, 1>), g, b, 0, p.stream, codes, planes, xT,
+                               partial, out, int(p.in), p.batch, tb, c.nranges, c.rows_per_range,
+                               segs);
+        else
+            hipLaunchKernelGGL((dsm_kernel<K, NT, kMaxSegs>), g, b, 0, p.stream, codes, planes,
+                               xT, partial, out, int(p.in), p.batch, tb, c.nranges,
+                               c.rows_per_range, segs);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+template <int K>
+hipError_t launch_m1(const Problem &p, const DsCfg &c, const Segs &segs, const uint16_t *xT,
+                     float *partial) {
+    return launch_m2<K, 1>(p, c, segs, xT, partial);
+}
+
 }  // namespace
+
+bool dsm_supported(const Problem &p) {
+    if (p.B != 16 || (p.K != 1 && p.K != 2)) return false;
+    if (p.batch < 1 || p.batch > kDsmMaxBatch) return false;
+    const int64_t G = p.in / kGroup;
+    if (G % 8) return false;
+    if (p.out > (1 << 28) || int64_t(p.batch) * p.in > (int64_t(1) << 31)) return false;
+    const uintptr_t a = reinterpret_cast<uintptr_t>(p.codes) |
+                        reinterpret_cast<uintptr_t>(p.codebooks) |
+                        reinterpret_cast<uintptr_t>(p.x);
+    return (a & 15u) == 0;
+}
+
+// workspace: [K*8][batch][T] fp32 partial sums, then xT [8][batch][G] fp16 (256-byte aligned)
+static size_t dsm_partial_bytes(const Problem &p) {
+    return (size_t(p.K) * 8 * size_t(p.batch) * size_t(p.out) * sizeof(float) + 255) / 256 * 256;
+}
+
+size_t dsm_workspace_bytes(const Problem &p) {
+    return dsm_partial_bytes(p) + size_t(p.batch) * size_t(p.in) * 2;
+}
+
+hipError_t launch_dsm(const Problem &p, void *workspace) {
+    Segs segs = p.segs;
+    const DsCfg c = ds_cfg(p, &segs);
+    float *partial = static_cast<float *>(workspace);
+    uint16_t *xT = reinterpret_cast<uint16_t *>(static_cast<char *>(workspace) + dsm_partial_bytes(p));
+    const int G = int(p.in / kGroup);
+    const int64_t n = int64_t(p.batch) * G;
+    const int blocks = int((n + 255) / 256 < 2048 ? (n + 255) / 256 : 2048);
+    hipLaunchKernelGGL(xt_kernel, dim3(blocks), dim3(256), 0, p.stream,
+                       static_cast<const uint16_t *>(p.x), xT, p.batch, G);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    e = p.K == 1 ? launch_m1<1>(p, c, segs, xT, partial) : launch_m1<2>(p, c, segs, xT, partial);
+    if (e != hipSuccess) return e;
+    return launch_partial_sum_segs(partial, segs, p.batch, p.K * 8, p.stream);
+}
 
 bool ds_supported(const Problem &p) {
     if (p.B != 16 || (p.K != 1 && p.K != 2)) return false;

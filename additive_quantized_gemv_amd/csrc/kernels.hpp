@@ -73,6 +73,9 @@ hipError_t launch_pack_codes_lut(const void *src, void *dst, int64_t out, int64_
 bool ds_supported(const Problem &p);
 size_t ds_workspace_bytes(const Problem &p);
 hipError_t launch_ds(const Problem &p, void *workspace);
+bool dsm_supported(const Problem &p);
+size_t dsm_workspace_bytes(const Problem &p);
+hipError_t launch_dsm(const Problem &p, void *workspace);
 hipError_t launch_pack_codebooks(const void *cb, void *planes, int K, int B, hipStream_t s);
 hipError_t launch_unpack_codebooks(const void *planes, void *cb, int K, int B, hipStream_t s);
 

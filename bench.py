@@ -160,6 +160,9 @@ def main():
     ap.add_argument("--layers", type=int, default=0,
                     help="--workload layer7b: a decode sweep over this many layers, each with its "
                          "own weights, captured as one HIP graph (e.g. 32 for Llama-2-7B)")
+    ap.add_argument("--packed", action="store_true",
+                    help="--workload layer7b: weights packed once at load (aqlm_gemv_packed[_grouped]) "
+                         "instead of the canonical layout through aqlm_gemm")
     ap.add_argument("--grouped", action="store_true",
                     help="--workload layer7b: q|k|v and gate|up as one grouped call each "
                          "(members share the input); the separate calls are timed beside")
@@ -367,9 +370,13 @@ def layer_bench(args, torch, np, aq, synth):
             codes = p["codes"] if B == 8 else p["codes"].view(np.int16)
             entry.append((torch.from_numpy(codes).to(dev), torch.from_numpy(p["codebooks"]).to(dev),
                           torch.from_numpy(p["x"]).to(dev)))
+            if args.packed:   # packed once at load; the canonical tensors are dropped
+                w = aq.pack_weights(entry[-1][0], entry[-1][1])
+                entry[-1] = (w, None, entry[-1][2])
         sets.append(entry)
     ys = [torch.empty((batch, out), dtype=torch.float16, device=dev) for _, out, _ in layer]
-    variants = [aq.selected_variant(*sets[0][i], gemm=True) for i in range(len(layer))]
+    variants = (["packed"] * len(layer) if args.packed else
+                [aq.selected_variant(*sets[0][i], gemm=True) for i in range(len(layer))])
     stream = torch.cuda.Stream()
     # launch units: runs of linears that read the same activations (q|k|v, gate|up) become
     # one grouped call with the first member's input; otherwise one call per linear
@@ -385,11 +392,17 @@ def layer_bench(args, torch, np, aq, synth):
             units.append([i])
 
     def call(i, r):
-        aq.gemm(*sets[r][i], out=ys[i])
+        if args.packed:
+            aq.gemv_packed(sets[r][i][0], sets[r][i][2], out=ys[i])
+        else:
+            aq.gemm(*sets[r][i], out=ys[i])
 
     def call_unit(u, r):
         if len(u) == 1:
             call(u[0], r)
+        elif args.packed:
+            aq.gemv_packed_grouped([sets[r][i][0] for i in u], sets[r][u[0]][2],
+                                   out=[ys[i] for i in u])
         else:
             aq.gemm_grouped([sets[r][i][0] for i in u], [sets[r][i][1] for i in u],
                             sets[r][u[0]][2], out=[ys[i] for i in u])
@@ -446,7 +459,8 @@ def layer_bench(args, torch, np, aq, synth):
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
                 "kernel": f"{d['variant']} ({d['linear']} {d['shape']})"}
     result = {"metric": f"AQLM {args.scheme} Llama-2-7B layer ({','.join(n for n, _, _ in layer)}), "
-                        f"batch {batch}{', grouped q|k|v and gate|up' if args.grouped else ''}: "
+                        f"batch {batch}{', packed weights' if args.packed else ''}"
+                        f"{', grouped q|k|v and gate|up' if args.grouped else ''}: "
                         f"layer time and achieved rates",
               "value": round(layer_bytes / dt_layer / 1e9, 1), "unit": "GB/s",
               "n_gpus": 1, "steps": reps * copies, "warmup": max(2, args.warmup // 10),

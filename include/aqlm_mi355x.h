@@ -75,7 +75,7 @@ typedef enum {
     AQLM_VARIANT_L2 = 4,      /* B = 16: codebook gathered through L2, batch <= 8            */
     AQLM_VARIANT_MFMA = 5,    /* decode to fp16 fragments + fp16 matrix cores, any batch     */
     AQLM_VARIANT_SPLIT = 6    /* B = 16, packed codebooks: one codebook position per CU,
-                                 batch <= 4 (aqlm_gemv_packed only)                        */
+                                 batch <= 16 (aqlm_gemv_packed only)                       */
 } aqlm_variant_t;
 
 /*
@@ -163,13 +163,17 @@ aqlm_status_t aqlm_unpack_codes(const void *packed, void *codes, int64_t out_fea
  * - 16-bit codes, K in {1,2}, batch <= 4: the position-split kernel
  *   (AQLM_VARIANT_SPLIT): the K*8 codebook planes live in the LDS of K*8
  *   workgroups per row range and a second kernel adds their partial sums.
+ * - 16-bit codes, K in {1,2}, batch 5..16, in_features a multiple of 64,
+ *   16-byte aligned pointers: the same planes on the matrix cores (a small
+ *   kernel first writes x transposed by position into the workspace).
  * - 2x8, batch 1, 16-byte aligned pointers: the lookup-table kernel reading
  *   the code tiles (1 KiB contiguous per wave load).
  * - otherwise the packed operands are unpacked into the stream's workspace and
- *   the product runs as aqlm_gemv.
- * Uses the per-(device, stream) workspace (partial sums, or the unpacked
- * operands); on a capturing stream without a large enough workspace it returns
- * AQLM_ERR_UNSUPPORTED (make one call on the stream first).
+ *   the product runs as aqlm_gemm does (matrix cores from batch 16, their
+ *   partial sums after the operands), else as aqlm_gemv.
+ * Uses the per-(device, stream) workspace (partial sums, transposed x, or the
+ * unpacked operands); on a capturing stream without a large enough workspace it
+ * returns AQLM_ERR_UNSUPPORTED (make one call on the stream first).
  */
 aqlm_status_t aqlm_gemv_packed(const void *packed_codes, const void *packed_codebooks,
                                const void *x, void *y, int64_t out_features, int64_t in_features,

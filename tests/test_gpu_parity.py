@@ -355,6 +355,15 @@ PACKED = [
     (40, 512, 2, 8, 1), (65, 520, 2, 8, 1), (1, 64, 2, 8, 1), (300, 4096, 2, 8, 1),
     (257, 11008, 2, 8, 1), (1023, 4160, 2, 8, 1), (5000, 512, 2, 8, 1), (96, 512, 2, 8, 4),
     (64, 512, 1, 8, 2),
+    # 16-bit codes above batch 4: the position split on the matrix cores (one-step rows,
+    # a partial last k-step, several tiles per wave, token blocks of 32 past batch 32)
+    (300, 4096, 1, 16, 5), (100, 4096, 1, 16, 16), (257, 11008, 1, 16, 17),
+    (130, 2048, 1, 16, 33), (77, 1024, 1, 16, 64), (64, 512, 1, 16, 100), (40, 4096, 1, 16, 128),
+    (1000, 4096, 1, 16, 16), (17, 256, 1, 16, 7), (33, 64, 1, 16, 16), (50, 1024, 2, 16, 16),
+    (96, 520, 2, 16, 40),
+    (65, 520, 1, 16, 16),      # in/8 not a multiple of 8: unpacked, generic kernel
+    # 2x8 from batch 16: unpacked, then the matrix cores (persistent / tiled with partial sums)
+    (300, 4096, 2, 8, 16), (257, 4096, 2, 8, 33), (96, 512, 2, 8, 128),
 ]
 
 
@@ -373,7 +382,8 @@ def test_gemv_packed(aq, orc, case):
 @pytest.mark.parametrize("case", [("mlp_1x16_7b", 11008, 4096, 1), ("mlp_1x16_7b", 4096, 11008, 1),
                                   ("mlp_1x16_70b", 28672, 8192, 4), ("mlp_1x16_70b", 8192, 28672, 1),
                                   ("proj_1x16_4096", 4096, 4096, 1), ("mlp_2x8_7b", 11008, 4096, 1),
-                                  ("mlp_2x8_7b", 4096, 11008, 1)],
+                                  ("mlp_2x8_7b", 4096, 11008, 1), ("mlp_1x16_7b", 11008, 4096, 16),
+                                  ("mlp_1x16_7b", 4096, 11008, 128), ("mlp_2x8_7b", 4096, 11008, 16)],
                          ids=lambda c: f"{c[0]}-{c[1]}x{c[2]}-b{c[3]}")
 def test_full_size_packed_sampled(aq, orc, case):
     import torch
@@ -391,11 +401,12 @@ def test_full_size_packed_sampled(aq, orc, case):
     assert np.all(e <= TOL), f"{case}: {e.max():.3e}"
 
 
+@pytest.mark.parametrize("batch", [1, 16, 40])
 @pytest.mark.parametrize("KB", [(1, 16), (2, 8)])
-def test_packed_graph_replay(aq, orc, KB):
+def test_packed_graph_replay(aq, orc, KB, batch):
     import torch
     K, B = KB
-    p = synth.make_problem(2000, 4096, K, B, batch=1, sigma_cb=0.02, config=1600 + K)
+    p = synth.make_problem(2000, 4096, K, B, batch=batch, sigma_cb=0.02, config=1600 + K + batch)
     codes, cb, x = _dev(p)
     stream = torch.cuda.Stream()
     with torch.cuda.stream(stream):
@@ -462,6 +473,9 @@ PACKED_GROUPED = [
     ((130, 50), 2048, 1, 16, 3),
     ((96, 64), 512, 2, 8, 2),                # unpacked matrix by matrix
     ((40, 24), 512, 2, 16, 1),
+    ((300, 17, 64), 4096, 1, 16, 16),        # position split on the matrix cores
+    ((130, 50), 2048, 1, 16, 40),
+    ((96, 64), 512, 2, 8, 16),               # unpacked, matrix cores
 ]
 
 
