@@ -519,7 +519,8 @@ hipError_t launch_m1(const Problem &p, const DsCfg &c, const Segs &segs, const u
 
 bool dsm_supported(const Problem &p) {
     if (p.B != 16 || (p.K != 1 && p.K != 2)) return false;
-    if (p.batch < 1 || p.batch > kDsmMaxBatch) return false;
+    // two codebooks double the lookups per weight: past batch 8 the canonical kernels win
+    if (p.batch < 1 || p.batch > (p.K == 1 ? kDsmMaxBatch : 8)) return false;
     const int64_t G = p.in / kGroup;
     if (G % 8) return false;
     if (p.out > (1 << 28) || int64_t(p.batch) * p.in > (int64_t(1) << 31)) return false;

@@ -70,6 +70,29 @@ template <> struct CodeBlock<1, 8> { typedef uint32_t type; };
 template <> struct CodeBlock<2, 8> { typedef u32x2 type; };
 template <> struct CodeBlock<1, 16> { typedef u32x2 type; };
 template <> struct CodeBlock<2, 16> { typedef u32x4 type; };
+template <> struct CodeBlock<4, 8> { typedef u32x4 type; };
+template <> struct CodeBlock<8, 8> { typedef u32x8 type; };
+
+// Decode of one group from K > 2 codebook vectors: the fp32 left fold in codebook order,
+// rounded once to fp16 (the fp16 value aqlm_dequantize writes).  K <= 2 adds in fp16
+// directly, which rounds the exact sum once and is the same value.
+template <int K>
+__device__ __forceinline__ half8 fold_fp32(const uint4 (&v)[K]) {
+    float f[8];
+    const half8 h0 = __builtin_bit_cast(half8, v[0]);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f[e] = float(h0[e]);
+#pragma unroll
+    for (int k = 1; k < K; ++k) {
+        const half8 h = __builtin_bit_cast(half8, v[k]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) f[e] += float(h[e]);
+    }
+    half8 r;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) r[e] = _Float16(f[e]);
+    return r;
+}
 
 template <int K, int BITS>
 __device__ __forceinline__ uint32_t block_code(const typename CodeBlock<K, BITS>::type &cw, int n) {
@@ -79,6 +102,8 @@ __device__ __forceinline__ uint32_t block_code(const typename CodeBlock<K, BITS>
     } else if constexpr (K * BITS == 16) {
         const uint32_t w = (n >> (BITS == 8 ? 2 : 1)) ? cw.y : cw.x;
         return BITS == 8 ? (w >> (8 * (n & 3))) & 0xFFu : (w >> (16 * (n & 1))) & 0xFFFFu;
+    } else if constexpr (BITS == 8) {
+        return (cw[n >> 2] >> (8 * (n & 3))) & 0xFFu;
     } else {
         const int wi = n >> 1;
         const uint32_t w = wi == 0 ? cw.x : wi == 1 ? cw.y : wi == 2 ? cw.z : cw.w;
@@ -185,6 +210,14 @@ mfma_kernel(const uint16_t *__restrict__ x, float *__restrict__ partial, int in,
     auto gather = [&](const cblock_t &cw, uint4 (&v0)[STEPS], uint4 (&v1)[STEPS]) {
 #pragma unroll
         for (int s = 0; s < STEPS; ++s) {
+            if constexpr (K > 2) {
+                // (8-bit codes only) folded here in fp32; v0 holds the fp16 result
+                uint4 v[K];
+#pragma unroll
+                for (int k = 0; k < K; ++k) v[k] = cbs[k * 256 + block_code<K, BITS>(cw, s * K + k)];
+                v0[s] = __builtin_bit_cast(uint4, fold_fp32<K>(v));
+                continue;
+            }
             const uint32_t c0 = block_code<K, BITS>(cw, s * K);
             v0[s] = BITS == 8 ? cbs[c0] : cbg[c0];
             if constexpr (K == 2) {
@@ -216,6 +249,7 @@ mfma_kernel(const uint16_t *__restrict__ x, float *__restrict__ partial, int in,
     cblock_t cw[2];
     half8 acur[STEPS];
     uint4 g0[STEPS], g1[STEPS];                  // g1 only used when K = 2
+    (void)g1;
     {
         // prologue: chunk 0 decoded and staged; chunks 1 and 2 in flight.
         // (Every split has at least one chunk.)  The codebook loads go first and
@@ -499,12 +533,15 @@ mfma_kw_kernel(const uint8_t *__restrict__ codes, const uint16_t *__restrict__ c
     // vector per thread and matrix: K*256 <= 1024 threads), the first tile's codes and,
     // with one unit per wave, the activations; the staging store then waits for the
     // codebooks.
-    uint4 cbv[NSEGS];
+    constexpr int CBPT = (CBE + kKw * kWave - 1) / (kKw * kWave);   // vectors per thread
+    uint4 cbv[NSEGS][CBPT > 0 ? CBPT : 1];
     if constexpr (CBE > 0) {
 #pragma unroll
         for (int q = 0; q < NSEGS; ++q) {
             const uint4 *src = NSEGS == 1 ? cbg : static_cast<const uint4 *>(segs.cb[min(q, segs.n - 1)]);
-            cbv[q] = src[min(int(threadIdx.x), CBE - 1)];
+#pragma unroll
+            for (int i = 0; i < CBPT; ++i)
+                cbv[q][i] = src[min(int(threadIdx.x) + i * kKw * kWave, CBE - 1)];
         }
     }
     int tile = blockIdx.x;
@@ -516,7 +553,10 @@ mfma_kw_kernel(const uint8_t *__restrict__ codes, const uint16_t *__restrict__ c
         // unconditional (threads past the end rewrite the last vector with its own
         // value), so the codebook load is not sunk behind the others
 #pragma unroll
-        for (int q = 0; q < NSEGS; ++q) cbs[q * CBE + min(int(threadIdx.x), CBE - 1)] = cbv[q];
+        for (int q = 0; q < NSEGS; ++q)
+#pragma unroll
+            for (int i = 0; i < CBPT; ++i)
+                cbs[q * CBE + min(int(threadIdx.x) + i * kKw * kWave, CBE - 1)] = cbv[q][i];
         __syncthreads();
     }
 
@@ -546,11 +586,19 @@ mfma_kw_kernel(const uint8_t *__restrict__ codes, const uint16_t *__restrict__ c
             half8 a[8];
 #pragma unroll
             for (int s = 0; s < 8; ++s) {
-                const uint32_t c0 = seg_code<BITS, NW>(cw[i], s * K);
-                half8 f = __builtin_bit_cast(half8, cbm[c0]);
-                if constexpr (K == 2) {
-                    const uint32_t c1 = seg_code<BITS, NW>(cw[i], s * K + 1);
-                    f = f + __builtin_bit_cast(half8, cbm[(1u << BITS) + c1]);
+                half8 f;
+                if constexpr (K > 2) {
+                    uint4 v[K];
+#pragma unroll
+                    for (int k = 0; k < K; ++k) v[k] = cbm[k * (1u << BITS) + seg_code<BITS, NW>(cw[i], s * K + k)];
+                    f = fold_fp32<K>(v);
+                } else {
+                    const uint32_t c0 = seg_code<BITS, NW>(cw[i], s * K);
+                    f = __builtin_bit_cast(half8, cbm[c0]);
+                    if constexpr (K == 2) {
+                        const uint32_t c1 = seg_code<BITS, NW>(cw[i], s * K + 1);
+                        f = f + __builtin_bit_cast(half8, cbm[(1u << BITS) + c1]);
+                    }
                 }
                 a[s] = ok ? f : half8{};
             }
@@ -639,17 +687,26 @@ hipError_t launch_kw(const Problem &p) {
 bool kw_fits(const Problem &p) {
     const int64_t G = p.in / kGroup;
     if (p.batch > 32 || G % 8) return false;
+    // 8 codebooks of 8-bit codes: 32 KiB of LDS per matrix, one matrix only
+    if (p.K == 8 && p.segs.n > 1) return false;
     const int nt = p.batch > 16 ? 2 : 1;
     const int64_t maxu = ((G + 31) / 32 + kKw - 1) / kKw;
-    const int lim = p.B == 8 ? (p.K == 1 ? kw_max_units<1, 8>(nt) : kw_max_units<2, 8>(nt))
-                             : (p.K == 1 ? kw_max_units<1, 16>(nt) : kw_max_units<2, 16>(nt));
+    int lim = 0;
+    if (p.B == 8)
+        lim = p.K == 1 ? kw_max_units<1, 8>(nt) : p.K == 2 ? kw_max_units<2, 8>(nt)
+            : p.K == 4 ? kw_max_units<4, 8>(nt) : kw_max_units<8, 8>(nt);
+    else
+        lim = p.K == 1 ? kw_max_units<1, 16>(nt) : kw_max_units<2, 16>(nt);
     return maxu <= lim;
 }
 
 }  // namespace
 
 bool mfma_supported(const Problem &p) {
-    if (!((p.K == 1 || p.K == 2) && (p.B == 8 || p.B == 16))) return false;
+    // K in {1, 2} for either code width; 4 and 8 codebooks of 8-bit codes
+    const bool kb = ((p.K == 1 || p.K == 2) && (p.B == 8 || p.B == 16)) ||
+                    ((p.K == 4 || p.K == 8) && p.B == 8);
+    if (!kb) return false;
     if (p.batch < 1) return false;
     const int64_t G = p.in / kGroup;
     if (G % 4) return false;
@@ -670,7 +727,9 @@ size_t mfma_workspace_bytes(const Problem &p) {
 // workspace: KSPLIT x batch x T fp32 partial tiles (unused when KSPLIT = 1)
 hipError_t launch_mfma(const Problem &p, void *workspace) {
     if (kw_fits(p)) {
-        if (p.B == 8) return p.K == 1 ? launch_kw<1, 8>(p) : launch_kw<2, 8>(p);
+        if (p.B == 8)
+            return p.K == 1 ? launch_kw<1, 8>(p) : p.K == 2 ? launch_kw<2, 8>(p)
+                 : p.K == 4 ? launch_kw<4, 8>(p) : launch_kw<8, 8>(p);
         return p.K == 1 ? launch_kw<1, 16>(p) : launch_kw<2, 16>(p);
     }
     Segs segs = p.segs;
@@ -678,7 +737,9 @@ hipError_t launch_mfma(const Problem &p, void *workspace) {
     float *partial = c.ksplit > 1 ? static_cast<float *>(workspace) : nullptr;
     hipError_t e;
     if (p.B == 8)
-        e = p.K == 1 ? launch_kb<1, 8>(p, c, segs, partial) : launch_kb<2, 8>(p, c, segs, partial);
+        e = p.K == 1 ? launch_kb<1, 8>(p, c, segs, partial)
+          : p.K == 2 ? launch_kb<2, 8>(p, c, segs, partial)
+          : p.K == 4 ? launch_kb<4, 8>(p, c, segs, partial) : launch_kb<8, 8>(p, c, segs, partial);
     else
         e = p.K == 1 ? launch_kb<1, 16>(p, c, segs, partial) : launch_kb<2, 16>(p, c, segs, partial);
     if (e != hipSuccess || c.ksplit == 1) return e;

@@ -153,7 +153,7 @@ def main():
                          "copy: device-to-device copies of 64 and 256 MiB (reference "
                          "transfers that calibrate the FETCH_SIZE / WRITE_SIZE counters)")
     ap.add_argument("--batch", type=int, default=16, help="tokens for --workload layer7b")
-    ap.add_argument("--scheme", default="2x8", choices=["2x8", "1x16"],
+    ap.add_argument("--scheme", default="2x8", choices=["2x8", "1x16", "2x16", "8x8", "4x8"],
                     help="scheme for --workload layer7b")
     ap.add_argument("--linears", default="q,k,v,o,gate,up,down",
                     help="comma-separated subset of the layer's linears for --workload layer7b")
@@ -350,7 +350,7 @@ MFMA_PEAK_FP16_TFLOPS = 2500.0
 def layer_bench(args, torch, np, aq, synth):
     """The seven linears of a Llama-2-7B layer at one batch size through aqlm_gemm
     (matrix cores from batch 16), rotating over copies larger than 2x the Infinity Cache."""
-    K, B = (2, 8) if args.scheme == "2x8" else (1, 16)
+    K, B = (int(v) for v in args.scheme.split("x"))
     batch = args.batch
     wanted = [n.strip() for n in args.linears.split(",") if n.strip()]
     unknown = set(wanted) - {n for n, _, _ in LAYER_7B}

@@ -73,7 +73,8 @@ typedef enum {
     AQLM_VARIANT_LDS = 2,     /* B = 8: codebooks staged in LDS, gather + fp32 dot, batch<=8 */
     AQLM_VARIANT_LUT = 3,     /* K = 2, B = 8, batch 1: per-group codebook.x lookup tables   */
     AQLM_VARIANT_L2 = 4,      /* B = 16: codebook gathered through L2, batch <= 8            */
-    AQLM_VARIANT_MFMA = 5,    /* decode to fp16 fragments + fp16 matrix cores, any batch     */
+    AQLM_VARIANT_MFMA = 5,    /* decode to fp16 fragments + fp16 matrix cores, any batch;
+                                 K in {1,2}, or K in {4,8} with B = 8; in/8 a multiple of 4 */
     AQLM_VARIANT_SPLIT = 6    /* B = 16, packed codebooks: one codebook position per CU,
                                  batch <= 16 (aqlm_gemv_packed only)                       */
 } aqlm_variant_t;
@@ -163,7 +164,7 @@ aqlm_status_t aqlm_unpack_codes(const void *packed, void *codes, int64_t out_fea
  * - 16-bit codes, K in {1,2}, batch <= 4: the position-split kernel
  *   (AQLM_VARIANT_SPLIT): the K*8 codebook planes live in the LDS of K*8
  *   workgroups per row range and a second kernel adds their partial sums.
- * - 16-bit codes, K in {1,2}, batch 5..16, in_features a multiple of 64,
+ * - 16-bit codes, batch 5..16 (K = 1) or 5..8 (K = 2), in_features a multiple of 64,
  *   16-byte aligned pointers: the same planes on the matrix cores (a small
  *   kernel first writes x transposed by position into the workspace).
  * - 2x8, batch 1, 16-byte aligned pointers: the lookup-table kernel reading

@@ -577,3 +577,32 @@ def test_grouped_capture_small_workspace(aq, orc, warm):
             for m, p in enumerate(ps):
                 check_y(ys[m], orc.gemv(p["codes"], p["codebooks"], p["x"], 2, 8),
                         f"capture {warm} {m}")
+
+
+@pytest.mark.parametrize("case", [
+    # out, in, K, B, batch: persistent kernel (in <= 4096, batch <= 16), tiled kernel otherwise
+    (160, 1024, 4, 8, 16), (160, 1024, 8, 8, 16), (160, 1024, 4, 8, 17), (160, 1024, 8, 8, 33),
+    (300, 4160, 4, 8, 16), (257, 2048, 8, 8, 128), (96, 512, 4, 8, 64), (33, 64, 8, 8, 20),
+], ids=lambda c: "x".join(map(str, c)))
+def test_mfma_four_and_eight_codebooks(aq, orc, case):
+    """K = 4 and 8 codebooks of 8-bit codes on the matrix cores: each group's fp32 fold
+    rounded once to fp16 (the dequantized fp16 W) times x."""
+    out, in_, K, B, batch = case
+    p = synth.make_problem(out, in_, K, B, batch=batch, sigma_cb=0.01, config=2400 + out + K + batch)
+    codes, cb, x = _dev(p)
+    assert aq.variant_supported("mfma", codes, cb, x)
+    assert aq.selected_variant(codes, cb, x, gemm=True) == "mfma"
+    yref = orc.gemv(p["codes"], p["codebooks"], p["x"], K, B)
+    check_y(aq.gemm(codes, cb, x), yref, f"gemm {case}")
+
+
+@pytest.mark.parametrize("case", [((100, 257), 1024, 4, 8, 16), ((64, 33), 512, 8, 8, 16),
+                                  ((64, 33, 17), 1024, 4, 8, 40)],
+                         ids=lambda c: "-".join(map(str, c[0])) + "x" + "x".join(map(str, c[1:])))
+def test_grouped_four_and_eight_codebooks(aq, orc, case):
+    outs, in_, K, B, batch = case
+    ps = _group(outs, in_, K, B, batch, 2500 + sum(outs) + K)
+    dev = [_dev(p) for p in ps]
+    ys = aq.gemm_grouped([d[0] for d in dev], [d[1] for d in dev], dev[0][2])
+    for m, (y, p) in enumerate(zip(ys, ps)):
+        check_y(y, orc.gemv(p["codes"], p["codebooks"], p["x"], K, B), f"grouped {case} {m}")
