@@ -26,7 +26,8 @@ __all__ = ["gemv", "gemm", "gemv_variant", "gemv_packed", "pack_codebooks", "unp
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libaqlm_mi355x.so")
 
-VARIANTS = {"auto": 0, "generic": 1, "lds": 2, "lut": 3, "l2": 4, "mfma": 5, "split": 6}
+VARIANTS = {"auto": 0, "generic": 1, "lds": 2, "lut": 3, "l2": 4, "mfma": 5, "split": 6,
+            "prefill": 7}
 _STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "HIP error"}
 
 

@@ -17,6 +17,11 @@ namespace {
 
 constexpr int kGroup = 8;
 constexpr int kMfmaMinBatchDefault = 16;
+// Measured on MI355X (7B layer linears, canonical weights): the prefill path overtakes the
+// matrix-core kernels at batch 256 for 16-bit codes (decoding a 1 MiB codebook through
+// L2 per token tile costs more) and at 1024 for 8-bit codes with K <= 2.
+constexpr int kPrefillMinBatch16 = 256;
+constexpr int kPrefillMinBatch8 = 1024;
 
 thread_local char g_last_error[256] = "";
 
@@ -41,7 +46,18 @@ int forced_variant() {
     if (!std::strcmp(v, "l2")) return AQLM_VARIANT_L2;
     if (!std::strcmp(v, "mfma")) return AQLM_VARIANT_MFMA;
     if (!std::strcmp(v, "split")) return AQLM_VARIANT_SPLIT;
+    if (!std::strcmp(v, "prefill")) return AQLM_VARIANT_PREFILL;
     return AQLM_VARIANT_AUTO;
+}
+
+// batch from which aqlm_gemm decodes W once and runs one library GEMM
+// (AQLM_PREFILL_MIN_BATCH overrides)
+int prefill_min_batch(const aqlm::Problem &p) {
+    const int def = (p.B == 16 || p.K >= 4) ? kPrefillMinBatch16 : kPrefillMinBatch8;
+    const char *v = std::getenv("AQLM_PREFILL_MIN_BATCH");
+    if (!v || !*v) return def;
+    const int n = std::atoi(v);
+    return n >= 1 ? n : def;
 }
 
 int mfma_min_batch() {
@@ -144,6 +160,7 @@ bool supported_one(int variant, const aqlm::Problem &p) {
         case AQLM_VARIANT_LUT: return aqlm::lut_supported(p);
         case AQLM_VARIANT_L2: return aqlm::l2_supported(p);
         case AQLM_VARIANT_MFMA: return aqlm::mfma_supported(p);
+        case AQLM_VARIANT_PREFILL: return aqlm::mfma_supported(p);
         default: return false;
     }
 }
@@ -151,6 +168,8 @@ bool supported_one(int variant, const aqlm::Problem &p) {
 int choose(bool gemm, const aqlm::Problem &p) {
     const int forced = forced_variant();
     if (forced != AQLM_VARIANT_AUTO && supported(forced, p)) return forced;
+    if (gemm && p.batch >= prefill_min_batch(p) && supported(AQLM_VARIANT_PREFILL, p))
+        return AQLM_VARIANT_PREFILL;
     if (gemm && p.batch >= mfma_min_batch() && supported(AQLM_VARIANT_MFMA, p))
         return AQLM_VARIANT_MFMA;
     if (supported(AQLM_VARIANT_LUT, p)) return AQLM_VARIANT_LUT;
@@ -226,7 +245,8 @@ aqlm_status_t run(int variant, const aqlm::Problem &p) {
                      aqlm_variant_name(variant), (long long)p.out, (long long)p.in, p.K, p.B,
                      p.batch);
     // kernels without a matrix table run once per matrix
-    if (p.segs.n > 1 && (variant == AQLM_VARIANT_LDS || variant == AQLM_VARIANT_GENERIC)) {
+    if (p.segs.n > 1 && (variant == AQLM_VARIANT_LDS || variant == AQLM_VARIANT_GENERIC ||
+                         variant == AQLM_VARIANT_PREFILL)) {
         for (int m = 0; m < p.segs.n; ++m) {
             const aqlm_status_t st = run(variant, segment(p, m));
             if (st != AQLM_OK) return st;
@@ -283,6 +303,19 @@ aqlm_status_t run(int variant, const aqlm::Problem &p) {
                 }
             }
             e = aqlm::launch_mfma(p, ws);
+            break;
+        }
+        case AQLM_VARIANT_PREFILL: {
+            void *ws = nullptr;
+            e = get_workspace(p.stream, aqlm::prefill_workspace_bytes(p), &ws);
+            if (e != hipSuccess) break;
+            if (!ws) {
+                // capturing stream without a large enough workspace: the matrix cores
+                if (log_enabled())
+                    std::fprintf(stderr, "[aqlm] prefill: no workspace on a capturing stream\n");
+                return run(AQLM_VARIANT_MFMA, p);
+            }
+            e = aqlm::launch_prefill(p, ws);
             break;
         }
         default:
@@ -464,6 +497,7 @@ const char *aqlm_variant_name(int variant) {
         case AQLM_VARIANT_L2: return "l2";
         case AQLM_VARIANT_MFMA: return "mfma";
         case AQLM_VARIANT_SPLIT: return "split";
+        case AQLM_VARIANT_PREFILL: return "prefill";
         default: return "unknown";
     }
 }

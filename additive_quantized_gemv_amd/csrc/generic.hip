@@ -184,6 +184,47 @@ hipError_t launch_generic(const Problem &p) {
     return hipGetLastError();
 }
 
+// Dense fp16 W for the prefill path: one thread per group, the K codebook vectors read as
+// 16-byte loads, the fp32 left fold rounded once (the value dequantize_kernel writes with
+// w_fp16), one 16-byte store.  W is [out][in] row-major.
+template <int B>
+__global__ void __launch_bounds__(256)
+dequant16_kernel(const void *__restrict__ codes, const uint4 *__restrict__ cb,
+                 uint4 *__restrict__ W, int64_t ngroups, int K) {
+    for (int64_t g = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; g < ngroups;
+         g += int64_t(gridDim.x) * blockDim.x) {
+        float w[8];
+        for (int k = 0; k < K; ++k) {
+            const uint32_t c = B == 8 ? uint32_t(static_cast<const uint8_t *>(codes)[g * K + k])
+                                      : uint32_t(static_cast<const uint16_t *>(codes)[g * K + k]);
+            const uint4 v = cb[(int64_t(k) << B) + c];
+            const uint32_t h[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                const float f = h2f(uint16_t(h[t >> 1] >> (16 * (t & 1))));
+                w[t] = (k == 0) ? f : w[t] + f;
+            }
+        }
+        uint32_t o[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[i] = uint32_t(f2h_bits(w[2 * i])) | (uint32_t(f2h_bits(w[2 * i + 1])) << 16);
+        W[g] = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+}
+
+hipError_t launch_dequant16(const Problem &p, void *W) {
+    const int64_t n = p.out * (p.in / kGroup);
+    int64_t blocks = (n + 255) / 256;
+    if (blocks > 8192) blocks = 8192;
+    if (p.B == 8)
+        hipLaunchKernelGGL(dequant16_kernel<8>, dim3(unsigned(blocks)), dim3(256), 0, p.stream, p.codes,
+                           static_cast<const uint4 *>(p.codebooks), static_cast<uint4 *>(W), n, p.K);
+    else
+        hipLaunchKernelGGL(dequant16_kernel<16>, dim3(unsigned(blocks)), dim3(256), 0, p.stream, p.codes,
+                           static_cast<const uint4 *>(p.codebooks), static_cast<uint4 *>(W), n, p.K);
+    return hipGetLastError();
+}
+
 hipError_t launch_dequantize(const Problem &p, void *W, int w_fp16) {
     const int64_t n = p.out * (p.in / kGroup);
     int64_t blocks = (n + 255) / 256;

@@ -48,6 +48,13 @@ hipError_t launch_copy_bytes(const void *src, void *dst, int64_t n, hipStream_t 
 
 // Dense W (fp32 when w_fp16 == 0, fp16 otherwise).
 hipError_t launch_dequantize(const Problem &p, void *W, int w_fp16);
+// dense fp16 W ([out][in], 16-byte aligned) for the prefill path; same bits as
+// launch_dequantize with w_fp16
+hipError_t launch_dequant16(const Problem &p, void *W);
+// prefill: W decoded once into the workspace, then one fp16 GEMM (hipBLASLt) with fp32
+// accumulation; workspace = W (out*in fp16, 256-byte aligned) + the GEMM's own scratch
+size_t prefill_workspace_bytes(const Problem &p);
+hipError_t launch_prefill(const Problem &p, void *workspace);
 
 // Gather kernel for 8-bit codes (codebooks staged in LDS), batch <= 8.
 bool gather_supported(const Problem &p);

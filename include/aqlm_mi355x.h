@@ -75,8 +75,11 @@ typedef enum {
     AQLM_VARIANT_L2 = 4,      /* B = 16: codebook gathered through L2, batch <= 8            */
     AQLM_VARIANT_MFMA = 5,    /* decode to fp16 fragments + fp16 matrix cores, any batch;
                                  K in {1,2}, or K in {4,8} with B = 8; in/8 a multiple of 4 */
-    AQLM_VARIANT_SPLIT = 6    /* B = 16, packed codebooks: one codebook position per CU,
+    AQLM_VARIANT_SPLIT = 6,   /* B = 16, packed codebooks: one codebook position per CU,
                                  batch <= 16 (aqlm_gemv_packed only)                       */
+    AQLM_VARIANT_PREFILL = 7  /* prefill-size batches: W decoded once to fp16 in the
+                                 workspace, one hipBLASLt GEMM (fp32 accumulation); the
+                                 same K, B and shapes as AQLM_VARIANT_MFMA               */
 } aqlm_variant_t;
 
 /*
@@ -91,7 +94,11 @@ aqlm_status_t aqlm_gemv(const void *codes, const void *codebooks, const void *x,
 
 /*
  * Same product and arguments as aqlm_gemv; for batch >= 16 it uses the
- * dequantize-to-fp16 + MFMA kernel, below that it behaves as aqlm_gemv.
+ * dequantize-to-fp16 + MFMA kernels, below that it behaves as aqlm_gemv.  From
+ * prefill-size batches (256 for 16-bit codes or K >= 4, 1024 otherwise;
+ * AQLM_PREFILL_MIN_BATCH overrides) W is instead decoded once into the stream's workspace as
+ * dense fp16 (out*in*2 bytes plus 64 MiB of GEMM scratch, kept like every
+ * workspace) and multiplied by one hipBLASLt fp16 GEMM with fp32 accumulation.
  */
 aqlm_status_t aqlm_gemm(const void *codes, const void *codebooks, const void *x, void *y,
                         int64_t out_features, int64_t in_features, int K, int B, int batch,

@@ -606,3 +606,59 @@ def test_grouped_four_and_eight_codebooks(aq, orc, case):
     ys = aq.gemm_grouped([d[0] for d in dev], [d[1] for d in dev], dev[0][2])
     for m, (y, p) in enumerate(zip(ys, ps)):
         check_y(y, orc.gemv(p["codes"], p["codebooks"], p["x"], K, B), f"grouped {case} {m}")
+
+
+@pytest.mark.parametrize("case", [
+    # out, in, K, B, batch (aqlm_gemm from batch 256 (16-bit codes, K >= 4) or 1024: W decoded
+    # once, one library GEMM)
+    (300, 4096, 2, 8, 1024), (257, 1024, 1, 16, 600), (96, 512, 4, 8, 513), (1000, 2048, 2, 8, 1100),
+    (64, 256, 8, 8, 300), (130, 512, 2, 16, 256),
+], ids=lambda c: "x".join(map(str, c)))
+def test_prefill(aq, orc, case):
+    out, in_, K, B, batch = case
+    p = synth.make_problem(out, in_, K, B, batch=batch, sigma_cb=0.02, config=2600 + out + batch)
+    codes, cb, x = _dev(p)
+    assert aq.selected_variant(codes, cb, x, gemm=True) == "prefill"
+    yref = orc.gemv(p["codes"], p["codebooks"], p["x"], K, B)
+    y = aq.gemm(codes, cb, x)
+    check_y(y, yref, f"prefill {case}")
+    assert bool((aq.gemm(codes, cb, x) == y).all())
+
+
+def test_prefill_forced_small_batch(aq, orc):
+    """The prefill variant at any batch (named), and its grouped form (matrix by matrix)."""
+    for batch in (1, 3, 16):
+        p = synth.make_problem(200, 1024, 2, 8, batch=batch, sigma_cb=0.02, config=2700 + batch)
+        codes, cb, x = _dev(p)
+        yref = orc.gemv(p["codes"], p["codebooks"], p["x"], 2, 8)
+        check_y(aq.gemv_variant("prefill", codes, cb, x), yref, f"prefill forced b{batch}")
+    ps = _group((300, 17, 64), 1024, 1, 16, 512, 2800)
+    dev = [_dev(p) for p in ps]
+    ys = aq.gemm_grouped([d[0] for d in dev], [d[1] for d in dev], dev[0][2])
+    for m, (y, p) in enumerate(zip(ys, ps)):
+        check_y(y, orc.gemv(p["codes"], p["codebooks"], p["x"], 1, 16), f"prefill grouped {m}")
+
+
+@pytest.mark.parametrize("warm", ["warm", "cold"])
+def test_prefill_graph_replay(aq, orc, warm):
+    """Captured with a workspace (prefill in the graph) and without one (matrix cores)."""
+    import torch
+    p = synth.make_problem(512, 2048, 2, 8, batch=1024, sigma_cb=0.02, config=2900)
+    codes, cb, x = _dev(p)
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        eager = aq.gemm(codes, cb, x).clone() if warm == "warm" else None
+        y = torch.empty((1024, 512), dtype=torch.float16, device="cuda")
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            aq.gemm(codes, cb, x, out=y)
+        yref = orc.gemv(p["codes"], p["codebooks"], p["x"], 2, 8)
+        for _ in range(3):
+            y.fill_(3.0)
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            check_y(y, yref, f"prefill graph {warm}")
+            if eager is not None:
+                assert bool((y == eager).all())
