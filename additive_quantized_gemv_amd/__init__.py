@@ -95,6 +95,10 @@ def _load():
     lib.aqlm_status_string.restype = ctypes.c_char_p
     lib.aqlm_variant_name.argtypes = [ci]
     lib.aqlm_variant_name.restype = ctypes.c_char_p
+    lib.aqlm_cpu_gemv.argtypes = [vp, vp, vp, vp, i64, i64, ci, ci, ci, ci]
+    lib.aqlm_cpu_gemv.restype = ci
+    lib.aqlm_cpu_isa.argtypes = []
+    lib.aqlm_cpu_isa.restype = ctypes.c_char_p
     _lib = lib
     return lib
 
@@ -269,6 +273,45 @@ def gemv_grouped(codes, codebooks, x, out=None):
 def gemm_grouped(codes, codebooks, x, out=None):
     """gemv_grouped with the matrix-core kernels from batch 16 (as gemm)."""
     return _grouped_canonical("aqlm_gemm_grouped", codes, codebooks, x, out)
+
+
+def cpu_gemv(codes, codebooks, x, out=None, threads: int = 0):
+    """y = W x on the host cores from host (CPU) tensors, same layouts as gemv.
+
+    Token generation without a GPU: lookup tables for 8-bit codes, F16C decode for
+    16-bit codes, rows split over ``threads`` OpenMP threads (0: the OpenMP default);
+    the result does not depend on the thread count.
+    """
+    torch = _torch()
+    lib = _load()
+    if codes.dim() != 3:
+        raise ValueError("codes must be [out][in/8][K]")
+    K, B = codes.shape[2], _bits_of(codes)
+    if codebooks.dtype != torch.float16 or tuple(codebooks.shape) != (K, 1 << B, 8):
+        raise ValueError(f"codebooks must be float16 {[K, 1 << B, 8]}")
+    if x.dtype != torch.float16:
+        raise TypeError("x must be float16")
+    x2 = x.unsqueeze(0) if x.dim() == 1 else x
+    if x2.dim() != 2 or x2.shape[1] != codes.shape[1] * 8:
+        raise ValueError("x must be [batch][in] with in = 8 * codes.shape[1]")
+    for t, n in ((codes, "codes"), (codebooks, "codebooks"), (x2, "x")):
+        if t.is_cuda:
+            raise ValueError(f"{n} must be a host tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{n} must be contiguous")
+    out_f, in_f, batch = codes.shape[0], codes.shape[1] * 8, x2.shape[0]
+    y = out if out is not None else torch.empty((batch, out_f), dtype=torch.float16)
+    if (y.dtype != torch.float16 or tuple(y.shape) != (batch, out_f) or not y.is_contiguous()
+            or y.is_cuda):
+        raise ValueError("out must be a contiguous float16 [batch][out] host tensor")
+    _check(lib.aqlm_cpu_gemv(codes.data_ptr(), codebooks.data_ptr(), x2.data_ptr(), y.data_ptr(),
+                             out_f, in_f, K, B, batch, int(threads)), "aqlm_cpu_gemv")
+    return y if x.dim() == 2 else y[0]
+
+
+def cpu_isa() -> str:
+    """Vector instruction set the host kernel uses here ("avx512", "avx2" or "none")."""
+    return _load().aqlm_cpu_isa().decode()
 
 
 def gemv_packed_grouped(weights, x, out=None):

@@ -147,12 +147,16 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--warm", action="store_true", help="also time cache-resident (no rotation)")
-    ap.add_argument("--workload", default="mlp", choices=["mlp", "layer7b", "copy"],
+    ap.add_argument("--workload", default="mlp", choices=["mlp", "layer7b", "copy", "cpu"],
                     help="mlp: the batch-1 MLP products (default, the headline line); "
                          "layer7b: the seven linears of a Llama-2-7B layer through aqlm_gemm; "
+                         "cpu: the mlp products on the host cores (aqlm_cpu_gemv, no GPU); "
                          "copy: device-to-device copies of 64 and 256 MiB (reference "
                          "transfers that calibrate the FETCH_SIZE / WRITE_SIZE counters)")
-    ap.add_argument("--batch", type=int, default=16, help="tokens for --workload layer7b")
+    ap.add_argument("--batch", type=int, default=16,
+                    help="tokens for --workload layer7b (and cpu, where the default is 1)")
+    ap.add_argument("--threads", type=int, default=0,
+                    help="--workload cpu: host threads (0 = the OpenMP default)")
     ap.add_argument("--scheme", default="2x8", choices=["2x8", "1x16", "2x16", "8x8", "4x8"],
                     help="scheme for --workload layer7b")
     ap.add_argument("--linears", default="q,k,v,o,gate,up,down",
@@ -180,6 +184,9 @@ def main():
     import additive_quantized_gemv_amd as aq
     from additive_quantized_gemv_amd import synth
 
+    if args.workload == "cpu":
+        aq._load()
+        return cpu_kernel_bench(args, torch, np, aq, synth)
     if not torch.cuda.is_available():
         print("no GPU available", file=sys.stderr)
         sys.exit(1)
@@ -340,6 +347,118 @@ def copy_bench(args, torch):
         del a, b
     print(json.dumps({"workload": "device copy (counter calibration)", "copies": res}),
           flush=True)
+
+
+def host_l3_bytes():
+    """Total L3 of the host (sum over distinct L3 instances), 0 if unknown."""
+    seen, total = set(), 0
+    base = "/sys/devices/system/cpu"
+    try:
+        for cpu in os.listdir(base):
+            idx = os.path.join(base, cpu, "cache", "index3")
+            if not re.fullmatch(r"cpu\d+", cpu) or not os.path.isdir(idx):
+                continue
+            with open(os.path.join(idx, "shared_cpu_list")) as f:
+                key = f.read().strip()
+            if key in seen:
+                continue
+            seen.add(key)
+            with open(os.path.join(idx, "size")) as f:
+                v = f.read().strip()
+            total += int(v[:-1]) << (10 if v.endswith("K") else 20) if v[-1] in "KM" else int(v)
+    except OSError:
+        return 0
+    return total
+
+
+def cpu_kernel_bench(args, torch, np, aq, synth):
+    """The four MLP products on the host cores through aqlm_cpu_gemv, the oracle timed
+    beside it on the same bytes.  Copies rotate so that the weights stream from DRAM
+    (rotation set > 2x the host's L3)."""
+    from oracle import Oracle
+    batch = 1 if args.batch == 16 and "--batch" not in sys.argv else args.batch
+    per_copy = sum(algorithmic_bytes(o, i, K, B, batch) for _, o, i, K, B in WORKLOAD)
+    l3 = host_l3_bytes()
+    copies = args.copies or max(2, math.ceil(2 * max(l3, 32 << 20) / per_copy))
+    sets = []
+    for r in range(copies):
+        entry = []
+        for name, out, in_, K, B in WORKLOAD:
+            p = synth.make_problem(out, in_, K, B, batch=batch, sigma_cb=SIGMA_CB,
+                                   config=CONFIG_IDS[B] * 10 + (0 if out > in_ else 1), copy=r)
+            codes = torch.from_numpy(p["codes"] if B == 8 else p["codes"].view(np.int16))
+            entry.append((codes, torch.from_numpy(p["codebooks"]), torch.from_numpy(p["x"]), p))
+        sets.append(entry)
+    ys = [torch.empty((batch, out), dtype=torch.float16) for _, out, _, _, _ in WORKLOAD]
+    print(f"[bench] cpu kernel ({aq.cpu_isa()}), {copies} rotation copies, "
+          f"{per_copy * copies / 2**20:.0f} MiB", file=sys.stderr, flush=True)
+    steps = args.steps if "--steps" in sys.argv else 50
+    warmup = args.warmup if "--warmup" in sys.argv else 3
+    per = [0.0] * len(WORKLOAD)
+    for s in range(warmup + steps):
+        r = s % copies
+        for i in range(len(WORKLOAD)):
+            codes, cb, x, _ = sets[r][i]
+            t0 = time.perf_counter()
+            aq.cpu_gemv(codes, cb, x, out=ys[i], threads=args.threads)
+            if s >= warmup:
+                per[i] += time.perf_counter() - t0
+    dt = sum(per) / steps
+    # parity of the last step's outputs against the oracle (copy of that step)
+    orc = Oracle()
+    r = (warmup + steps - 1) % copies
+    max_err = 0.0
+    for (name, out, in_, K, B), (_, _, _, p), y in zip(WORKLOAD, sets[r], ys):
+        yref = orc.gemv(p["codes"], p["codebooks"], p["x"], K, B)
+        e = np.max(np.abs(y.float().numpy() - yref), axis=1) / (np.max(np.abs(yref), axis=1) + 1e-6)
+        max_err = max(max_err, float(e.max()))
+    base = None
+    if not args.no_cpu_baseline:
+        t0, reps, done = time.perf_counter(), 0, 0
+        while True:
+            for (name, out, in_, K, B), (_, _, _, p) in zip(WORKLOAD, sets[0]):
+                orc.gemv(p["codes"], p["codebooks"], p["x"], K, B)
+                done += algorithmic_bytes(out, in_, K, B, batch)
+            reps += 1
+            if time.perf_counter() - t0 >= args.cpu_seconds:
+                break
+        ot = time.perf_counter() - t0
+        base = {"value": round(done / ot / 1e9, 4), "unit": "GB/s", "cores": orc.max_threads(),
+                "kind": "oracle",
+                "sample": f"full decode to fp32 W + double matvec of the four products of one "
+                          f"step (copy 0), repeated {reps}x in {ot:.1f} s",
+                "ms_per_step": round(ot / reps * 1e3, 2)}
+    # context: dense fp16 and fp32 W x on the same cores (torch), two copies rotating
+    dense = {}
+    if args.threads > 0:
+        torch.set_num_threads(args.threads)
+    for name, out, in_, K, B in WORKLOAD:
+        for dt_name, dt_t in (("fp16", torch.float16), ("fp32", torch.float32)):
+            Ws = [torch.randn(out, in_).to(dt_t) for _ in range(2)]
+            xv = torch.randn(in_).to(dt_t)
+            for W in Ws:
+                W @ xv
+            t0 = time.perf_counter()
+            for it in range(10):
+                Ws[it % 2] @ xv
+            dense[f"{name.split()[1]} {dt_name}"] = round((time.perf_counter() - t0) / 10 * 1e6, 1)
+            del Ws
+    nt = args.threads if args.threads > 0 else torch.get_num_threads()
+    result = {"metric": "AQLM GEMV on the host cores: algorithmic GB/s, 2x8 & 1x16 MLP shapes",
+              "value": round(per_copy / dt / 1e9, 3), "unit": "GB/s", "n_gpus": 0,
+              "steps": steps, "warmup": warmup, "ms_per_step": round(dt * 1e3, 3),
+              "higher_is_better": True, "scaling": "strong", "vs_baseline": None,
+              "dtype": "f32", "data": "synthetic",
+              "config": {"workload": f"Llama-2-7B MLP shapes 11008x4096 and 4096x11008, "
+                                     f"2x8 and 1x16, batch {batch}, host cores",
+                         "isa": aq.cpu_isa(), "threads": nt, "rotation_copies": copies,
+                         "host_l3_mib": round(l3 / 2**20, 1)},
+              "per_product_us": {name: round(t / steps * 1e6, 1)
+                                 for (name, *_), t in zip(WORKLOAD, per)},
+              "max_rel_err_vs_oracle": max_err,
+              "dense_torch_us": dense,
+              "cpu_baseline": base}
+    print(json.dumps(result), flush=True)
 
 
 LAYER_7B = [("q", 4096, 4096), ("k", 4096, 4096), ("v", 4096, 4096), ("o", 4096, 4096),

@@ -48,7 +48,9 @@
  * object) returns AQLM_ERR_HIP; aqlm_last_error() then gives the HIP message.
  * Tuned kernels that cannot take a shape (rows not a multiple of 16 bytes,
  * unaligned pointers, too much LDS) are silently replaced by the generic
- * kernel; AQLM_ERR_UNSUPPORTED comes only from aqlm_gemv_variant.
+ * kernel; AQLM_ERR_UNSUPPORTED comes only from aqlm_gemv_variant, from
+ * aqlm_gemv_packed under capture without a workspace, and from aqlm_cpu_gemv on a
+ * host without AVX2.
  */
 #ifndef AQLM_MI355X_H
 #define AQLM_MI355X_H
@@ -210,6 +212,29 @@ aqlm_status_t aqlm_gemv_packed_grouped(int n, const void *const *packed_codes,
                                        void *const *y, const int64_t *out_features,
                                        int64_t in_features, int K, int B, int batch,
                                        void *stream);
+
+/*
+ * The same product on the host cores (token generation on the CPU): host pointers in
+ * the canonical layouts of aqlm_gemv, y [batch][out] fp16 written by the call, which
+ * returns when it is done.  fp32 arithmetic throughout (8-bit codes with K in {1,2,4}:
+ * per-group codebook.x lookup tables and AVX-512 / AVX2 gathers; 16-bit codes with K in
+ * {1,2}: F16C decode + FMA; anything else: scalar code), y rounded once to fp16; the
+ * result meets the same bar against the exact product as the GPU kernels and does not
+ * depend on `threads`.  threads <= 0: the OpenMP default.  AQLM_ERR_INVALID_ARGUMENT
+ * for a null pointer, a size < 1, in_features not a multiple of 8, K outside 1..8, B
+ * not 8 or 16 or out*in/8 or batch*in above 2^40 (no overlap check: y must not alias
+ * an input); AQLM_ERR_UNSUPPORTED on a host without AVX2, FMA and F16C.  No device is
+ * involved.
+ * (Page "Extreme Compression of Large Language Models via Additive Quantization",
+ * abstract: the method's token generation also runs on CPUs.)
+ */
+aqlm_status_t aqlm_cpu_gemv(const void *codes, const void *codebooks, const void *x, void *y,
+                            int64_t out_features, int64_t in_features, int K, int B, int batch,
+                            int threads);
+/* Instruction set the CPU kernel uses on this host: "avx512", "avx2" or "none".  The
+ * environment variable AQLM_CPU_ISA=avx2, read on each call, keeps an AVX-512 host on
+ * the AVX2 kernels. */
+const char *aqlm_cpu_isa(void);
 
 /* K*B/group bits per weight (bitrate formula of the decode section). */
 double aqlm_bits_per_weight(int K, int B, int group);
