@@ -3,15 +3,21 @@
 // Same product as aqlm_gemv (page "AQLM (Additive Quantization for LLMs)", section
 // "Niveau intermediaire": each 8-wide group of a row is the sum of K codebook
 // vectors), computed in fp32 from host memory:
-// * 8-bit codes (any K): a row's codes, read in memory order, form the element sequence
-//   e = j*K + k (group j, codebook k).  Per token, the table of element e holds
+// * decode (16-bit codes with K in {1, 2}; 8-bit codes with K = 1): the codebook vectors
+//   of two groups (AVX2: one) are converted to fp32 (F16C), summed over k and
+//   multiplied with x (FMA); a 1 MiB codebook is served by the core's L2.
+// * 8-bit codes with K = 2: a group's two code bytes, read as one little-endian 16-bit
+//   index c0 + 256*c1, select an entry of the pair codebook P[c0 + 256*c1] =
+//   C_0[c0] + C_1[c1] rounded once to fp16 (the fold the matrix-core kernels use),
+//   built per call (1 MiB); the product then runs as the 16-bit K = 1 decode.  Gathers
+//   are slow on some hosts; this needs one 16-byte load per group instead.
+// * 8-bit codes with K > 2: a row's codes, read in memory order, form the element
+//   sequence e = j*K + k (group j, codebook k).  Per token, the table of element e holds
 //   C_k[c] . x[8j .. 8j+7] for the 256 codes c (fp32, built once by all threads); a
 //   row's product is then the sum over its elements of T[e][code[e]]: 16 lookups per
-//   AVX-512 gather (AVX2: 8).  Each thread walks its rows slice by slice along e, so a
-//   slice's tables (kSliceElems KiB) stay in the core's L1 while its rows read them.
-// * 16-bit codes (K in {1, 2}): the codebook vectors of two groups (AVX2: one) are
-//   converted to fp32 (F16C) and multiplied with x (FMA); the 1 MiB codebook is served
-//   by the core's L2.
+//   AVX-512 gather (AVX2: 8).  Rows are walked in blocks whose codes stay in L2, and
+//   within a block slice by slice along e, so a slice's tables (kSliceElems KiB) stay
+//   in L1 while the block's rows read them.
 // * 16-bit codes with K > 2: plain scalar code, the fp32 fold then the dot.
 // The host needs AVX2, FMA and F16C (AVX-512 F/BW/VL is used where present).  Each row's
 // sum is accumulated in an order fixed by the row alone, so the result does not depend
@@ -215,40 +221,42 @@ void rows_lut_avx2(const uint8_t *codes, int64_t E, int64_t o0, int64_t o1, cons
 // ------------------------------------------------------------------ 16-bit codes: decode
 // Row o: two groups per step into one 16-lane fp32 vector; two accumulators (even and
 // odd steps) hide the FMA latency, added at the end; an odd last group is scalar.
-// groups j and j+1 of the row whose codes start at cr, folded, as 16 fp32 lanes
-template <int K>
+// groups j and j+1 of the row whose codes (type C, codebooks of `entries` vectors)
+// start at cr, folded, as 16 fp32 lanes
+template <int K, typename C>
 __attribute__((target("avx512f"), always_inline)) inline
-__m512 dec16_pair(const uint16_t *cr, const uint16_t *cb, int64_t j) {
+__m512 dec_pair(const C *cr, const uint16_t *cb, int64_t entries, int64_t j) {
     __m512 v = _mm512_setzero_ps();
     for (int k = 0; k < K; ++k) {
         const __m128i a = _mm_loadu_si128(reinterpret_cast<const __m128i *>(
-            cb + ((int64_t(k) << 16) + cr[j * K + k]) * kGroup));
+            cb + (k * entries + cr[j * K + k]) * kGroup));
         const __m128i b = _mm_loadu_si128(reinterpret_cast<const __m128i *>(
-            cb + ((int64_t(k) << 16) + cr[(j + 1) * K + k]) * kGroup));
+            cb + (k * entries + cr[(j + 1) * K + k]) * kGroup));
         v = _mm512_add_ps(v, _mm512_cvtph_ps(_mm256_inserti128_si256(_mm256_castsi128_si256(a), b, 1)));
     }
     return v;
 }
 
-template <int K>
+template <int K, typename C>
 __attribute__((target("avx512f")))
-float row_dec16_avx512(const uint16_t *codes, const uint16_t *cb, const float *xf, int64_t G, int64_t o) {
-    const uint16_t *cr = codes + o * G * K;
+float row_dec_avx512(const C *codes, const uint16_t *cb, int64_t entries, const float *xf, int64_t G,
+                     int64_t o) {
+    const C *cr = codes + o * G * K;
     __m512 acc0 = _mm512_setzero_ps(), acc1 = _mm512_setzero_ps();
     int64_t j = 0;
     for (; j + 4 <= G; j += 4) {
-        acc0 = _mm512_fmadd_ps(dec16_pair<K>(cr, cb, j), _mm512_loadu_ps(xf + j * kGroup), acc0);
-        acc1 = _mm512_fmadd_ps(dec16_pair<K>(cr, cb, j + 2), _mm512_loadu_ps(xf + (j + 2) * kGroup), acc1);
+        acc0 = _mm512_fmadd_ps(dec_pair<K>(cr, cb, entries, j), _mm512_loadu_ps(xf + j * kGroup), acc0);
+        acc1 = _mm512_fmadd_ps(dec_pair<K>(cr, cb, entries, j + 2), _mm512_loadu_ps(xf + (j + 2) * kGroup), acc1);
     }
     if (j + 2 <= G) {
-        acc0 = _mm512_fmadd_ps(dec16_pair<K>(cr, cb, j), _mm512_loadu_ps(xf + j * kGroup), acc0);
+        acc0 = _mm512_fmadd_ps(dec_pair<K>(cr, cb, entries, j), _mm512_loadu_ps(xf + j * kGroup), acc0);
         j += 2;
     }
     float s = _mm512_reduce_add_ps(_mm512_add_ps(acc0, acc1));
     if (j < G) {
         float w[8] = {};
         for (int k = 0; k < K; ++k) {
-            const uint16_t *v = cb + ((int64_t(k) << 16) + cr[j * K + k]) * kGroup;
+            const uint16_t *v = cb + (k * entries + cr[j * K + k]) * kGroup;
             for (int t = 0; t < 8; ++t) w[t] += h2f(v[t]);
         }
         for (int t = 0; t < 8; ++t) s += w[t] * xf[j * kGroup + t];
@@ -256,14 +264,15 @@ float row_dec16_avx512(const uint16_t *codes, const uint16_t *cb, const float *x
     return s;
 }
 
-template <int K>
-float row_dec16_avx2(const uint16_t *codes, const uint16_t *cb, const float *xf, int64_t G, int64_t o) {
-    const uint16_t *cr = codes + o * G * K;
+template <int K, typename C>
+float row_dec_avx2(const C *codes, const uint16_t *cb, int64_t entries, const float *xf, int64_t G,
+                   int64_t o) {
+    const C *cr = codes + o * G * K;
     auto one = [&](int64_t j) {
         __m256 v = _mm256_setzero_ps();
         for (int k = 0; k < K; ++k)
             v = _mm256_add_ps(v, _mm256_cvtph_ps(_mm_loadu_si128(reinterpret_cast<const __m128i *>(
-                                     cb + ((int64_t(k) << 16) + cr[j * K + k]) * kGroup))));
+                                     cb + (k * entries + cr[j * K + k]) * kGroup))));
         return v;
     };
     __m256 acc0 = _mm256_setzero_ps(), acc1 = _mm256_setzero_ps();
@@ -274,6 +283,26 @@ float row_dec16_avx2(const uint16_t *codes, const uint16_t *cb, const float *xf,
     }
     if (j < G) acc0 = _mm256_fmadd_ps(one(j), _mm256_loadu_ps(xf + j * kGroup), acc0);
     return hsum256(_mm256_add_ps(acc0, acc1));
+}
+
+// ------------------------------------------------------------------ 2x8: pair codebook
+// P[c0 + 256*c1][t] = fp16(C_0[c0][t] + C_1[c1][t]) for the c1 of c1_begin .. c1_end-1
+void pair_codebook(const uint16_t *cb, int c1_begin, int c1_end, uint16_t *P) {
+    for (int c1 = c1_begin; c1 < c1_end; ++c1) {
+        const __m256 b = _mm256_cvtph_ps(_mm_loadu_si128(reinterpret_cast<const __m128i *>(cb + (256 + c1) * kGroup)));
+        for (int c0 = 0; c0 < 256; ++c0) {
+            const __m256 a = _mm256_cvtph_ps(_mm_loadu_si128(reinterpret_cast<const __m128i *>(cb + c0 * kGroup)));
+            _mm_storeu_si128(reinterpret_cast<__m128i *>(P + (int64_t(c1) * 256 + c0) * kGroup),
+                             _mm256_cvtps_ph(_mm256_add_ps(a, b), _MM_FROUND_TO_NEAREST_INT));
+        }
+    }
+}
+
+template <int K, typename C>
+float row_dec(Isa isa, const C *codes, const uint16_t *cb, int64_t entries, const float *xf, int64_t G,
+              int64_t o) {
+    return isa == kAvx512 ? row_dec_avx512<K>(codes, cb, entries, xf, G, o)
+                          : row_dec_avx2<K>(codes, cb, entries, xf, G, o);
 }
 
 aqlm_status_t cpu_gemv(const void *codes_, const void *codebooks_, const void *x_, void *y_,
@@ -293,7 +322,13 @@ aqlm_status_t cpu_gemv(const void *codes_, const void *codebooks_, const void *x
     uint16_t *y = static_cast<uint16_t *>(y_);
     const Isa isa = detect();
     const int nt = threads > 0 ? threads : omp_get_max_threads();
-    const bool lut = B == 8;
+    const bool lut = B == 8 && K > 2;
+    const bool pair = B == 8 && K == 2;
+    std::vector<uint16_t> P(pair ? size_t(65536) * kGroup : 0);
+    if (pair) {
+#pragma omp parallel for num_threads(nt) schedule(static)
+        for (int c1 = 0; c1 < 256; c1 += 16) pair_codebook(cb, c1, c1 + 16, P.data());
+    }
 
     std::vector<float> xf(static_cast<size_t>(in));
     std::vector<float> cbt(lut ? size_t(K) * 8 * 256 : 0);
@@ -324,12 +359,14 @@ aqlm_status_t cpu_gemv(const void *codes_, const void *codebooks_, const void *x
             } else {
                 for (int64_t o = o0; o < o1; ++o) {
                     float s;
-                    if (K <= 2 && isa == kAvx512)
-                        s = K == 1 ? row_dec16_avx512<1>(c16, cb, xf.data(), G, o)
-                                   : row_dec16_avx512<2>(c16, cb, xf.data(), G, o);
-                    else if (K <= 2)
-                        s = K == 1 ? row_dec16_avx2<1>(c16, cb, xf.data(), G, o)
-                                   : row_dec16_avx2<2>(c16, cb, xf.data(), G, o);
+                    if (pair)   // the two code bytes of a group as one 16-bit index
+                        s = row_dec<1>(isa, c16, P.data(), 65536, xf.data(), G, o);
+                    else if (B == 8)
+                        s = row_dec<1>(isa, codes, cb, 256, xf.data(), G, o);
+                    else if (K == 1)
+                        s = row_dec<1>(isa, c16, cb, 65536, xf.data(), G, o);
+                    else if (K == 2)
+                        s = row_dec<2>(isa, c16, cb, 65536, xf.data(), G, o);
                     else
                         s = row_dot_scalar(c16, cb, xf.data(), G, K, o);
                     acc[o] = s;

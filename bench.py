@@ -379,7 +379,7 @@ def cpu_kernel_bench(args, torch, np, aq, synth):
     batch = 1 if args.batch == 16 and "--batch" not in sys.argv else args.batch
     per_copy = sum(algorithmic_bytes(o, i, K, B, batch) for _, o, i, K, B in WORKLOAD)
     l3 = host_l3_bytes()
-    copies = args.copies or max(2, math.ceil(2 * max(l3, 32 << 20) / per_copy))
+    copies = args.copies or max(2, math.ceil(max(2 * l3, 256 << 20) / per_copy))
     sets = []
     for r in range(copies):
         entry = []
@@ -428,20 +428,22 @@ def cpu_kernel_bench(args, torch, np, aq, synth):
                 "sample": f"full decode to fp32 W + double matvec of the four products of one "
                           f"step (copy 0), repeated {reps}x in {ot:.1f} s",
                 "ms_per_step": round(ot / reps * 1e3, 2)}
-    # context: dense fp16 and fp32 W x on the same cores (torch), two copies rotating
+    # context: dense fp16 and fp32 W x on the same cores (torch), copies rotating over
+    # the same amount of memory as the quantized weights
     dense = {}
     if args.threads > 0:
         torch.set_num_threads(args.threads)
-    for name, out, in_, K, B in WORKLOAD:
+    for shape in sorted({(o, i) for _, o, i, _, _ in WORKLOAD}, reverse=True):
         for dt_name, dt_t in (("fp16", torch.float16), ("fp32", torch.float32)):
-            Ws = [torch.randn(out, in_).to(dt_t) for _ in range(2)]
-            xv = torch.randn(in_).to(dt_t)
+            n = max(2, math.ceil(max(2 * l3, 256 << 20) / (shape[0] * shape[1] * dt_t.itemsize)))
+            Ws = [torch.randn(shape).to(dt_t) for _ in range(n)]
+            xv = torch.randn(shape[1]).to(dt_t)
             for W in Ws:
                 W @ xv
             t0 = time.perf_counter()
-            for it in range(10):
-                Ws[it % 2] @ xv
-            dense[f"{name.split()[1]} {dt_name}"] = round((time.perf_counter() - t0) / 10 * 1e6, 1)
+            for it in range(4 * n):
+                Ws[it % n] @ xv
+            dense[f"{shape[0]}x{shape[1]} {dt_name}"] = round((time.perf_counter() - t0) / (4 * n) * 1e6, 1)
             del Ws
     nt = args.threads if args.threads > 0 else torch.get_num_threads()
     result = {"metric": "AQLM GEMV on the host cores: algorithmic GB/s, 2x8 & 1x16 MLP shapes",

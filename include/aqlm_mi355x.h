@@ -216,9 +216,11 @@ aqlm_status_t aqlm_gemv_packed_grouped(int n, const void *const *packed_codes,
 /*
  * The same product on the host cores (token generation on the CPU): host pointers in
  * the canonical layouts of aqlm_gemv, y [batch][out] fp16 written by the call, which
- * returns when it is done.  fp32 arithmetic throughout (8-bit codes with K in {1,2,4}:
- * per-group codebook.x lookup tables and AVX-512 / AVX2 gathers; 16-bit codes with K in
- * {1,2}: F16C decode + FMA; anything else: scalar code), y rounded once to fp16; the
+ * returns when it is done.  fp32 arithmetic (16-bit codes with K in {1,2} and 8-bit codes
+ * with K = 1: F16C decode + FMA; 2x8: the same decode over a per-call pair codebook
+ * P[c0 + 256*c1] = C_0[c0] + C_1[c1] rounded once to fp16, as the matrix-core kernels
+ * round the fold; 8-bit codes with K > 2: per-group codebook.x lookup tables and AVX-512
+ * / AVX2 gathers; 16-bit codes with K > 2: scalar code), y rounded once to fp16; the
  * result meets the same bar against the exact product as the GPU kernels and does not
  * depend on `threads`.  threads <= 0: the OpenMP default.  AQLM_ERR_INVALID_ARGUMENT
  * for a null pointer, a size < 1, in_features not a multiple of 8, K outside 1..8, B
