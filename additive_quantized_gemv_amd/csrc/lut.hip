@@ -23,6 +23,11 @@
 //   workgroup of a row range sums the slices) needs an agent-scope release fence
 //   per workgroup, i.e. an L2 write-back; measured on MI355X that single-kernel
 //   form took 24 us per 11008x4096 product against 7 + 4 us for the two kernels.
+//   A form without the fence (partials written with write-through agent-scope
+//   atomic stores, an arrival counter per row block, the last workgroup summing
+//   with coherent loads) is correct but slower too: 10.0 against 8.6 us per call
+//   for 4096x11008, the store round trip plus the re-read costing more than the
+//   second launch from a graph.
 // * Every code load of a wave (up to 32 rows) is issued before the tables are
 //   built, so each wave waits for HBM once.
 // * Packed variant (aqlm_pack_codes): the codes of a slice are stored as tiles
