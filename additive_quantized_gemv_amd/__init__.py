@@ -134,7 +134,7 @@ def _prep(codes, codebooks, x, K, B, packed=False):
     B = Bc if B is None else int(B)
     if B != Bc or K != codes.shape[2]:
         raise ValueError("K/B do not match the codes tensor")
-    want = (K, 8, 1 << B) if packed else (K, 1 << B, 8)
+    want = packed_codebooks_shape(K, B) if packed else (K, 1 << B, 8)
     if codebooks.dtype != torch.float16 or tuple(codebooks.shape) != want:
         raise ValueError(f"codebooks must be float16 {list(want)}")
     if x.dtype != torch.float16:
@@ -207,8 +207,8 @@ def gemv_packed(weights: PackedWeights, x, out=None):
     torch = _torch()
     lib = _load()
     w = weights
-    if w.codebooks.dtype != torch.float16 or tuple(w.codebooks.shape) != (w.K, 8, 1 << w.B):
-        raise ValueError("packed codebooks must be float16 [K][8][2^B]")
+    if w.codebooks.dtype != torch.float16 or tuple(w.codebooks.shape) != packed_codebooks_shape(w.K, w.B):
+        raise ValueError(f"packed codebooks must be float16 {list(packed_codebooks_shape(w.K, w.B))}")
     if w.codes.numel() * w.codes.element_size() != packed_codes_bytes(w.out_features,
                                                                        w.in_features, w.K, w.B):
         raise ValueError("packed codes have the wrong size")
@@ -366,29 +366,40 @@ def unpack_codes(packed, out_features, in_features, K, B):
     return C
 
 
+def packed_codebooks_shape(K: int, B: int) -> tuple:
+    """Shape of pack_codebooks' result: [K][8][256] planes (B = 8) or [K][4][65536][2]
+    position pairs (B = 16)."""
+    return (K, 8, 256) if B == 8 else (K, 4, 1 << B, 2)
+
+
 def pack_codebooks(codebooks, out=None):
-    """Plane-major copy [K][8][2^B] of codebooks [K][2^B][8] (a one-time weight layout change)."""
+    """Packed copy of codebooks [K][2^B][8] (a one-time weight layout change): for B = 8
+    the planes P[k][t][c] = C[k][c][t]; for B = 16 the position pairs
+    P[k][q][c][s] = C[k][c][2q + s]."""
     torch = _torch()
     lib = _load()
     K, E, g = codebooks.shape
     if codebooks.dtype != torch.float16 or g != 8 or E not in (256, 65536) or not codebooks.is_cuda \
             or not codebooks.is_contiguous():
         raise ValueError("codebooks must be a contiguous device float16 [K][2^B][8] tensor")
-    P = out if out is not None else torch.empty((K, 8, E), dtype=torch.float16,
-                                                 device=codebooks.device)
+    P = out if out is not None else torch.empty(packed_codebooks_shape(K, E.bit_length() - 1),
+                                                 dtype=torch.float16, device=codebooks.device)
+    if P.dtype != torch.float16 or P.numel() != K * E * 8 or not P.is_contiguous():
+        raise ValueError("out must be a contiguous float16 tensor of the codebooks' size")
     _check(lib.aqlm_pack_codebooks(codebooks.data_ptr(), P.data_ptr(), K, E.bit_length() - 1,
                                    _stream()), "aqlm_pack_codebooks")
     return P
 
 
 def unpack_codebooks(packed, out=None):
-    """Inverse of pack_codebooks: [K][8][2^B] -> [K][2^B][8]."""
+    """Inverse of pack_codebooks: -> [K][2^B][8]."""
     torch = _torch()
     lib = _load()
-    K, g, E = packed.shape
-    if packed.dtype != torch.float16 or g != 8 or E not in (256, 65536) or not packed.is_cuda \
-            or not packed.is_contiguous():
-        raise ValueError("packed must be a contiguous device float16 [K][8][2^B] tensor")
+    K = packed.shape[0]
+    E = 256 if tuple(packed.shape) == (K, 8, 256) else 65536
+    if packed.dtype != torch.float16 or tuple(packed.shape) != packed_codebooks_shape(K, E.bit_length() - 1) \
+            or not packed.is_cuda or not packed.is_contiguous():
+        raise ValueError("packed must be a contiguous device float16 [K][8][256] or [K][4][65536][2] tensor")
     C = out if out is not None else torch.empty((K, E, 8), dtype=torch.float16,
                                                  device=packed.device)
     _check(lib.aqlm_unpack_codebooks(packed.data_ptr(), C.data_ptr(), K, E.bit_length() - 1,

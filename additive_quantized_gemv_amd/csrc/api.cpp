@@ -225,7 +225,9 @@ hipError_t get_workspace(hipStream_t stream, size_t bytes, void **out) {
 aqlm_status_t pack_common(const void *src, void *dst, int K, int B, void *stream, bool pack) {
     if (!src || !dst || K < 1 || K > 8 || (B != 8 && B != 16)) return AQLM_ERR_INVALID_ARGUMENT;
     const int64_t bytes = int64_t(K) * (int64_t(1) << B) * kGroup * 2;
-    if (((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) & 1u) ||
+    // 16-bit codes are packed as 32-bit position pairs
+    const uintptr_t align = B == 16 ? 3u : 1u;
+    if (((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) & align) ||
         overlaps(src, bytes, dst, bytes))
         return AQLM_ERR_INVALID_ARGUMENT;
     const hipStream_t s = static_cast<hipStream_t>(stream);

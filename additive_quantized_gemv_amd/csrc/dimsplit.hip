@@ -4,24 +4,40 @@
 // Quantization for LLMs)", section "Niveau intermediaire") splits over its 8
 // positions t:
 //     y[b][o] = sum_t sum_k sum_j C_k[i_k(o,j)][t] * x[b][8j + t].
-// One position of one codebook is a plane of 65536 fp16 values = 128 KiB, which
-// fits the LDS of a CU, while the whole 1 MiB codebook does not.  So a workgroup
-// owns one plane (k, t) and one range of rows: it streams every code of its rows
-// and turns each into a 2-byte LDS read, instead of a 16-byte gather through L2,
-// whose request rate caps the plain 16-bit kernel.
+// The whole 1 MiB codebook does not fit the LDS of a CU, but 128 KiB of it does.
+// So a workgroup owns one slice of it and one range of rows: it streams every code
+// of its rows and turns each into an LDS read, instead of a 16-byte gather through
+// L2, whose request rate caps the plain 16-bit kernel.
 //
-// * Codebooks are taken pre-packed plane-major, [K][8][65536] fp16
-//   (aqlm_pack_codebooks: a one-time layout change of the weights).
+// * Codebooks are taken pre-packed as position pairs, [K][4][65536] x 2 fp16
+//   (aqlm_pack_codebooks: a one-time layout change of the weights): word (k, q, c)
+//   holds positions 2q and 2q+1 of entry c.
+// * Batch <= 4, pair form (one codebook; batch 1, or batch 2 with in <= 4096): a
+//   workgroup owns positions (2q, 2q+1) of the codebook for one half h of the code
+//   space (32768 words = 128 KiB, followed by a zero word).  Every lane looks up
+//   every code, at byte min(4*code - h*128 KiB, 128 KiB) (unsigned): a code of the
+//   other half lands on the zero word, which all such lanes read at one address (a
+//   broadcast).  Measured on MI355X, a 64-lane random 4-byte read with half of the
+//   lanes on one address takes 5.4 cycles against 7.3 for 64 random 2-byte reads,
+//   and it returns two positions per useful lane, so the lookups of a row cost ~27%
+//   fewer LDS cycles than one 2-byte read per position.  The address is two VALU
+//   operations (v_mad_u32_u16 picks the code's 16 bits, scales and offsets it; min).
+// * Batch <= 4, plane form (otherwise): a workgroup owns position t of codebook k,
+//   the 65536-entry plane taken from the pairs while staging, and looks up 2 bytes
+//   per code; with several tokens sharing the lookups, one position per workgroup
+//   halves the activation bytes each token reads from LDS.
 // * The K*8 workgroups of one row range get block ids that are equal modulo 8,
 //   so the dispatcher puts them on the same XCD: the codes come from HBM once and
 //   from that XCD's L2 for the other planes.
 // * Each wave walks its rows' 16-byte code chunks with several chunks in flight
-//   (a ring of 5..8 loads, issued branch-free); plane values for two codes are
-//   packed into one register and multiplied with v_dot2_f32_f16 against the
-//   matching activations, which sit in LDS as a plane x[b][8j + t] too.  Rows are
-//   summed across lanes several at a time by a transposing butterfly.
-// * Per-plane row sums go to a workspace; a second kernel adds the K*8 planes in
-//   order and writes fp16 y.
+//   (a ring of 5..8 loads, issued branch-free); each looked-up pair is multiplied
+//   with v_dot2_f32_f16 against the matching activation pair x[b][8j + 2q .. +1],
+//   staged in LDS (in registers at batch 1).  Rows are summed across lanes several
+//   at a time by a transposing butterfly.
+// * Per-workgroup row sums go to a workspace; a second kernel adds the K*8 parts
+//   in order and writes fp16 y.
+#include <type_traits>
+
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -30,12 +46,59 @@ namespace {
 
 constexpr int kDsWaves = 16;
 constexpr int kEntries = 65536;
-constexpr int kXPlaneHalves = 14336;   // batch * in/8 activations of one position
+constexpr int kHalf = kEntries / 2;     // code-space half of one batch-1 workgroup
+constexpr int kXPairs = 7168;           // in/8 activation pairs of one position pair (batch 1)
+constexpr int kXPlaneHalves = 14336;    // batch * in/8 activations of one position (batch 2..4)
+// LDS words of the batch <= 4 kernel: the larger of its two layouts
+constexpr int kDsLdsWords = (kHalf + 4 + kXPairs) > (kEntries / 2 + kXPlaneHalves / 2)
+                                ? (kHalf + 4 + kXPairs) : (kEntries / 2 + kXPlaneHalves / 2);
 // tokens of the matrix-core form: one 16-token tile (measured on MI355X against unpacking
 // and the canonical kernels: 1.3-6x faster at batches 5..8, even at 16, slower from 32)
 constexpr int kDsmMaxBatch = 16;
 
 typedef _Float16 hf;
+
+// 4 * (low / high 16 bits of w) + boff in one v_mad_u32_u16 (the two-op shift-and-add
+// the compiler emits otherwise makes the VALU, not the LDS, the limit of the lookups)
+__device__ __forceinline__ uint32_t pair_byte_lo(uint32_t w, uint32_t boff) {
+    uint32_t r;
+    asm("v_mad_u32_u16 %0, %1, 4, %2" : "=v"(r) : "v"(w), "s"(boff));
+    return r;
+}
+__device__ __forceinline__ uint32_t pair_byte_hi(uint32_t w, uint32_t boff) {
+    uint32_t r;
+    asm("v_mad_u32_u16 %0, %1, 4, %2 op_sel:[1,0,0,0]" : "=v"(r) : "v"(w), "s"(boff));
+    return r;
+}
+
+// Plane t of codebook k (65536 fp16) into LDS from the packed pairs: half (t & 1) of
+// each pair word (k, t >> 1, c), 4 entries per 16-byte load, rounds of 8 loads per
+// thread, every load of a round issued before its LDS writes.  Called by all threads.
+__device__ __forceinline__ void stage_plane(const uint16_t *__restrict__ planes, int k, int t, _Float16 *tab) {
+    const uint4 *src = reinterpret_cast<const uint4 *>(
+        reinterpret_cast<const uint32_t *>(planes) + (size_t(k) * 4 + (t >> 1)) * kEntries);
+    uint2 *dst = reinterpret_cast<uint2 *>(tab);
+    const uint32_t sel = (t & 1) ? 0x07060302u : 0x05040100u;   // the high or low halves
+    constexpr int kThreads = kDsWaves * kWave;
+    constexpr int PER = kEntries / 4 / kThreads;
+#pragma unroll
+    for (int r0 = 0; r0 < PER; r0 += 8) {
+        uint4 tmp[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) tmp[i] = src[threadIdx.x + (r0 + i) * kThreads];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            dst[threadIdx.x + (r0 + i) * kThreads] =
+                make_uint2(__builtin_amdgcn_perm(tmp[i].y, tmp[i].x, sel),
+                           __builtin_amdgcn_perm(tmp[i].w, tmp[i].z, sel));
+    }
+}
+
+// ds_kernel's pair form: one codebook, activation pairs of all tokens in registers
+// (two codebooks measured slower in it: 149 against 144 us per 2x16 7B layer)
+constexpr bool ds_pair_form(int K, int nb, int nseg) {
+    return K == 1 && (nb == 1 ? nseg <= 4 : nb == 2 && nseg == 1);
+}
 
 template <int NSEG>
 struct DsShape {
@@ -49,20 +112,32 @@ __global__ void __launch_bounds__(kDsWaves * kWave)
 ds_kernel(const uint8_t *__restrict__ codes1, const uint16_t *__restrict__ planes1,
           const uint16_t *__restrict__ x, float *__restrict__ partial, int out1, int in,
           int batch, int nranges, int rows_per_range, const Segs segs) {
-    constexpr int P = K * 8;                 // planes
+    constexpr int P = K * 8;                 // parts
     constexpr int GPC = 8 / K;               // groups per 16-byte chunk
     constexpr int RB = DsShape<NSEG>::RB;
     constexpr int D = DsShape<NSEG>::D;
-    __shared__ __attribute__((aligned(16))) hf tab[kEntries];
-    __shared__ __attribute__((aligned(16))) hf xs[kXPlaneHalves];
+    // PAIR (one codebook, and the activation pairs of all tokens fit in registers
+    // without spilling: batch 1 with NSEG <= 4, batch 2 with NSEG = 1):
+    // part (k, q, h) = position pair q of codebook k for code half h; LDS words
+    // 0 .. kHalf-1 hold its pairs, word kHalf a zero (the other half's codes), then
+    // the activation pairs x[b][8j + 2q .. +1].  Otherwise part (k, t) = position t,
+    // the 65536-entry plane taken from the pairs while staging, then the activations
+    // x[b][8j + t]: read from LDS per token, one position per part reads half the
+    // activation bytes of the pair form.
+    constexpr bool PAIR = ds_pair_form(K, NB, NSEG);
+    __shared__ __attribute__((aligned(16))) uint32_t lds[kDsLdsWords];
+    uint32_t *const tab = lds;                                        // PAIR
+    uint32_t *const xs = lds + kHalf + 4;                             // PAIR
+    hf *const tabh = reinterpret_cast<hf *>(lds);                     // !PAIR
+    hf *const xsh = reinterpret_cast<hf *>(lds + kEntries / 2);       // !PAIR
 
-    // block -> (plane, row range); the planes of a range share id % 8, i.e. an XCD
+    // block -> (part, row range); the parts of a range share id % 8, i.e. an XCD
     const int id = blockIdx.x;
     const int grp = id / (P * 8), rem = id - grp * (P * 8);
     const int p = rem >> 3;
     const int rr = grp * 8 + (rem & 7);
     if (rr >= nranges) return;
-    const int k = p >> 3, t = p & 7;
+    const int k = p >> 3, q = (p >> 1) & 3, h = p & 1, t = p & 7;
     // this range's matrix: the arguments for one matrix (NS == 1), else from segs
     // (ranges of each matrix numbered consecutively, segs.aux0)
     const int mi = seg_of<NS>(segs.n, segs.aux0, rr);
@@ -106,40 +181,62 @@ ds_kernel(const uint8_t *__restrict__ codes1, const uint16_t *__restrict__ plane
         return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(rp + lane_off[sg]));
     };
 
-    {
-        // 128 KiB plane: every load of a thread issued before its LDS writes.  The
-        // plane gates all work, so it goes first; code loads issued with it would
-        // compete for the same bandwidth and delay it (about 2.5 us measured).
-        const uint4 *src = reinterpret_cast<const uint4 *>(planes + size_t(p) * kEntries);
+    // The table gates all work, so it is staged first; code loads issued with it
+    // would compete for the same bandwidth and delay it (about 2.5 us measured).
+    // Every load of a thread (of a round) is issued before its LDS writes.
+    if constexpr (PAIR) {
+        // 128 KiB of pairs
+        const uint4 *src = reinterpret_cast<const uint4 *>(
+            reinterpret_cast<const uint32_t *>(planes) + (size_t(k) * 4 + q) * kEntries + size_t(h) * kHalf);
         uint4 *dst = reinterpret_cast<uint4 *>(tab);
-        constexpr int PER = kEntries / 8 / (kDsWaves * kWave);
+        constexpr int PER = kHalf / 4 / (kDsWaves * kWave);
         uint4 tmp[PER];
 #pragma unroll
         for (int i = 0; i < PER; ++i) tmp[i] = src[threadIdx.x + i * kDsWaves * kWave];
 #pragma unroll
         for (int i = 0; i < PER; ++i) dst[threadIdx.x + i * kDsWaves * kWave] = tmp[i];
+        if (threadIdx.x == 0) tab[kHalf] = 0u;
+    } else {
+        stage_plane(planes, k, t, tabh);
+    }
+    // activations: x[b][8j + 2q .. +1] (PAIR) or x[b][8j + t]
+    if constexpr (PAIR && NB == 1) {
+        for (int j = threadIdx.x; j < G; j += blockDim.x)
+            xs[j] = *reinterpret_cast<const uint32_t *>(x + size_t(j) * kGroup + 2 * q);
+    } else {
         for (int b = 0; b < batch; ++b)
-            for (int j = threadIdx.x; j < G; j += blockDim.x)
-                xs[b * G + j] = __builtin_bit_cast(hf, x[size_t(b) * in + size_t(j) * kGroup + t]);
+            for (int j = threadIdx.x; j < G; j += blockDim.x) {
+                const uint16_t *src = x + size_t(b) * in + size_t(j) * kGroup;
+                if constexpr (PAIR) xs[b * G + j] = *reinterpret_cast<const uint32_t *>(src + 2 * q);
+                else xsh[b * G + j] = __builtin_bit_cast(hf, src[t]);
+            }
     }
     __syncthreads();
+    // byte address of a code's pair: 4*code - h*128 KiB, clamped to the zero word
+    const uint32_t boff = h ? uint32_t(0) - uint32_t(kHalf * 4) : 0u;
+    const char *tabb = reinterpret_cast<const char *>(tab);
     if (nitems == 0) return;
 
     u32x4 ring[D];
 #pragma unroll
     for (int q = 0; q < D; ++q) ring[q] = load_item(q, q % NSEG);
 
-    // at batch 1 each lane's activations (GPC per chunk position) stay in registers
-    constexpr bool XREG = NB == 1;
-    hf xr[XREG ? NSEG : 1][GPC];
-    if constexpr (XREG) {
+    // PAIR: each lane's activation pairs (GPC per chunk position and token) stay in
+    // registers; a token past the batch repeats the last one (its sums are not stored),
+    // so the loads need no condition (a conditional one becomes a branch per load)
+    uint32_t xr[PAIR ? NSEG : 1][GPC][PAIR ? NB : 1];
+    if constexpr (PAIR) {
 #pragma unroll
         for (int sg = 0; sg < NSEG; ++sg) {
             const int c = min(lane + kWave * sg, NC - 1);
 #pragma unroll
-            for (int g = 0; g < GPC; ++g) xr[sg][g] = xs[c * GPC + g];
+            for (int g = 0; g < GPC; ++g)
+#pragma unroll
+                for (int b = 0; b < NB; ++b)
+                    xr[sg][g][b] = xs[(NB == 1 ? 0 : min(b, batch - 1)) * G + c * GPC + g];
         }
     }
+    const uint32_t ksh = 16u * uint32_t(k);   // K = 2: codebook k's code is half k of a word
 
     for (int base = 0; base < nitems; base += D) {
         float acc[RB][NB];
@@ -156,35 +253,53 @@ ds_kernel(const uint8_t *__restrict__ codes1, const uint16_t *__restrict__ plane
             ring[q] = load_item(item + D, seg);
             const bool ok = item < nitems && lane_ok[seg];
             const int c = min(lane + kWave * seg, NC - 1);
-            // plane values of this chunk's codes (codebook k of each group)
-            hf v[GPC];
+            if constexpr (PAIR) {
+                // pairs of this chunk's codes (codebook k of each group), zero for the
+                // other half; code n = g*K + k of the chunk: word n/2 is g/2 (K = 1) or g
+                // (K = 2), known at compile time; only K = 2 selects the half at run time
+                uint32_t v[GPC];
 #pragma unroll
-            for (int g = 0; g < GPC; ++g) {
-                // code n = g*K + k of the chunk: word n/2 is g/2 (K = 1) or g (K = 2),
-                // known at compile time; only K = 2 selects the half at run time
-                uint32_t code;
-                if constexpr (K == 1) {
-                    const uint32_t w = cw[g >> 1];
-                    code = (g & 1) ? (w >> 16) : (w & 0xFFFFu);
-                } else {
-                    code = (cw[g] >> (16 * k)) & 0xFFFFu;
+                for (int g = 0; g < GPC; ++g) {
+                    uint32_t byte;
+                    if constexpr (K == 1)
+                        byte = (g & 1) ? pair_byte_hi(cw[g >> 1], boff) : pair_byte_lo(cw[g >> 1], boff);
+                    else   // the low 16 bits after the shift are codebook k's code
+                        byte = pair_byte_lo(cw[g] >> ksh, boff);
+                    byte = min(byte, uint32_t(kHalf * 4));
+                    v[g] = *reinterpret_cast<const uint32_t *>(tabb + byte);
                 }
-                v[g] = tab[code];
-            }
 #pragma unroll
-            for (int b = 0; b < NB; ++b) {
-                if (NB == 1 || b < batch) {
-                    const hf *xp = xs + b * G + c * GPC;
+                for (int b = 0; b < NB; ++b) {
                     float d = 0.0f;
 #pragma unroll
-                    for (int g = 0; g < GPC; g += 2) {
-                        const half2v a = {v[g], v[g + 1]};
-                        half2v xv;
-                        if constexpr (XREG) xv = half2v{xr[seg][g], xr[seg][g + 1]};
-                        else xv = half2v{xp[g], xp[g + 1]};
-                        d = __builtin_amdgcn_fdot2(a, xv, d, false);
-                    }
+                    for (int g = 0; g < GPC; ++g)
+                        d = __builtin_amdgcn_fdot2(as_h2(v[g]), as_h2(xr[seg][g][b]), d, false);
                     acc[r][b] += ok ? d : 0.0f;
+                }
+            } else {
+                // plane values of this chunk's codes, two per register for v_dot2
+                hf v[GPC];
+#pragma unroll
+                for (int g = 0; g < GPC; ++g) {
+                    uint32_t code;
+                    if constexpr (K == 1) {
+                        const uint32_t w = cw[g >> 1];
+                        code = (g & 1) ? (w >> 16) : (w & 0xFFFFu);
+                    } else {
+                        code = (cw[g] >> (16 * k)) & 0xFFFFu;
+                    }
+                    v[g] = tabh[code];
+                }
+#pragma unroll
+                for (int b = 0; b < NB; ++b) {
+                    if (b < batch) {
+                        const hf *xp = xsh + b * G + c * GPC;
+                        float d = 0.0f;
+#pragma unroll
+                        for (int g = 0; g < GPC; g += 2)
+                            d = __builtin_amdgcn_fdot2(half2v{v[g], v[g + 1]}, half2v{xp[g], xp[g + 1]}, d, false);
+                        acc[r][b] += ok ? d : 0.0f;
+                    }
                 }
             }
         }
@@ -276,17 +391,7 @@ dsm_kernel(const uint8_t *__restrict__ codes1, const uint16_t *__restrict__ plan
     const int r_begin = lrr * rows_per_range;
     const int r_end = min(out, r_begin + rows_per_range);
 
-    {
-        // 128 KiB plane: every load of a thread issued before its LDS writes
-        const uint4 *src = reinterpret_cast<const uint4 *>(planes + size_t(p) * kEntries);
-        uint4 *dst = reinterpret_cast<uint4 *>(tab);
-        constexpr int PER = kEntries / 8 / (kDsWaves * kWave);
-        uint4 tmp[PER];
-#pragma unroll
-        for (int i = 0; i < PER; ++i) tmp[i] = src[threadIdx.x + i * kDsWaves * kWave];
-#pragma unroll
-        for (int i = 0; i < PER; ++i) dst[threadIdx.x + i * kDsWaves * kWave] = tmp[i];
-    }
+    stage_plane(planes, k, t, tab);   // plane t (128 KiB) from the pairs
     __syncthreads();
 
     const int ntiles = (r_end - r_begin + 15) / 16;   // <= 0: nothing to do
@@ -388,27 +493,38 @@ dsm_kernel(const uint8_t *__restrict__ codes1, const uint16_t *__restrict__ plan
     }
 }
 
-// planes[k][t][c] = codebooks[k][c][t]
+// Packed codebooks: W = 1 (8-bit codes): planes[k][t][c] = codebooks[k][c][t] (fp16);
+// W = 2 (16-bit codes): pairs[k][q][c] = codebooks[k][c][2q .. 2q+1] (32-bit words).
+template <int W>
 __global__ void __launch_bounds__(256)
-pack_kernel(const uint16_t *__restrict__ cb, uint16_t *__restrict__ planes, int K, int entries) {
+pack_kernel(const uint16_t *__restrict__ cb, uint16_t *__restrict__ packed, int K, int entries) {
+    using U = typename std::conditional<W == 1, uint16_t, uint32_t>::type;
+    constexpr int N = 8 / W;   // units per entry
+    const U *__restrict__ src = reinterpret_cast<const U *>(cb);
+    U *__restrict__ dst = reinterpret_cast<U *>(packed);
     const int64_t n = int64_t(K) * entries;
     for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
          i += int64_t(gridDim.x) * blockDim.x) {
         const int64_t kk = i / entries, c = i - kk * entries;
 #pragma unroll
-        for (int t = 0; t < 8; ++t) planes[(kk * 8 + t) * entries + c] = cb[i * 8 + t];
+        for (int t = 0; t < N; ++t) dst[(kk * N + t) * entries + c] = src[i * N + t];
     }
 }
 
-// codebooks[k][c][t] = planes[k][t][c]
+// the inverse of pack_kernel<W>
+template <int W>
 __global__ void __launch_bounds__(256)
-unpack_kernel(const uint16_t *__restrict__ planes, uint16_t *__restrict__ cb, int K, int entries) {
+unpack_kernel(const uint16_t *__restrict__ packed, uint16_t *__restrict__ cb, int K, int entries) {
+    using U = typename std::conditional<W == 1, uint16_t, uint32_t>::type;
+    constexpr int N = 8 / W;
+    const U *__restrict__ src = reinterpret_cast<const U *>(packed);
+    U *__restrict__ dst = reinterpret_cast<U *>(cb);
     const int64_t n = int64_t(K) * entries;
     for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
          i += int64_t(gridDim.x) * blockDim.x) {
         const int64_t kk = i / entries, c = i - kk * entries;
 #pragma unroll
-        for (int t = 0; t < 8; ++t) cb[i * 8 + t] = planes[(kk * 8 + t) * entries + c];
+        for (int t = 0; t < N; ++t) dst[i * N + t] = src[(kk * N + t) * entries + c];
     }
 }
 
@@ -561,20 +677,24 @@ bool ds_supported(const Problem &p) {
     if (p.batch < 1 || p.batch > 4) return false;
     const int64_t G = p.in / kGroup;
     if (G % (8 / p.K)) return false;
-    if (int64_t(p.batch) * G > kXPlaneHalves) return false;
     const int64_t NC = G / (8 / p.K);
-    if ((NC + kWave - 1) / kWave > 8) return false;
+    const int64_t nseg = (NC + kWave - 1) / kWave;
+    if (nseg > 8) return false;
+    // the kernel's two LDS layouts (see ds_kernel)
+    const int nb = p.batch <= 1 ? 1 : p.batch <= 2 ? 2 : 4;
+    if (int64_t(p.batch) * G > (ds_pair_form(p.K, nb, int(nseg)) ? kXPairs : kXPlaneHalves)) return false;
     if (p.out > (1 << 28)) return false;
     const uintptr_t a = reinterpret_cast<uintptr_t>(p.codes) |
                         reinterpret_cast<uintptr_t>(p.codebooks);
-    return (a & 15u) == 0;
+    // activation pairs are staged with 4-byte loads
+    return (a & 15u) == 0 && (reinterpret_cast<uintptr_t>(p.x) & 3u) == 0;
 }
 
 size_t ds_workspace_bytes(const Problem &p) {
     return size_t(p.K) * 8 * size_t(p.batch) * size_t(p.out) * sizeof(float);
 }
 
-// segs.cb holds the packed planes [K][8][65536]; workspace: K*8 x batch x T fp32
+// segs.cb holds the packed pairs [K][4][65536]; workspace: K*8 x batch x T fp32
 hipError_t launch_ds(const Problem &p, void *workspace) {
     Segs segs = p.segs;
     const DsCfg c = ds_cfg(p, &segs);
@@ -588,9 +708,14 @@ hipError_t launch_pack_codebooks(const void *cb, void *planes, int K, int B, hip
     const int entries = 1 << B;
     const int64_t n = int64_t(K) * entries;
     const int blocks = int((n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096);
-    hipLaunchKernelGGL(pack_kernel, dim3(blocks), dim3(256), 0, s,
-                       static_cast<const uint16_t *>(cb), static_cast<uint16_t *>(planes), K,
-                       entries);
+    if (B == 16)
+        hipLaunchKernelGGL(pack_kernel<2>, dim3(blocks), dim3(256), 0, s,
+                           static_cast<const uint16_t *>(cb), static_cast<uint16_t *>(planes), K,
+                           entries);
+    else
+        hipLaunchKernelGGL(pack_kernel<1>, dim3(blocks), dim3(256), 0, s,
+                           static_cast<const uint16_t *>(cb), static_cast<uint16_t *>(planes), K,
+                           entries);
     return hipGetLastError();
 }
 
@@ -598,9 +723,14 @@ hipError_t launch_unpack_codebooks(const void *planes, void *cb, int K, int B, h
     const int entries = 1 << B;
     const int64_t n = int64_t(K) * entries;
     const int blocks = int((n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096);
-    hipLaunchKernelGGL(unpack_kernel, dim3(blocks), dim3(256), 0, s,
-                       static_cast<const uint16_t *>(planes), static_cast<uint16_t *>(cb), K,
-                       entries);
+    if (B == 16)
+        hipLaunchKernelGGL(unpack_kernel<2>, dim3(blocks), dim3(256), 0, s,
+                           static_cast<const uint16_t *>(planes), static_cast<uint16_t *>(cb), K,
+                           entries);
+    else
+        hipLaunchKernelGGL(unpack_kernel<1>, dim3(blocks), dim3(256), 0, s,
+                           static_cast<const uint16_t *>(planes), static_cast<uint16_t *>(cb), K,
+                           entries);
     return hipGetLastError();
 }
 

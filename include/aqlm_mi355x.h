@@ -77,8 +77,8 @@ typedef enum {
     AQLM_VARIANT_L2 = 4,      /* B = 16: codebook gathered through L2, batch <= 8            */
     AQLM_VARIANT_MFMA = 5,    /* decode to fp16 fragments + fp16 matrix cores, any batch;
                                  K in {1,2}, or K in {4,8} with B = 8; in/8 a multiple of 4 */
-    AQLM_VARIANT_SPLIT = 6,   /* B = 16, packed codebooks: one codebook position per CU,
-                                 batch <= 16 (aqlm_gemv_packed only)                       */
+    AQLM_VARIANT_SPLIT = 6,   /* B = 16, packed codebooks: a slice of the codebook per
+                                 CU, batch <= 16 (aqlm_gemv_packed only)                   */
     AQLM_VARIANT_PREFILL = 7  /* prefill-size batches: W decoded once to fp16 in the
                                  workspace, one hipBLASLt GEMM (fp32 accumulation); the
                                  same K, B and shapes as AQLM_VARIANT_MFMA               */
@@ -135,11 +135,14 @@ aqlm_status_t aqlm_dequantize(const void *codes, const void *codebooks, void *W,
                               void *stream);
 
 /*
- * Packed codebook layout for 16-bit codes: plane-major [K][8][2^B] fp16, i.e.
- * packed[k][t][c] = codebooks[k][c][t].  Same bytes as the codebooks; a one-time
- * change of the weights' layout (not part of the product).  It lets a CU keep
- * one position of a 65536-entry codebook (128 KiB) in LDS.  B in {8, 16};
- * `packed` must not overlap `codebooks`.
+ * Packed codebook layouts (same bytes as the codebooks; a one-time change of the
+ * weights' layout, not part of the product).  B in {8, 16}; `packed` must not
+ * overlap `codebooks`; both 2-byte aligned (4-byte for B = 16).
+ * - B = 8: plane-major [K][8][256] fp16, packed[k][t][c] = codebooks[k][c][t].
+ * - B = 16: position pairs [K][4][65536][2] fp16,
+ *   packed[k][q][c][s] = codebooks[k][c][2q + s]: one 32-bit word holds positions
+ *   2q and 2q+1 of an entry, so half of the code space of one position pair
+ *   (32768 words = 128 KiB) fits the LDS of a CU.
  */
 aqlm_status_t aqlm_pack_codebooks(const void *codebooks, void *packed, int K, int B, void *stream);
 
@@ -171,11 +174,13 @@ aqlm_status_t aqlm_unpack_codes(const void *packed, void *codes, int64_t out_fea
  * The product of aqlm_gemv from packed weights: codes from aqlm_pack_codes,
  * codebooks from aqlm_pack_codebooks.  Same y, same argument rules.
  * - 16-bit codes, K in {1,2}, batch <= 4: the position-split kernel
- *   (AQLM_VARIANT_SPLIT): the K*8 codebook planes live in the LDS of K*8
- *   workgroups per row range and a second kernel adds their partial sums.
+ *   (AQLM_VARIANT_SPLIT): each of K*8 workgroups per row range holds one position
+ *   pair of one codebook for one half of the code space in LDS (codes of the other
+ *   half read a zero word), and a second kernel adds their partial sums.
  * - 16-bit codes, batch 5..16 (K = 1) or 5..8 (K = 2), in_features a multiple of 64,
- *   16-byte aligned pointers: the same planes on the matrix cores (a small
- *   kernel first writes x transposed by position into the workspace).
+ *   16-byte aligned pointers: the same split on the matrix cores, one position per
+ *   workgroup (taken from the pairs while the table is staged; a small kernel first
+ *   writes x transposed by position into the workspace).
  * - 2x8, batch 1, 16-byte aligned pointers: the lookup-table kernel reading
  *   the code tiles (1 KiB contiguous per wave load).
  * - otherwise the packed operands are unpacked into the stream's workspace and

@@ -105,6 +105,7 @@ def test_pack_invalid(lib):
     assert lib.aqlm_pack_codebooks(CB, Y, 1, 12, None) == 1
     assert lib.aqlm_pack_codebooks(CB, CB + 64, 1, 16, None) == 1     # overlapping
     assert lib.aqlm_unpack_codebooks(CB + 1, Y, 1, 16, None) == 1     # misaligned
+    assert lib.aqlm_pack_codebooks(CB + 2, Y, 1, 16, None) == 1       # pairs need 4 bytes
     assert lib.aqlm_gemv_packed(0, CB, X, Y, 16, 64, 1, 16, 1, None) == 1
     assert lib.aqlm_gemv_packed(C, CB, X, Y, 16, 60, 1, 16, 1, None) == 1
 

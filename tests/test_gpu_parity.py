@@ -310,8 +310,11 @@ def test_pack_unpack_exact(aq, KB):
     cb = torch.from_numpy(p["codebooks"]).cuda()
     P = aq.pack_codebooks(cb)
     torch.cuda.synchronize()
-    assert np.array_equal(P.cpu().numpy().view(np.uint16),
-                          np.ascontiguousarray(p["codebooks"].transpose(0, 2, 1)).view(np.uint16))
+    c = p["codebooks"].view(np.uint16)
+    # B = 8: planes P[k][t][c] = C[k][c][t]; B = 16: pairs P[k][q][c][s] = C[k][c][2q + s]
+    want = c.transpose(0, 2, 1) if B == 8 else c.reshape(K, 1 << B, 4, 2).transpose(0, 2, 1, 3)
+    assert P.shape == want.shape
+    assert np.array_equal(P.cpu().numpy().view(np.uint16), np.ascontiguousarray(want))
     assert np.array_equal(aq.unpack_codebooks(P).cpu().numpy().view(np.uint16),
                           p["codebooks"].view(np.uint16))
 
