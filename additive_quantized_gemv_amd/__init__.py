@@ -180,7 +180,7 @@ def gemv(codes, codebooks, x, K=None, B=None, out=None):
 
 
 def gemm(codes, codebooks, x, K=None, B=None, out=None):
-    """Y = X W^T; for batch >= 16 decodes to fp16 and runs on the matrix cores."""
+    """Y = X W^T; from batch 2 (4 for eight codebooks) decodes to fp16 and runs on the matrix cores."""
     return _product("aqlm_gemm", codes, codebooks, x, K, B, out)
 
 
@@ -271,7 +271,7 @@ def gemv_grouped(codes, codebooks, x, out=None):
 
 
 def gemm_grouped(codes, codebooks, x, out=None):
-    """gemv_grouped with the matrix-core kernels from batch 16 (as gemm)."""
+    """gemv_grouped with the matrix-core kernels from batch 2 (as gemm)."""
     return _grouped_canonical("aqlm_gemm_grouped", codes, codebooks, x, out)
 
 

@@ -16,7 +16,12 @@
 namespace {
 
 constexpr int kGroup = 8;
-constexpr int kMfmaMinBatchDefault = 16;
+// Batch from which aqlm_gemm takes the matrix cores.  Measured on MI355X (7B layer,
+// grouped, us, gather kernels -> matrix cores): 2x8 b2 80 -> 42, b8 260 -> 48; 1x16 b2
+// 129 -> 123, b8 323 -> 131; 4x8 b2 104 -> 89; 2x16 b8 340 -> 244; 8x8 b2 147 -> 184
+// (the fp32 fold of 8 codebooks per group), b8 335 -> 185.
+constexpr int kMfmaMinBatch = 2;
+constexpr int kMfmaMinBatch8Codebooks = 4;
 // Measured on MI355X (7B layer linears, canonical weights): the prefill path overtakes the
 // matrix-core kernels at batch 256 for 16-bit codes (decoding a 1 MiB codebook through
 // L2 per token tile costs more) and at 1024 for 8-bit codes with K <= 2.
@@ -60,11 +65,12 @@ int prefill_min_batch(const aqlm::Problem &p) {
     return n >= 1 ? n : def;
 }
 
-int mfma_min_batch() {
+int mfma_min_batch(int K) {
+    const int def = K >= 8 ? kMfmaMinBatch8Codebooks : kMfmaMinBatch;
     const char *v = std::getenv("AQLM_MFMA_MIN_BATCH");
-    if (!v || !*v) return kMfmaMinBatchDefault;
+    if (!v || !*v) return def;
     const int n = std::atoi(v);
-    return n >= 1 ? n : kMfmaMinBatchDefault;
+    return n >= 1 ? n : def;
 }
 
 // [a, a+na) and [b, b+nb) overlap?
@@ -170,7 +176,7 @@ int choose(bool gemm, const aqlm::Problem &p) {
     if (forced != AQLM_VARIANT_AUTO && supported(forced, p)) return forced;
     if (gemm && p.batch >= prefill_min_batch(p) && supported(AQLM_VARIANT_PREFILL, p))
         return AQLM_VARIANT_PREFILL;
-    if (gemm && p.batch >= mfma_min_batch() && supported(AQLM_VARIANT_MFMA, p))
+    if (gemm && p.batch >= mfma_min_batch(p.K) && supported(AQLM_VARIANT_MFMA, p))
         return AQLM_VARIANT_MFMA;
     if (supported(AQLM_VARIANT_LUT, p)) return AQLM_VARIANT_LUT;
     if (supported(AQLM_VARIANT_LDS, p)) return AQLM_VARIANT_LDS;
@@ -610,7 +616,7 @@ aqlm_status_t aqlm_gemv_packed_grouped(int n, const void *const *packed_codes,
     // unpacked operands, then (matrix cores) that kernel's own workspace
     const size_t unpacked = tiled ? cb_off + size_t(cbbytes) : size_t(cbbytes);
     const size_t ops_off = (unpacked + 255) / 256 * 256;
-    const bool gemm = !generic && batch >= mfma_min_batch();
+    const bool gemm = !generic && batch >= mfma_min_batch(K);
     size_t mfma_ws = 0;
     if (!split && !splitm && !lutp && gemm) {
         const aqlm::Problem shape = make_problem(p.codes, p.codebooks, p.x, p.y, p.out, p.in, K,

@@ -1,7 +1,9 @@
 // Batched additive-quantized GEMM on the gfx950 matrix cores.
 //
-// At batch >= 16 the product is a real dense contraction, so W is decoded to
-// fp16 and fed to v_mfma_f32_{16x16x32,32x32x16}_f16 (fp32 accumulation).
+// With several tokens the product is a dense contraction, so W is decoded to fp16
+// and fed to v_mfma_f32_{16x16x32,32x32x16}_f16 (fp32 accumulation).  Even at 2
+// tokens (a 16-token tile mostly padding) this beats the gather kernels on MI355X:
+// a group is decoded once for all tokens and the matrix cores are otherwise idle.
 // Decode rule: page "AQLM (Additive Quantization for LLMs)", section "Niveau
 // intermediaire".  Each lane's A fragment is exactly one 8-wide group of one
 // row (8 consecutive k), so a lane decodes one group straight into its MFMA

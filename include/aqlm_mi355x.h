@@ -95,8 +95,9 @@ aqlm_status_t aqlm_gemv(const void *codes, const void *codebooks, const void *x,
                         void *stream);
 
 /*
- * Same product and arguments as aqlm_gemv; for batch >= 16 it uses the
- * dequantize-to-fp16 + MFMA kernels, below that it behaves as aqlm_gemv.  From
+ * Same product and arguments as aqlm_gemv; from batch 2 (4 for eight codebooks;
+ * AQLM_MFMA_MIN_BATCH overrides) it uses the decode-to-fp16 + MFMA kernels, at batch 1
+ * it behaves as aqlm_gemv.  From
  * prefill-size batches (256 for 16-bit codes or K >= 4, 1024 otherwise;
  * AQLM_PREFILL_MIN_BATCH overrides) W is instead decoded once into the stream's workspace as
  * dense fp16 (out*in*2 bytes plus 64 MiB of GEMM scratch, kept like every
@@ -184,7 +185,7 @@ aqlm_status_t aqlm_unpack_codes(const void *packed, void *codes, int64_t out_fea
  * - 2x8, batch 1, 16-byte aligned pointers: the lookup-table kernel reading
  *   the code tiles (1 KiB contiguous per wave load).
  * - otherwise the packed operands are unpacked into the stream's workspace and
- *   the product runs as aqlm_gemm does (matrix cores from batch 16, their
+ *   the product runs as aqlm_gemm does (matrix cores from batch 2, their
  *   partial sums after the operands), else as aqlm_gemv.
  * Uses the per-(device, stream) workspace (partial sums, transposed x, or the
  * unpacked operands); on a capturing stream without a large enough workspace it

@@ -178,7 +178,10 @@ def test_variant_choice_host_logic(lib):
     assert sel(0, 8192, 28672, 1, 16, 4) == "l2"
     assert sel(1, 4096, 4096, 2, 8, 16) == "mfma"
     assert sel(1, 4096, 4096, 1, 16, 128) == "mfma"
-    assert sel(1, 4096, 4096, 2, 8, 8) == "lds"
+    assert sel(1, 4096, 4096, 2, 8, 8) == "mfma"
+    assert sel(1, 4096, 4096, 2, 8, 1) == "lut"
+    assert sel(1, 4096, 4096, 8, 8, 2) == "lds"       # eight codebooks: matrix cores from 4
+    assert sel(1, 4096, 4096, 8, 8, 4) == "mfma"
     assert sel(0, 64, 24, 3, 8, 1) == "generic"
     assert lib.aqlm_variant_supported(3, C, CB, X, Y, 4096, 4096, 1, 16, 1) == 0  # lut needs 2x8
     assert lib.aqlm_variant_supported(5, C, CB, X, Y, 4096, 4096, 3, 8, 16) == 0  # mfma: K<=2
