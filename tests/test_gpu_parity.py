@@ -114,8 +114,9 @@ def test_batches(aq, orc, batch, KB):
     check_y(aq.gemm(codes, cb, x), yref, f"gemm b={batch}")
     check_y(aq.gemv(codes, cb, x), yref, f"gemv b={batch}")
     check_y(aq.gemv_variant("mfma", codes, cb, x), yref, f"mfma b={batch}")
-    if batch >= 16:
-        assert aq.selected_variant(codes, cb, x, gemm=True) == "mfma"
+    # aqlm_gemm takes the matrix cores from batch 2; aqlm_gemv never does
+    assert (aq.selected_variant(codes, cb, x, gemm=True) == "mfma") == (batch >= 2)
+    assert aq.selected_variant(codes, cb, x, gemm=False) != "mfma"
 
 
 @pytest.mark.parametrize("KB", [(1, 8), (2, 8), (3, 8), (4, 8), (8, 8), (1, 16), (2, 16)])
@@ -354,6 +355,9 @@ PACKED = [
     (300, 4096, 1, 16, 1), (65, 520, 1, 16, 1), (1, 64, 1, 16, 1), (257, 11008, 1, 16, 1),
     (130, 2048, 1, 16, 2), (77, 1024, 1, 16, 3), (160, 8192, 1, 16, 4), (96, 512, 2, 16, 1),
     (50, 1024, 2, 16, 4), (64, 512, 1, 16, 8), (1000, 28672, 1, 16, 1),
+    # the split kernel's two forms: pairs at batch 1 up to 4 chunk positions per lane
+    # (in 16384) and at batch 2 with one; one position per workgroup past that
+    (64, 16384, 1, 16, 1), (40, 20480, 1, 16, 1), (100, 11008, 1, 16, 2), (33, 2048, 2, 16, 2),
     # 2x8: the tiled lookup-table kernel at batch 1 (ragged rows, partial slices), else unpacked
     (40, 512, 2, 8, 1), (65, 520, 2, 8, 1), (1, 64, 2, 8, 1), (300, 4096, 2, 8, 1),
     (257, 11008, 2, 8, 1), (1023, 4160, 2, 8, 1), (5000, 512, 2, 8, 1), (96, 512, 2, 8, 4),
@@ -368,6 +372,22 @@ PACKED = [
     # 2x8 from batch 16: unpacked, then the matrix cores (persistent / tiled with partial sums)
     (300, 4096, 2, 8, 16), (257, 4096, 2, 8, 33), (96, 512, 2, 8, 128),
 ]
+
+
+@pytest.mark.parametrize("KB", [(1, 16), (2, 8)])
+def test_gemv_packed_unaligned_x(aq, orc, KB):
+    """x 2 bytes off a 4-byte boundary: the split and lookup-table kernels stage x with
+    wider loads, so the product takes the unpacked path, with the same result."""
+    import torch
+    K, B = KB
+    p = synth.make_problem(256, 4096, K, B, batch=1, sigma_cb=0.02, config=1490 + K)
+    codes, cb, x = _dev(p)
+    buf = torch.empty(4096 + 1, dtype=torch.float16, device=x.device)
+    buf[1:] = x[0]
+    xu = buf[1:]
+    assert xu.data_ptr() % 4 == 2
+    yref = orc.gemv(p["codes"], p["codebooks"], p["x"], K, B)
+    check_y(aq.gemv_packed(aq.pack_weights(codes, cb), xu), yref, f"packed unaligned x {KB}")
 
 
 @pytest.mark.parametrize("case", PACKED, ids=lambda c: "x".join(map(str, c)))
