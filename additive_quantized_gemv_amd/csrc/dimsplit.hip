@@ -94,11 +94,11 @@ __device__ __forceinline__ void stage_plane(const uint16_t *__restrict__ planes,
     }
 }
 
-// ds_kernel's pair form: one codebook, activation pairs of all tokens in registers
+// ds_kernel's pair form: one codebook, batch 1 (activation pairs in registers up to 4
+// chunk positions per lane, else read from LDS) or batch 2 with one chunk position
 // (two codebooks measured slower in it: 149 against 144 us per 2x16 7B layer)
-constexpr bool ds_pair_form(int K, int nb, int nseg) {
-    return K == 1 && (nb == 1 ? nseg <= 4 : nb == 2 && nseg == 1);
-}
+constexpr bool ds_pair_form(int K, int nb, int nseg) { return K == 1 && (nb == 1 || nseg == 1) && nb <= 2; }
+constexpr bool ds_pair_xreg(int nb, int nseg) { return nb * nseg <= 4; }
 
 template <int NSEG>
 struct DsShape {
@@ -116,8 +116,8 @@ ds_kernel(const uint8_t *__restrict__ codes1, const uint16_t *__restrict__ plane
     constexpr int GPC = 8 / K;               // groups per 16-byte chunk
     constexpr int RB = DsShape<NSEG>::RB;
     constexpr int D = DsShape<NSEG>::D;
-    // PAIR (one codebook, and the activation pairs of all tokens fit in registers
-    // without spilling: batch 1 with NSEG <= 4, batch 2 with NSEG = 1):
+    // PAIR (one codebook; batch 1, or batch 2 with NSEG = 1; the activation pairs sit in
+    // registers when they fit without spilling, XREG, else they are read from LDS):
     // part (k, q, h) = position pair q of codebook k for code half h; LDS words
     // 0 .. kHalf-1 hold its pairs, word kHalf a zero (the other half's codes), then
     // the activation pairs x[b][8j + 2q .. +1].  Otherwise part (k, t) = position t,
@@ -125,6 +125,7 @@ ds_kernel(const uint8_t *__restrict__ codes1, const uint16_t *__restrict__ plane
     // x[b][8j + t]: read from LDS per token, one position per part reads half the
     // activation bytes of the pair form.
     constexpr bool PAIR = ds_pair_form(K, NB, NSEG);
+    constexpr bool XREG = PAIR && ds_pair_xreg(NB, NSEG);
     __shared__ __attribute__((aligned(16))) uint32_t lds[kDsLdsWords];
     uint32_t *const tab = lds;                                        // PAIR
     uint32_t *const xs = lds + kHalf + 4;                             // PAIR
@@ -224,8 +225,8 @@ ds_kernel(const uint8_t *__restrict__ codes1, const uint16_t *__restrict__ plane
     // PAIR: each lane's activation pairs (GPC per chunk position and token) stay in
     // registers; a token past the batch repeats the last one (its sums are not stored),
     // so the loads need no condition (a conditional one becomes a branch per load)
-    uint32_t xr[PAIR ? NSEG : 1][GPC][PAIR ? NB : 1];
-    if constexpr (PAIR) {
+    uint32_t xr[XREG ? NSEG : 1][GPC][XREG ? NB : 1];
+    if constexpr (XREG) {
 #pragma unroll
         for (int sg = 0; sg < NSEG; ++sg) {
             const int c = min(lane + kWave * sg, NC - 1);
@@ -270,10 +271,26 @@ ds_kernel(const uint8_t *__restrict__ codes1, const uint16_t *__restrict__ plane
                 }
 #pragma unroll
                 for (int b = 0; b < NB; ++b) {
+                    uint32_t xv[GPC];
+                    if constexpr (XREG) {
+#pragma unroll
+                        for (int g = 0; g < GPC; ++g) xv[g] = xr[seg][g][b];
+                    } else {
+                        // GPC * 4 bytes, 16-byte aligned (G is a multiple of GPC)
+                        const uint4 *xq = reinterpret_cast<const uint4 *>(xs + b * G + c * GPC);
+#pragma unroll
+                        for (int i = 0; i < GPC / 4; ++i) {
+                            const uint4 t4 = xq[i];
+                            xv[4 * i] = t4.x;
+                            xv[4 * i + 1] = t4.y;
+                            xv[4 * i + 2] = t4.z;
+                            xv[4 * i + 3] = t4.w;
+                        }
+                    }
                     float d = 0.0f;
 #pragma unroll
                     for (int g = 0; g < GPC; ++g)
-                        d = __builtin_amdgcn_fdot2(as_h2(v[g]), as_h2(xr[seg][g][b]), d, false);
+                        d = __builtin_amdgcn_fdot2(as_h2(v[g]), as_h2(xv[g]), d, false);
                     acc[r][b] += ok ? d : 0.0f;
                 }
             } else {
