@@ -22,6 +22,10 @@ constexpr int kGroup = 8;
 // (the fp32 fold of 8 codebooks per group), b8 335 -> 185.
 constexpr int kMfmaMinBatch = 2;
 constexpr int kMfmaMinBatch8Codebooks = 4;
+// Canonical 16-bit codes at small batches: the split kernel, its codebook packed into the
+// workspace on every call, against the L2-gather kernel and the matrix cores.
+constexpr int kSplitMaxBatch = 4;
+constexpr int kSplitMaxBatchGemm = 2;
 // Measured on MI355X (7B layer linears, canonical weights): the prefill path overtakes the
 // matrix-core kernels at batch 256 for 16-bit codes (decoding a 1 MiB codebook through
 // L2 per token tile costs more) and at 1024 for 8-bit codes with K <= 2.
@@ -167,6 +171,7 @@ bool supported_one(int variant, const aqlm::Problem &p) {
         case AQLM_VARIANT_L2: return aqlm::l2_supported(p);
         case AQLM_VARIANT_MFMA: return aqlm::mfma_supported(p);
         case AQLM_VARIANT_PREFILL: return aqlm::mfma_supported(p);
+        case AQLM_VARIANT_SPLIT: return aqlm::ds_supported(p);
         default: return false;
     }
 }
@@ -176,6 +181,10 @@ int choose(bool gemm, const aqlm::Problem &p) {
     if (forced != AQLM_VARIANT_AUTO && supported(forced, p)) return forced;
     if (gemm && p.batch >= prefill_min_batch(p) && supported(AQLM_VARIANT_PREFILL, p))
         return AQLM_VARIANT_PREFILL;
+    // 16-bit codes: the split kernel (codebook packed per call) up to batch 4, or 2 where
+    // the matrix cores are allowed
+    if (p.batch <= (gemm ? kSplitMaxBatchGemm : kSplitMaxBatch) && supported(AQLM_VARIANT_SPLIT, p))
+        return AQLM_VARIANT_SPLIT;
     if (gemm && p.batch >= mfma_min_batch(p.K) && supported(AQLM_VARIANT_MFMA, p))
         return AQLM_VARIANT_MFMA;
     if (supported(AQLM_VARIANT_LUT, p)) return AQLM_VARIANT_LUT;
@@ -311,6 +320,19 @@ aqlm_status_t run(int variant, const aqlm::Problem &p) {
                 }
             }
             e = aqlm::launch_mfma(p, ws);
+            break;
+        }
+        case AQLM_VARIANT_SPLIT: {
+            void *ws = nullptr;
+            e = get_workspace(p.stream, aqlm::split_canonical_workspace_bytes(p), &ws);
+            if (e != hipSuccess) break;
+            if (!ws) {
+                // capturing stream without a large enough workspace: the L2-gather kernel
+                if (log_enabled())
+                    std::fprintf(stderr, "[aqlm] split: no workspace on a capturing stream\n");
+                return run(supported(AQLM_VARIANT_L2, p) ? AQLM_VARIANT_L2 : AQLM_VARIANT_GENERIC, p);
+            }
+            e = aqlm::launch_split_canonical(p, ws);
             break;
         }
         case AQLM_VARIANT_PREFILL: {

@@ -528,6 +528,25 @@ pack_kernel(const uint16_t *__restrict__ cb, uint16_t *__restrict__ packed, int 
     }
 }
 
+// pack_kernel<2> for the codebooks of the matrices of segs (blockIdx.y = matrix m),
+// written to dst + m * K * 65536 * 8 halves
+__global__ void __launch_bounds__(256)
+pack_pairs_segs_kernel(const Segs segs, uint32_t *__restrict__ dst, int K) {
+    const int m = blockIdx.y;
+    const uint32_t *__restrict__ src = static_cast<const uint32_t *>(pick(segs.cb, m));
+    uint32_t *__restrict__ out = dst + size_t(m) * K * kEntries * 4;
+    const int64_t n = int64_t(K) * kEntries;
+    for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+         i += int64_t(gridDim.x) * blockDim.x) {
+        const int64_t kk = i / kEntries, c = i - kk * kEntries;
+        const uint4 v = reinterpret_cast<const uint4 *>(src)[i];   // entry c: 4 pairs
+        out[(kk * 4 + 0) * kEntries + c] = v.x;
+        out[(kk * 4 + 1) * kEntries + c] = v.y;
+        out[(kk * 4 + 2) * kEntries + c] = v.z;
+        out[(kk * 4 + 3) * kEntries + c] = v.w;
+    }
+}
+
 // the inverse of pack_kernel<W>
 template <int W>
 __global__ void __launch_bounds__(256)
@@ -719,6 +738,30 @@ hipError_t launch_ds(const Problem &p, void *workspace) {
     hipError_t e = p.K == 1 ? launch1<1>(p, c, segs, partial) : launch1<2>(p, c, segs, partial);
     if (e != hipSuccess) return e;
     return launch_partial_sum_segs(partial, segs, p.batch, p.K * 8, p.stream);
+}
+
+size_t split_canonical_pack_bytes(const Problem &p) {
+    return size_t(p.segs.n) * size_t(p.K) * kEntries * 16;
+}
+
+size_t split_canonical_workspace_bytes(const Problem &p) {
+    return split_canonical_pack_bytes(p) + ds_workspace_bytes(p);
+}
+
+// Canonical codebooks: each matrix's codebook is packed into position pairs in the
+// workspace (one launch for all matrices), then the split kernel runs on them.
+hipError_t launch_split_canonical(const Problem &p, void *workspace) {
+    uint32_t *pairs = static_cast<uint32_t *>(workspace);
+    const int64_t n = int64_t(p.K) * kEntries;
+    const int blocks = int((n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024);
+    hipLaunchKernelGGL(pack_pairs_segs_kernel, dim3(blocks, unsigned(p.segs.n)), dim3(256), 0,
+                       p.stream, p.segs, pairs, p.K);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    Problem q = p;
+    for (int m = 0; m < p.segs.n; ++m) q.segs.cb[m] = pairs + size_t(m) * p.K * kEntries * 4;
+    q.codebooks = q.segs.cb[0];
+    return launch_ds(q, static_cast<char *>(workspace) + split_canonical_pack_bytes(p));
 }
 
 hipError_t launch_pack_codebooks(const void *cb, void *planes, int K, int B, hipStream_t s) {

@@ -80,6 +80,9 @@ hipError_t launch_pack_codes_lut(const void *src, void *dst, int64_t out, int64_
 bool ds_supported(const Problem &p);
 size_t ds_workspace_bytes(const Problem &p);
 hipError_t launch_ds(const Problem &p, void *workspace);
+// the same from canonical codebooks (16-byte aligned): packed into the workspace first
+size_t split_canonical_workspace_bytes(const Problem &p);
+hipError_t launch_split_canonical(const Problem &p, void *workspace);
 bool dsm_supported(const Problem &p);
 size_t dsm_workspace_bytes(const Problem &p);
 hipError_t launch_dsm(const Problem &p, void *workspace);

@@ -77,8 +77,10 @@ typedef enum {
     AQLM_VARIANT_L2 = 4,      /* B = 16: codebook gathered through L2, batch <= 8            */
     AQLM_VARIANT_MFMA = 5,    /* decode to fp16 fragments + fp16 matrix cores, any batch;
                                  K in {1,2}, or K in {4,8} with B = 8; in/8 a multiple of 4 */
-    AQLM_VARIANT_SPLIT = 6,   /* B = 16, packed codebooks: a slice of the codebook per
-                                 CU, batch <= 16 (aqlm_gemv_packed only)                   */
+    AQLM_VARIANT_SPLIT = 6,   /* B = 16: a slice of the codebook per CU, batch <= 4
+                                 (packed codebooks, or canonical ones packed into the
+                                 stream's workspace on each call); aqlm_gemv_packed also
+                                 at batch 5..16 on the matrix cores                      */
     AQLM_VARIANT_PREFILL = 7  /* prefill-size batches: W decoded once to fp16 in the
                                  workspace, one hipBLASLt GEMM (fp32 accumulation); the
                                  same K, B and shapes as AQLM_VARIANT_MFMA               */
@@ -87,6 +89,10 @@ typedef enum {
 /*
  * y = W x for a batch of activation rows (token generation).  Picks a
  * gather/lookup kernel for the (K, B, batch, shape); never the matrix cores.
+ * 16-bit codes with K in {1,2} at batch <= 4 (aligned as AQLM_VARIANT_SPLIT needs)
+ * take the codebook-split kernel: the codebooks are packed into position pairs in
+ * the stream's workspace on each call (K MiB per matrix), then split over CUs; a
+ * capturing stream without a large enough workspace gets the L2-gather kernel.
  * Arguments: device pointers as laid out above; out_features, in_features >= 1
  * with in_features % 8 == 0; K in 1..8; B in {8, 16}; batch >= 1.
  */
@@ -95,9 +101,10 @@ aqlm_status_t aqlm_gemv(const void *codes, const void *codebooks, const void *x,
                         void *stream);
 
 /*
- * Same product and arguments as aqlm_gemv; from batch 2 (4 for eight codebooks;
- * AQLM_MFMA_MIN_BATCH overrides) it uses the decode-to-fp16 + MFMA kernels, at batch 1
- * it behaves as aqlm_gemv.  From
+ * Same product and arguments as aqlm_gemv; from batch 2 (4 for eight codebooks, 3 for
+ * 16-bit codes, which take the split kernel up to batch 2; AQLM_MFMA_MIN_BATCH overrides
+ * the first two) it uses the decode-to-fp16 + MFMA kernels, below that it behaves as
+ * aqlm_gemv.  From
  * prefill-size batches (256 for 16-bit codes or K >= 4, 1024 otherwise;
  * AQLM_PREFILL_MIN_BATCH overrides) W is instead decoded once into the stream's workspace as
  * dense fp16 (out*in*2 bytes plus 64 MiB of GEMM scratch, kept like every

@@ -174,8 +174,12 @@ def test_variant_choice_host_logic(lib):
     assert sel(0, 11008, 4096, 2, 8, 1) == "lut"
     assert sel(0, 4096, 11008, 2, 8, 1) == "lut"
     assert sel(0, 4096, 4096, 2, 8, 4) == "lds"
-    assert sel(0, 4096, 4096, 1, 16, 1) == "l2"
-    assert sel(0, 8192, 28672, 1, 16, 4) == "l2"
+    # 16-bit codes at small batches: the split kernel (codebook packed per call)
+    assert sel(0, 4096, 4096, 1, 16, 1) == "split"
+    assert sel(0, 8192, 28672, 1, 16, 4) == "split"
+    assert sel(0, 4096, 4096, 1, 16, 8) == "l2"
+    assert sel(1, 4096, 4096, 1, 16, 2) == "split"
+    assert sel(1, 4096, 4096, 1, 16, 4) == "mfma"
     assert sel(1, 4096, 4096, 2, 8, 16) == "mfma"
     assert sel(1, 4096, 4096, 1, 16, 128) == "mfma"
     assert sel(1, 4096, 4096, 2, 8, 8) == "mfma"

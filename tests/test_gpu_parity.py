@@ -60,7 +60,7 @@ def _variants_for(K, B, batch):
     if B == 8:
         v.append("lds")
     if B == 16:
-        v.append("l2")
+        v += ["l2", "split"]
     if K == 2 and B == 8 and batch == 1:
         v.append("lut")
     return v
@@ -114,8 +114,10 @@ def test_batches(aq, orc, batch, KB):
     check_y(aq.gemm(codes, cb, x), yref, f"gemm b={batch}")
     check_y(aq.gemv(codes, cb, x), yref, f"gemv b={batch}")
     check_y(aq.gemv_variant("mfma", codes, cb, x), yref, f"mfma b={batch}")
-    # aqlm_gemm takes the matrix cores from batch 2; aqlm_gemv never does
-    assert (aq.selected_variant(codes, cb, x, gemm=True) == "mfma") == (batch >= 2)
+    # aqlm_gemm takes the matrix cores from batch 2 (16-bit codes: from 3, the split kernel
+    # before); aqlm_gemv never does
+    want = batch >= (3 if B == 16 else 2)
+    assert (aq.selected_variant(codes, cb, x, gemm=True) == "mfma") == want
     assert aq.selected_variant(codes, cb, x, gemm=False) != "mfma"
 
 
