@@ -175,7 +175,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: this library has no multi-GPU path "
-              "(rows would shard with no exchange; see the design notes). Run with --gpus 1.",
+              "(each GPU would own a block of rows of W and needs no exchange). Run with --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
 
