@@ -687,3 +687,36 @@ def test_prefill_graph_replay(aq, orc, warm):
             check_y(y, yref, f"prefill graph {warm}")
             if eager is not None:
                 assert bool((y == eager).all())
+
+
+# ------------------------------------------------------------ the C ABI from plain C
+
+C_CHECK = [(300, 4096, 2, 8, 1), (257, 2048, 1, 16, 2), (256, 1024, 2, 8, 16)]
+
+
+@pytest.mark.parametrize("case", C_CHECK, ids=lambda c: "x".join(map(str, c)))
+def test_c_abi_program(aq, orc, case, tmp_path):
+    """tests/c_abi_check.c (built by build()) runs aqlm_gemv, aqlm_gemm and the packed
+    product from C with its own device buffers; its three y match the oracle."""
+    import os
+    import subprocess
+    exe = os.path.join(os.path.dirname(__file__), "c_abi_check")
+    if not os.path.exists(exe):
+        pytest.skip("tests/c_abi_check not built (build() compiles it)")
+    out, in_, K, B, batch = case
+    p = synth.make_problem(out, in_, K, B, batch=batch, sigma_cb=0.02, config=1700 + out)
+    src = tmp_path / "problem.bin"
+    with open(src, "wb") as f:
+        f.write(np.array([out, in_, K, B, batch], dtype=np.int64).tobytes())
+        f.write(np.ascontiguousarray(p["codes"]).tobytes())
+        f.write(np.ascontiguousarray(p["codebooks"]).tobytes())
+        f.write(np.ascontiguousarray(p["x"]).tobytes())
+    dst = tmp_path / "y.bin"
+    r = subprocess.run([exe, str(src), str(dst)], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stderr
+    ys = np.fromfile(dst, dtype=np.float16).reshape(3, batch, out)
+    yref = orc.gemv(p["codes"], p["codebooks"], p["x"], K, B)
+    for name, y in zip(("aqlm_gemv", "aqlm_gemm", "aqlm_gemv_packed"), ys):
+        assert np.all(np.isfinite(y)), name
+        e = rel_err(y, yref)
+        assert np.all(e <= TOL), f"{name} from C: max rel err {e.max():.3e}"
