@@ -170,6 +170,8 @@ lut_kernel(const uint16_t *__restrict__ x, float *__restrict__ partial, int G,
 // plane-major packed ones.  A workgroup's row range starts on an octet; wave w
 // takes the range's octets w, w + 16, w + 32, w + 48.
 constexpr int kOctetsPerWave = kRowsPerWave / 8;
+constexpr int kOctetsPerPass = kOctetsPerWave * kLutWaves;   // 64 octets = 512 rows
+constexpr int kMaxPasses = 8;
 
 template <int NS>
 __global__ void __launch_bounds__(kLutWaves * kWave)
@@ -228,6 +230,79 @@ lut_packed_kernel(const uint16_t *__restrict__ x, float *__restrict__ partial,
     }
 }
 
+// The same for row blocks of more than 512 rows: the block is walked in passes of 64
+// octets (wave w takes octets 64p + w + 16i), the tables built once and the next
+// pass's code tiles loaded while a pass is looked up (two register buffers, loads
+// from clamped octets, so none is conditional).  With 512-row blocks a large product
+// needs several rounds of workgroups, each building its tables again.
+template <int NS>
+__global__ void __launch_bounds__(kLutWaves * kWave)
+lut_packed_mp_kernel(const uint16_t *__restrict__ x, float *__restrict__ partial,
+                     int G, int rows_per_block, int nslices, const Segs segs) {
+    __shared__ __attribute__((aligned(16))) char lut[kLutBytes];
+
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int slice = blockIdx.x % nslices;
+    const int rb = blockIdx.x / nslices;
+    const int mi = seg_of<NS>(segs.n, segs.aux0, rb);
+    const int rblock = rb - pick(segs.aux0, mi);
+    const int out = pick(segs.row0, mi + 1) - pick(segs.row0, mi);
+    const u32x4 *__restrict__ pcodes = static_cast<const u32x4 *>(pick(segs.codes, mi));
+    const uint16_t *__restrict__ planes = static_cast<const uint16_t *>(pick(segs.cb, mi));
+    float *__restrict__ part = partial + size_t(slice) * seg_total<NS>(segs.n, segs.row0) + pick(segs.row0, mi);
+    const int j0 = slice * kSlice;
+    const int NQ = (out + 7) / 8;
+    const int r_begin = rblock * rows_per_block;             // a multiple of 8
+    const int r_end = min(out, r_begin + rows_per_block);
+    const int nq = (r_end - r_begin + 7) / 8;                 // >= 1
+    const int npass = (nq + kOctetsPerPass - 1) / kOctetsPerPass;
+
+    half4 a, bx[2];
+    load_build_operands<true>(planes, x, j0, G, wave, lane, a, bx);
+
+    const u32x4 *tile = pcodes + (size_t(slice) * NQ + r_begin / 8) * kWave + lane;
+    auto load_pass = [&](u32x4 (&code)[kOctetsPerWave], int pass) {
+#pragma unroll
+        for (int i = 0; i < kOctetsPerWave; ++i)
+            code[i] = __builtin_nontemporal_load(
+                tile + size_t(min(pass * kOctetsPerPass + wave + kLutWaves * i, nq - 1)) * kWave);
+    };
+    const uint32_t lanebase = (uint32_t(lane) << 2) | (1u << 16);
+    auto look_up = [&](const u32x4 (&code)[kOctetsPerWave], int pass) {
+#pragma unroll
+        for (int i = 0; i < kOctetsPerWave; i += 2) {
+            const int q0 = pass * kOctetsPerPass + wave + kLutWaves * i;
+            if (q0 >= nq) break;                                 // wave-uniform
+            float v[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const uint32_t w = code[i + r / 8][(r & 7) >> 1];
+                const bool hi = r & 1;
+                const uint32_t a0 = __builtin_amdgcn_perm(lanebase, w, hi ? 0x0C0C0204u : 0x0C0C0004u);
+                const uint32_t a1 = __builtin_amdgcn_perm(lanebase, w, hi ? 0x0C060304u : 0x0C060104u);
+                v[r] = lds_f32(lut, a0) + lds_f32(lut, a1);
+            }
+            const float sum = transpose_reduce<16>(v, lane);
+            const int vi = lane >> 2;
+            const int q = q0 + kLutWaves * (vi >> 3);
+            const int row = r_begin + 8 * q + (vi & 7);
+            if ((lane & 3) == 0 && q < nq && row < r_end) part[row] = sum;
+        }
+    };
+
+    u32x4 code[kOctetsPerWave], code2[kOctetsPerWave];
+    load_pass(code, 0);
+    store_tables(lut, a, bx, wave, lane);
+    __syncthreads();
+    for (int pass = 0; pass < npass; pass += 2) {
+        load_pass(code2, pass + 1);
+        look_up(code, pass);
+        load_pass(code, pass + 2);
+        if (pass + 1 < npass) look_up(code2, pass + 1);       // wave-uniform
+    }
+}
+
 // codes [out][G] (two 8-bit codes per 16-bit word) -> packed tiles; padding is code 0
 __global__ void __launch_bounds__(256)
 pack_codes_kernel(const uint16_t *__restrict__ codes, uint16_t *__restrict__ packed, int out,
@@ -274,13 +349,16 @@ LutCfg lut_cfg(const Problem &p, bool packed, Segs *segs = nullptr) {
     c.nslices = int((G + kSlice - 1) / kSlice);
     const int64_t max_rows = int64_t(kLutWaves) * kRowsPerWave;
     int64_t nrb = c.nslices >= 256 ? 1 : 256 / c.nslices;
-    const int64_t need = (p.out + max_rows - 1) / max_rows;
+    const int64_t most = max_rows * (packed ? kMaxPasses : 1);   // rows per block at most
+    const int64_t need = (p.out + most - 1) / most;
     if (nrb < need) nrb = need;
     int64_t rpb = (p.out + nrb - 1) / nrb;
     if (packed) rpb = (rpb + 7) / 8 * 8;                      // ranges start on an octet
     else rpb = (rpb + kLutWaves - 1) / kLutWaves * kLutWaves; // whole rows per wave
     if (rpb < kLutWaves) rpb = kLutWaves;
-    if (rpb > max_rows) rpb = max_rows;
+    // packed codes: up to kMaxPasses passes of 512 rows per block (one round of workgroups)
+    const int64_t cap = packed ? max_rows * kMaxPasses : max_rows;
+    if (rpb > cap) rpb = cap;
     // Each matrix of a grouped call gets whole blocks of its own; the blocks may not
     // outnumber nrb (a workgroup fills a CU's LDS: one more block column would run in
     // a second round), so the block grows until they fit.
@@ -290,7 +368,7 @@ LutCfg lut_cfg(const Problem &p, bool packed, Segs *segs = nullptr) {
         for (int m = 0; m < p.segs.n; ++m) t += (p.segs.row0[m + 1] - p.segs.row0[m] + r - 1) / r;
         return t;
     };
-    while (blocks(rpb) > nrb && rpb + unit <= max_rows) rpb += unit;
+    while (blocks(rpb) > nrb && rpb + unit <= cap) rpb += unit;
     c.rows_per_block = int(rpb);
     int64_t total = 0;
     for (int m = 0; m < p.segs.n; ++m) {
@@ -361,7 +439,18 @@ hipError_t launch_lut_packed(const Problem &p, void *workspace) {
     Segs segs = p.segs;
     const LutCfg c = lut_cfg(p, true, &segs);
     float *partial = static_cast<float *>(workspace);
-    if (segs.n == 1)
+    if (c.rows_per_block > kLutWaves * kRowsPerWave) {
+        if (segs.n == 1)
+            hipLaunchKernelGGL(lut_packed_mp_kernel<1>, dim3(c.nslices * c.nrblocks),
+                               dim3(kLutWaves * kWave), 0, p.stream,
+                               static_cast<const uint16_t *>(p.x), partial, int(p.in / kGroup),
+                               c.rows_per_block, c.nslices, segs);
+        else
+            hipLaunchKernelGGL(lut_packed_mp_kernel<kMaxSegs>, dim3(c.nslices * c.nrblocks),
+                               dim3(kLutWaves * kWave), 0, p.stream,
+                               static_cast<const uint16_t *>(p.x), partial, int(p.in / kGroup),
+                               c.rows_per_block, c.nslices, segs);
+    } else if (segs.n == 1)
         hipLaunchKernelGGL(lut_packed_kernel<1>, dim3(c.nslices * c.nrblocks),
                            dim3(kLutWaves * kWave), 0, p.stream,
                            static_cast<const uint16_t *>(p.x), partial, int(p.in / kGroup),

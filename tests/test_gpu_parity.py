@@ -426,6 +426,56 @@ def test_full_size_packed_sampled(aq, orc, case):
     assert np.all(e <= TOL), f"{case}: {e.max():.3e}"
 
 
+def _pass_rows(out, rows_per_block, seed):
+    """Sampled rows plus every row next to a 512-row pass boundary inside a row block."""
+    rows = set(_sampled_rows(out, seed=seed).tolist())
+    for b0 in range(0, out, rows_per_block):
+        for p0 in range(b0, min(out, b0 + rows_per_block), 512):
+            rows.update(r for r in (p0 - 1, p0, p0 + 1, p0 + 511) if 0 <= r < out)
+    return np.array(sorted(rows), dtype=np.int64)
+
+
+# 2x8 row blocks of more than 512 rows (the lookup-table kernel's multi-pass form):
+# out > 512 * (256 / slices), slices = in / 512
+MULTIPASS = [(4500, 16384), (4103, 16384), (28672, 8192), (2000, 65536)]
+
+
+@pytest.mark.parametrize("case", MULTIPASS, ids=lambda c: f"{c[0]}x{c[1]}")
+def test_packed_multipass(aq, orc, case):
+    import torch
+    out, in_ = case
+    p = synth.make_problem(out, in_, 2, 8, batch=1, sigma_cb=0.02, config=1800 + out)
+    codes, cb, x = _dev(p)
+    y = aq.gemv_packed(aq.pack_weights(codes, cb), x)
+    torch.cuda.synchronize()
+    slices = (in_ // 8 + 63) // 64
+    nrb = max(1, 256 // slices)
+    rows = _pass_rows(out, (-(-out // nrb) + 7) // 8 * 8, seed=out)   # blocks start on octets
+    yref = orc.gemv_rows(p["codes"], p["codebooks"], p["x"], 2, 8, rows)
+    e = rel_err(y.float().cpu().numpy()[:, rows], yref)
+    assert np.all(e <= TOL), f"{case}: {e.max():.3e}"
+
+
+def test_packed_grouped_multipass(aq, orc):
+    """Two matrices sharing x, one past the one-pass block size, in one grouped call."""
+    import torch
+    outs, in_ = (4099, 700), 16384
+    ps = [synth.make_problem(o, in_, 2, 8, batch=1, sigma_cb=0.02, config=1900 + i)
+          for i, o in enumerate(outs)]
+    x = torch.from_numpy(np.ascontiguousarray(ps[0]["x"])).cuda()
+    ws = []
+    for p in ps:
+        codes, cb, _ = _dev(p)
+        ws.append(aq.pack_weights(codes, cb))
+    ys = aq.gemv_packed_grouped(ws, x)
+    torch.cuda.synchronize()
+    for p, y, o in zip(ps, ys, outs):
+        rows = np.arange(o, dtype=np.int64)          # every row (the grouped blocks grow)
+        yref = orc.gemv_rows(p["codes"], p["codebooks"], ps[0]["x"], 2, 8, rows)
+        e = rel_err(y.float().cpu().numpy()[:, rows], yref)
+        assert np.all(e <= TOL), f"grouped {o}x{in_}: {e.max():.3e}"
+
+
 @pytest.mark.parametrize("batch", [1, 16, 40])
 @pytest.mark.parametrize("KB", [(1, 16), (2, 8)])
 def test_packed_graph_replay(aq, orc, KB, batch):
