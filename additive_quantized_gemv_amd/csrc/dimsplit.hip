@@ -126,6 +126,11 @@ ds_kernel(const uint8_t *__restrict__ codes1, const uint16_t *__restrict__ plane
     // activation bytes of the pair form.
     constexpr bool PAIR = ds_pair_form(K, NB, NSEG);
     constexpr bool XREG = PAIR && ds_pair_xreg(NB, NSEG);
+    // batch 1, pair form: chunks of RB rows handed out from an LDS counter, so the waves
+    // that the LDS serves first take more of them (with a fixed share per wave the last
+    // waves ended up to 5 us after the first, with the LDS idle meanwhile; 11008x4096:
+    // 15.2 -> 13.9 us per call measured on MI355X together with the lookahead below)
+    constexpr bool DYN = XREG && NB == 1;
     __shared__ __attribute__((aligned(16))) uint32_t lds[kDsLdsWords];
     uint32_t *const tab = lds;                                        // PAIR
     uint32_t *const xs = lds + kHalf + 4;                             // PAIR
@@ -197,6 +202,7 @@ ds_kernel(const uint8_t *__restrict__ codes1, const uint16_t *__restrict__ plane
 #pragma unroll
         for (int i = 0; i < PER; ++i) dst[threadIdx.x + i * kDsWaves * kWave] = tmp[i];
         if (threadIdx.x == 0) tab[kHalf] = 0u;
+        if (DYN && threadIdx.x == 0) lds[kHalf + 1] = kDsWaves;   // next free chunk
     } else {
         stage_plane(planes, k, t, tabh);
     }
@@ -216,6 +222,75 @@ ds_kernel(const uint8_t *__restrict__ codes1, const uint16_t *__restrict__ plane
     // byte address of a code's pair: 4*code - h*128 KiB, clamped to the zero word
     const uint32_t boff = h ? uint32_t(0) - uint32_t(kHalf * 4) : 0u;
     const char *tabb = reinterpret_cast<const char *>(tab);
+    if constexpr (DYN) {
+        // wave w starts with chunk w; each chunk takes the counter's next one, whose codes
+        // refill the ring slot by slot.  The first chunk is unconditional (clamped loads,
+        // masked stores): a loop entered behind a trip-count test lets the compiler sink
+        // the ring loads below the barrier.
+        const int nchunks = (r_end - r_begin + RB - 1) / RB;
+        uint32_t *const ctr = lds + kHalf + 1;
+        auto load_chunk = [&](int chunk, int s) -> u32x4 {
+            const int row = min(r_begin + min(chunk, nchunks - 1) * RB + s / NSEG, r_end - 1);
+            const uint8_t *rp = codes + size_t(row) * row_bytes;
+            return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(rp + lane_off[s % NSEG]));
+        };
+        u32x4 ring[D];
+#pragma unroll
+        for (int s = 0; s < D; ++s) {
+            ring[s] = load_chunk(wave, s);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        uint32_t xr[NSEG][GPC];
+#pragma unroll
+        for (int sg = 0; sg < NSEG; ++sg) {
+            const int c = min(lane + kWave * sg, NC - 1);
+#pragma unroll
+            for (int g = 0; g < GPC; ++g) xr[sg][g] = xs[c * GPC + g];
+        }
+        int cur = wave;
+        do {
+            uint32_t nx = 0;
+            if (lane == 0) nx = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            const int nxt = __builtin_amdgcn_readfirstlane(int(nx));
+            float acc[RB];
+#pragma unroll
+            for (int r = 0; r < RB; ++r) acc[r] = 0.0f;
+            // the lookups of slot s + 1 are issued before the products of slot s, so each
+            // wave keeps two slots of LDS reads in flight; the slot is refilled with the
+            // next chunk once its codes are consumed (in place, see the ring note below)
+            uint32_t vb[2][GPC];
+            auto look = [&](int s, uint32_t *v) {
+                const u32x4 cw = ring[s];
+#pragma unroll
+                for (int g = 0; g < GPC; ++g) {
+                    uint32_t byte = (g & 1) ? pair_byte_hi(cw[g >> 1], boff) : pair_byte_lo(cw[g >> 1], boff);
+                    byte = min(byte, uint32_t(kHalf * 4));
+                    v[g] = *reinterpret_cast<const uint32_t *>(tabb + byte);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                ring[s] = load_chunk(nxt, s);
+                __builtin_amdgcn_sched_barrier(0);
+            };
+            look(0, vb[0]);
+#pragma unroll
+            for (int s = 0; s < D; ++s) {
+                if (s + 1 < D) look(s + 1, vb[(s + 1) & 1]);
+                const uint32_t *v = vb[s & 1];
+                float d = 0.0f;
+#pragma unroll
+                for (int g = 0; g < GPC; ++g)
+                    d = __builtin_amdgcn_fdot2(as_h2(v[g]), as_h2(xr[s % NSEG][g]), d, false);
+                acc[s / NSEG] += lane_ok[s % NSEG] ? d : 0.0f;
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            const float sum = transpose_reduce<RB>(acc, lane);
+            const int row = r_begin + cur * RB + lane / (kWave / RB);
+            if ((lane & (kWave / RB - 1)) == 0 && row < r_end)
+                partial[size_t(p) * T + orow0 + row] = sum;
+            cur = nxt;
+        } while (cur < nchunks);
+        return;
+    }
     if (nitems == 0) return;
 
     u32x4 ring[D];
