@@ -49,9 +49,12 @@ constexpr int kEntries = 65536;
 constexpr int kHalf = kEntries / 2;     // code-space half of one batch-1 workgroup
 constexpr int kXPairs = 7168;           // in/8 activation pairs of one position pair (batch 1)
 constexpr int kXPlaneHalves = 14336;    // batch * in/8 activations of one position (batch 2..4)
+// words before the pair table: the batch-1 chunk counter, kept below 64 KiB (ds_append
+// takes its address from m0)
+constexpr int kCtrWords = 4;
 // LDS words of the batch <= 4 kernel: the larger of its two layouts
-constexpr int kDsLdsWords = (kHalf + 4 + kXPairs) > (kEntries / 2 + kXPlaneHalves / 2)
-                                ? (kHalf + 4 + kXPairs) : (kEntries / 2 + kXPlaneHalves / 2);
+constexpr int kDsLdsWords = (kCtrWords + kHalf + 4 + kXPairs) > (kEntries / 2 + kXPlaneHalves / 2)
+                                ? (kCtrWords + kHalf + 4 + kXPairs) : (kEntries / 2 + kXPlaneHalves / 2);
 // tokens of the matrix-core form: one 16-token tile (measured on MI355X against unpacking
 // and the canonical kernels: 1.3-6x faster at batches 5..8, even at 16, slower from 32)
 constexpr int kDsmMaxBatch = 16;
@@ -132,8 +135,8 @@ ds_kernel(const uint8_t *__restrict__ codes1, const uint16_t *__restrict__ plane
     // 15.2 -> 13.9 us per call measured on MI355X together with the lookahead below)
     constexpr bool DYN = XREG && NB == 1;
     __shared__ __attribute__((aligned(16))) uint32_t lds[kDsLdsWords];
-    uint32_t *const tab = lds;                                        // PAIR
-    uint32_t *const xs = lds + kHalf + 4;                             // PAIR
+    uint32_t *const tab = lds + kCtrWords;                            // PAIR
+    uint32_t *const xs = tab + kHalf + 4;                             // PAIR
     hf *const tabh = reinterpret_cast<hf *>(lds);                     // !PAIR
     hf *const xsh = reinterpret_cast<hf *>(lds + kEntries / 2);       // !PAIR
 
@@ -202,7 +205,7 @@ ds_kernel(const uint8_t *__restrict__ codes1, const uint16_t *__restrict__ plane
 #pragma unroll
         for (int i = 0; i < PER; ++i) dst[threadIdx.x + i * kDsWaves * kWave] = tmp[i];
         if (threadIdx.x == 0) tab[kHalf] = 0u;
-        if (DYN && threadIdx.x == 0) lds[kHalf + 1] = kDsWaves;   // next free chunk
+        if (DYN && threadIdx.x == 0) lds[0] = 2 * kDsWaves * kWave;   // next free chunk x 64
     } else {
         stage_plane(planes, k, t, tabh);
     }
@@ -223,12 +226,16 @@ ds_kernel(const uint8_t *__restrict__ codes1, const uint16_t *__restrict__ plane
     const uint32_t boff = h ? uint32_t(0) - uint32_t(kHalf * 4) : 0u;
     const char *tabb = reinterpret_cast<const char *>(tab);
     if constexpr (DYN) {
-        // wave w starts with chunk w; each chunk takes the counter's next one, whose codes
-        // refill the ring slot by slot.  The first chunk is unconditional (clamped loads,
-        // masked stores): a loop entered behind a trip-count test lets the compiler sink
-        // the ring loads below the barrier.
+        // wave w starts with chunks w and w + 16; each chunk takes the counter's next one for
+        // two chunks ahead, and the current next chunk's codes refill the ring slot by slot.
+        // The counter's value is read only after the chunk's last lookups: an atomic read at
+        // once waits for every LDS read queued before it, the other waves' included.  It is
+        // a ds_append (adds the 64 active lanes), which the compiler's atomic rewriting,
+        // with its immediate read of the result, leaves alone.  The
+        // first chunk is unconditional (clamped loads, masked stores): a loop entered behind
+        // a trip-count test lets the compiler sink the ring loads below the barrier.
         const int nchunks = (r_end - r_begin + RB - 1) / RB;
-        uint32_t *const ctr = lds + kHalf + 1;
+        uint32_t *const ctr = lds;
         auto load_chunk = [&](int chunk, int s) -> u32x4 {
             const int row = min(r_begin + min(chunk, nchunks - 1) * RB + s / NSEG, r_end - 1);
             const uint8_t *rp = codes + size_t(row) * row_bytes;
@@ -247,11 +254,10 @@ ds_kernel(const uint8_t *__restrict__ codes1, const uint16_t *__restrict__ plane
 #pragma unroll
             for (int g = 0; g < GPC; ++g) xr[sg][g] = xs[c * GPC + g];
         }
-        int cur = wave;
+        int cur = wave, nxt = wave + kDsWaves;
         do {
-            uint32_t nx = 0;
-            if (lane == 0) nx = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-            const int nxt = __builtin_amdgcn_readfirstlane(int(nx));
+            const int nx = __builtin_amdgcn_ds_append((__attribute__((address_space(3))) int *)(ctr));
+            __builtin_amdgcn_sched_barrier(0);
             float acc[RB];
 #pragma unroll
             for (int r = 0; r < RB; ++r) acc[r] = 0.0f;
@@ -283,11 +289,13 @@ ds_kernel(const uint8_t *__restrict__ codes1, const uint16_t *__restrict__ plane
                 acc[s / NSEG] += lane_ok[s % NSEG] ? d : 0.0f;
                 __builtin_amdgcn_sched_barrier(0);
             }
+            const int nxt2 = __builtin_amdgcn_readfirstlane(nx) / kWave;
             const float sum = transpose_reduce<RB>(acc, lane);
             const int row = r_begin + cur * RB + lane / (kWave / RB);
             if ((lane & (kWave / RB - 1)) == 0 && row < r_end)
                 partial[size_t(p) * T + orow0 + row] = sum;
             cur = nxt;
+            nxt = nxt2;
         } while (cur < nchunks);
         return;
     }
