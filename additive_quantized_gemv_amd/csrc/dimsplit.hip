@@ -129,11 +129,12 @@ ds_kernel(const uint8_t *__restrict__ codes1, const uint16_t *__restrict__ plane
     // activation bytes of the pair form.
     constexpr bool PAIR = ds_pair_form(K, NB, NSEG);
     constexpr bool XREG = PAIR && ds_pair_xreg(NB, NSEG);
-    // batch 1, pair form: chunks of RB rows handed out from an LDS counter, so the waves
+    // pair form with the activations in registers (batch 1, or 2 with one chunk position):
+    // chunks of RB rows handed out from an LDS counter, so the waves
     // that the LDS serves first take more of them (with a fixed share per wave the last
     // waves ended up to 5 us after the first, with the LDS idle meanwhile; 11008x4096:
     // 15.2 -> 13.9 us per call measured on MI355X together with the lookahead below)
-    constexpr bool DYN = XREG && NB == 1;
+    constexpr bool DYN = XREG;
     __shared__ __attribute__((aligned(16))) uint32_t lds[kDsLdsWords];
     uint32_t *const tab = lds + kCtrWords;                            // PAIR
     uint32_t *const xs = tab + kHalf + 4;                             // PAIR
@@ -247,20 +248,25 @@ ds_kernel(const uint8_t *__restrict__ codes1, const uint16_t *__restrict__ plane
             ring[s] = load_chunk(wave, s);
             __builtin_amdgcn_sched_barrier(0);
         }
-        uint32_t xr[NSEG][GPC];
+        // a token past the batch repeats the last one (its sums are not stored)
+        uint32_t xr[NSEG][GPC][NB];
 #pragma unroll
         for (int sg = 0; sg < NSEG; ++sg) {
             const int c = min(lane + kWave * sg, NC - 1);
 #pragma unroll
-            for (int g = 0; g < GPC; ++g) xr[sg][g] = xs[c * GPC + g];
+            for (int g = 0; g < GPC; ++g)
+#pragma unroll
+                for (int b = 0; b < NB; ++b) xr[sg][g][b] = xs[(NB == 1 ? 0 : min(b, batch - 1)) * G + c * GPC + g];
         }
         int cur = wave, nxt = wave + kDsWaves;
         do {
             const int nx = __builtin_amdgcn_ds_append((__attribute__((address_space(3))) int *)(ctr));
             __builtin_amdgcn_sched_barrier(0);
-            float acc[RB];
+            float acc[NB][RB];
 #pragma unroll
-            for (int r = 0; r < RB; ++r) acc[r] = 0.0f;
+            for (int b = 0; b < NB; ++b)
+#pragma unroll
+                for (int r = 0; r < RB; ++r) acc[b][r] = 0.0f;
             // the lookups of slot s + 1 are issued before the products of slot s, so each
             // wave keeps two slots of LDS reads in flight; the slot is refilled with the
             // next chunk once its codes are consumed (in place, see the ring note below)
@@ -282,18 +288,24 @@ ds_kernel(const uint8_t *__restrict__ codes1, const uint16_t *__restrict__ plane
             for (int s = 0; s < D; ++s) {
                 if (s + 1 < D) look(s + 1, vb[(s + 1) & 1]);
                 const uint32_t *v = vb[s & 1];
-                float d = 0.0f;
 #pragma unroll
-                for (int g = 0; g < GPC; ++g)
-                    d = __builtin_amdgcn_fdot2(as_h2(v[g]), as_h2(xr[s % NSEG][g]), d, false);
-                acc[s / NSEG] += lane_ok[s % NSEG] ? d : 0.0f;
+                for (int b = 0; b < NB; ++b) {
+                    float d = 0.0f;
+#pragma unroll
+                    for (int g = 0; g < GPC; ++g)
+                        d = __builtin_amdgcn_fdot2(as_h2(v[g]), as_h2(xr[s % NSEG][g][b]), d, false);
+                    acc[b][s / NSEG] += lane_ok[s % NSEG] ? d : 0.0f;
+                }
                 __builtin_amdgcn_sched_barrier(0);
             }
             const int nxt2 = __builtin_amdgcn_readfirstlane(nx) / kWave;
-            const float sum = transpose_reduce<RB>(acc, lane);
             const int row = r_begin + cur * RB + lane / (kWave / RB);
-            if ((lane & (kWave / RB - 1)) == 0 && row < r_end)
-                partial[size_t(p) * T + orow0 + row] = sum;
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                const float sum = transpose_reduce<RB>(acc[b], lane);
+                if ((lane & (kWave / RB - 1)) == 0 && row < r_end && (NB == 1 || b < batch))
+                    partial[(size_t(p) * (NB == 1 ? 1 : batch) + b) * T + orow0 + row] = sum;
+            }
             cur = nxt;
             nxt = nxt2;
         } while (cur < nchunks);
