@@ -49,12 +49,12 @@ constexpr int kEntries = 65536;
 constexpr int kHalf = kEntries / 2;     // code-space half of one batch-1 workgroup
 constexpr int kXPairs = 7168;           // in/8 activation pairs of one position pair (batch 1)
 constexpr int kXPlaneHalves = 14336;    // batch * in/8 activations of one position (batch 2..4)
-// words before the pair table: the batch-1 chunk counter, kept below 64 KiB (ds_append
-// takes its address from m0)
+// words before the tables: the row-chunk counter, kept below 64 KiB (ds_append takes its
+// address from m0)
 constexpr int kCtrWords = 4;
 // LDS words of the batch <= 4 kernel: the larger of its two layouts
-constexpr int kDsLdsWords = (kCtrWords + kHalf + 4 + kXPairs) > (kEntries / 2 + kXPlaneHalves / 2)
-                                ? (kCtrWords + kHalf + 4 + kXPairs) : (kEntries / 2 + kXPlaneHalves / 2);
+constexpr int kDsLdsWords = kCtrWords + ((kHalf + 4 + kXPairs) > (kEntries / 2 + kXPlaneHalves / 2)
+                                              ? (kHalf + 4 + kXPairs) : (kEntries / 2 + kXPlaneHalves / 2));
 // tokens of the matrix-core form: one 16-token tile (measured on MI355X against unpacking
 // and the canonical kernels: 1.3-6x faster at batches 5..8, even at 16, slower from 32)
 constexpr int kDsmMaxBatch = 16;
@@ -129,17 +129,15 @@ ds_kernel(const uint8_t *__restrict__ codes1, const uint16_t *__restrict__ plane
     // activation bytes of the pair form.
     constexpr bool PAIR = ds_pair_form(K, NB, NSEG);
     constexpr bool XREG = PAIR && ds_pair_xreg(NB, NSEG);
-    // pair form with the activations in registers (batch 1, or 2 with one chunk position):
-    // chunks of RB rows handed out from an LDS counter, so the waves
-    // that the LDS serves first take more of them (with a fixed share per wave the last
-    // waves ended up to 5 us after the first, with the LDS idle meanwhile; 11008x4096:
-    // 15.2 -> 13.9 us per call measured on MI355X together with the lookahead below)
-    constexpr bool DYN = XREG;
+    // Rows are handed out in chunks of RB from an LDS counter, so the waves that the LDS
+    // serves first take more of them (with a fixed share per wave the last waves ended up
+    // to 5 us after the first, with the LDS idle meanwhile; 11008x4096: 15.2 -> 13.9 us
+    // per call measured on MI355X together with the lookahead below).
     __shared__ __attribute__((aligned(16))) uint32_t lds[kDsLdsWords];
     uint32_t *const tab = lds + kCtrWords;                            // PAIR
     uint32_t *const xs = tab + kHalf + 4;                             // PAIR
-    hf *const tabh = reinterpret_cast<hf *>(lds);                     // !PAIR
-    hf *const xsh = reinterpret_cast<hf *>(lds + kEntries / 2);       // !PAIR
+    hf *const tabh = reinterpret_cast<hf *>(lds + kCtrWords);         // !PAIR
+    hf *const xsh = reinterpret_cast<hf *>(lds + kCtrWords + kEntries / 2);   // !PAIR
 
     // block -> (part, row range); the parts of a range share id % 8, i.e. an XCD
     const int id = blockIdx.x;
@@ -167,17 +165,12 @@ ds_kernel(const uint8_t *__restrict__ codes1, const uint16_t *__restrict__ plane
     const int NC = G / GPC;                  // chunks per row
     const int r_begin = lrr * rows_per_range;
     const int r_end = min(out, r_begin + rows_per_range);
-    const int rpw = (rows_per_range + kDsWaves - 1) / kDsWaves;
-    const int w_begin = r_begin + wave * rpw;
-    const int w_end = min(r_end, w_begin + rpw);
-    const int nitems = max(0, w_end - w_begin) * NSEG;
 
     // Branch-free loads: the row pointer is wave-uniform (scalar) and each lane adds
     // its chunk offset, clamped into the row; a conditional load would make the
-    // compiler wait for it at once.  Clamped lanes and items are masked where the
+    // compiler wait for it at once.  Clamped lanes and rows are masked where the
     // chunk is used.
     const size_t row_bytes = size_t(NC) * 16u;
-    const int nrows = max(1, w_end - w_begin);
     uint32_t lane_off[NSEG];
     bool lane_ok[NSEG];
 #pragma unroll
@@ -185,11 +178,6 @@ ds_kernel(const uint8_t *__restrict__ codes1, const uint16_t *__restrict__ plane
         lane_off[sg] = uint32_t(min(lane + kWave * sg, NC - 1)) * 16u;
         lane_ok[sg] = lane + kWave * sg < NC;
     }
-    auto load_item = [&](int item, int sg) -> u32x4 {
-        const int rowi = min(item / NSEG, nrows - 1);
-        const uint8_t *rp = codes + size_t(min(w_begin + rowi, out - 1)) * row_bytes;
-        return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(rp + lane_off[sg]));
-    };
 
     // The table gates all work, so it is staged first; code loads issued with it
     // would compete for the same bandwidth and delay it (about 2.5 us measured).
@@ -206,7 +194,6 @@ ds_kernel(const uint8_t *__restrict__ codes1, const uint16_t *__restrict__ plane
 #pragma unroll
         for (int i = 0; i < PER; ++i) dst[threadIdx.x + i * kDsWaves * kWave] = tmp[i];
         if (threadIdx.x == 0) tab[kHalf] = 0u;
-        if (DYN && threadIdx.x == 0) lds[0] = 2 * kDsWaves * kWave;   // next free chunk x 64
     } else {
         stage_plane(planes, k, t, tabh);
     }
@@ -222,107 +209,33 @@ ds_kernel(const uint8_t *__restrict__ codes1, const uint16_t *__restrict__ plane
                 else xsh[b * G + j] = __builtin_bit_cast(hf, src[t]);
             }
     }
+    if (threadIdx.x == 0) lds[0] = 2 * kDsWaves * kWave;   // next free row chunk x 64
     __syncthreads();
     // byte address of a code's pair: 4*code - h*128 KiB, clamped to the zero word
     const uint32_t boff = h ? uint32_t(0) - uint32_t(kHalf * 4) : 0u;
     const char *tabb = reinterpret_cast<const char *>(tab);
-    if constexpr (DYN) {
-        // wave w starts with chunks w and w + 16; each chunk takes the counter's next one for
-        // two chunks ahead, and the current next chunk's codes refill the ring slot by slot.
-        // The counter's value is read only after the chunk's last lookups: an atomic read at
-        // once waits for every LDS read queued before it, the other waves' included.  It is
-        // a ds_append (adds the 64 active lanes), which the compiler's atomic rewriting,
-        // with its immediate read of the result, leaves alone.  The
-        // first chunk is unconditional (clamped loads, masked stores): a loop entered behind
-        // a trip-count test lets the compiler sink the ring loads below the barrier.
-        const int nchunks = (r_end - r_begin + RB - 1) / RB;
-        uint32_t *const ctr = lds;
-        auto load_chunk = [&](int chunk, int s) -> u32x4 {
-            const int row = min(r_begin + min(chunk, nchunks - 1) * RB + s / NSEG, r_end - 1);
-            const uint8_t *rp = codes + size_t(row) * row_bytes;
-            return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(rp + lane_off[s % NSEG]));
-        };
-        u32x4 ring[D];
-#pragma unroll
-        for (int s = 0; s < D; ++s) {
-            ring[s] = load_chunk(wave, s);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        // a token past the batch repeats the last one (its sums are not stored)
-        uint32_t xr[NSEG][GPC][NB];
-#pragma unroll
-        for (int sg = 0; sg < NSEG; ++sg) {
-            const int c = min(lane + kWave * sg, NC - 1);
-#pragma unroll
-            for (int g = 0; g < GPC; ++g)
-#pragma unroll
-                for (int b = 0; b < NB; ++b) xr[sg][g][b] = xs[(NB == 1 ? 0 : min(b, batch - 1)) * G + c * GPC + g];
-        }
-        int cur = wave, nxt = wave + kDsWaves;
-        do {
-            const int nx = __builtin_amdgcn_ds_append((__attribute__((address_space(3))) int *)(ctr));
-            __builtin_amdgcn_sched_barrier(0);
-            float acc[NB][RB];
-#pragma unroll
-            for (int b = 0; b < NB; ++b)
-#pragma unroll
-                for (int r = 0; r < RB; ++r) acc[b][r] = 0.0f;
-            // the lookups of slot s + 1 are issued before the products of slot s, so each
-            // wave keeps two slots of LDS reads in flight; the slot is refilled with the
-            // next chunk once its codes are consumed (in place, see the ring note below)
-            uint32_t vb[2][GPC];
-            auto look = [&](int s, uint32_t *v) {
-                const u32x4 cw = ring[s];
-#pragma unroll
-                for (int g = 0; g < GPC; ++g) {
-                    uint32_t byte = (g & 1) ? pair_byte_hi(cw[g >> 1], boff) : pair_byte_lo(cw[g >> 1], boff);
-                    byte = min(byte, uint32_t(kHalf * 4));
-                    v[g] = *reinterpret_cast<const uint32_t *>(tabb + byte);
-                }
-                __builtin_amdgcn_sched_barrier(0);
-                ring[s] = load_chunk(nxt, s);
-                __builtin_amdgcn_sched_barrier(0);
-            };
-            look(0, vb[0]);
-#pragma unroll
-            for (int s = 0; s < D; ++s) {
-                if (s + 1 < D) look(s + 1, vb[(s + 1) & 1]);
-                const uint32_t *v = vb[s & 1];
-#pragma unroll
-                for (int b = 0; b < NB; ++b) {
-                    float d = 0.0f;
-#pragma unroll
-                    for (int g = 0; g < GPC; ++g)
-                        d = __builtin_amdgcn_fdot2(as_h2(v[g]), as_h2(xr[s % NSEG][g][b]), d, false);
-                    acc[b][s / NSEG] += lane_ok[s % NSEG] ? d : 0.0f;
-                }
-                __builtin_amdgcn_sched_barrier(0);
-            }
-            const int nxt2 = __builtin_amdgcn_readfirstlane(nx) / kWave;
-            const int row = r_begin + cur * RB + lane / (kWave / RB);
-#pragma unroll
-            for (int b = 0; b < NB; ++b) {
-                const float sum = transpose_reduce<RB>(acc[b], lane);
-                if ((lane & (kWave / RB - 1)) == 0 && row < r_end && (NB == 1 || b < batch))
-                    partial[(size_t(p) * (NB == 1 ? 1 : batch) + b) * T + orow0 + row] = sum;
-            }
-            cur = nxt;
-            nxt = nxt2;
-        } while (cur < nchunks);
-        return;
-    }
-    if (nitems == 0) return;
-
+    // Wave w starts with chunks w and w + 16; each chunk takes the counter's next one for
+    // two chunks ahead, and the current next chunk's codes refill the ring slot by slot.
+    // The counter's value is read only after the chunk's last lookups: an atomic read at
+    // once waits for every LDS read queued before it, the other waves' included.  It is
+    // a ds_append (adds the 64 active lanes), which the compiler's atomic rewriting, with
+    // its immediate read of the result, leaves alone.  The first chunk is unconditional
+    // (clamped loads, masked stores): a loop entered behind a trip-count test lets the
+    // compiler sink the ring loads below the barrier.
+    const int nchunks = (r_end - r_begin + RB - 1) / RB;
+    uint32_t *const ctr = lds;
+    auto load_chunk = [&](int chunk, int s) -> u32x4 {
+        const int row = min(r_begin + min(chunk, nchunks - 1) * RB + s / NSEG, r_end - 1);
+        const uint8_t *rp = codes + size_t(row) * row_bytes;
+        return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(rp + lane_off[s % NSEG]));
+    };
     u32x4 ring[D];
-    // issued slot by slot in the loop's own refill order (a reordered prologue makes
-    // the wait-count pass turn every wait in the loop into a wait for the whole ring)
 #pragma unroll
-    for (int q = 0; q < D; ++q) {
-        ring[q] = load_item(q, q % NSEG);
+    for (int s = 0; s < D; ++s) {
+        ring[s] = load_chunk(wave, s);
         __builtin_amdgcn_sched_barrier(0);
     }
-
-    // PAIR: each lane's activation pairs (GPC per chunk position and token) stay in
+    // XREG: each lane's activation pairs (GPC per chunk position and token) stay in
     // registers; a token past the batch repeats the last one (its sums are not stored),
     // so the loads need no condition (a conditional one becomes a branch per load)
     uint32_t xr[XREG ? NSEG : 1][GPC][XREG ? NB : 1];
@@ -338,38 +251,32 @@ ds_kernel(const uint8_t *__restrict__ codes1, const uint16_t *__restrict__ plane
         }
     }
     const uint32_t ksh = 16u * uint32_t(k);   // K = 2: codebook k's code is half k of a word
+    // looked-up values of one slot: pairs (PAIR) or plane halves
+    using VT = std::conditional_t<PAIR, uint32_t, hf>;
 
-    for (int base = 0; base < nitems; base += D) {
-        float acc[RB][NB];
+    int cur = wave, nxt = wave + kDsWaves;
+    do {
+        const int nx = __builtin_amdgcn_ds_append((__attribute__((address_space(3))) int *)(ctr));
+        __builtin_amdgcn_sched_barrier(0);
+        float acc[NB][RB];
 #pragma unroll
-        for (int r = 0; r < RB; ++r)
+        for (int b = 0; b < NB; ++b)
 #pragma unroll
-            for (int b = 0; b < NB; ++b) acc[r][b] = 0.0f;
+            for (int r = 0; r < RB; ++r) acc[b][r] = 0.0f;
+        // The lookups of slot s + 1 are issued before the products of slot s, so each wave
+        // keeps two slots of LDS reads in flight.  A slot is refilled with the next
+        // chunk's codes once its own are consumed, in place: a refill issued while the old
+        // value is still in use makes the compiler rotate the ring through register
+        // copies, and each copy waits for its load (measured: every iteration then waited
+        // for nearly the whole ring, 16.7 against 15.9 us per 11008x4096 1x16 call).
+        VT vb[2][GPC];
+        auto look = [&](int s, VT *v) {
+            const u32x4 cw = ring[s];
 #pragma unroll
-        for (int q = 0; q < D; ++q) {
-            const int item = base + q;
-            const u32x4 cw = ring[q];
-            const int r = q / NSEG;                        // compile-time
-            const int seg = q % NSEG;
-            // The slot is refilled (D items ahead) only once cw is dead, so the load lands
-            // in cw's own registers: a refill issued while cw is still in use makes the
-            // compiler rotate the ring through register copies, and each copy waits for
-            // its load, i.e. every iteration waited for nearly the whole ring (measured:
-            // 16.7 -> 15.9 us per 11008x4096 1x16 call once fixed).
-            auto refill = [&] {
-                __builtin_amdgcn_sched_barrier(0);
-                ring[q] = load_item(item + D, seg);
-                __builtin_amdgcn_sched_barrier(0);
-            };
-            const bool ok = item < nitems && lane_ok[seg];
-            const int c = min(lane + kWave * seg, NC - 1);
-            if constexpr (PAIR) {
-                // pairs of this chunk's codes (codebook k of each group), zero for the
-                // other half; code n = g*K + k of the chunk: word n/2 is g/2 (K = 1) or g
-                // (K = 2), known at compile time; only K = 2 selects the half at run time
-                uint32_t v[GPC];
-#pragma unroll
-                for (int g = 0; g < GPC; ++g) {
+            for (int g = 0; g < GPC; ++g) {
+                if constexpr (PAIR) {
+                    // pair of this code (codebook k of group g), zero for the other half;
+                    // code n = g*K + k of the chunk: word n/2 is g/2 (K = 1) or g (K = 2)
                     uint32_t byte;
                     if constexpr (K == 1)
                         byte = (g & 1) ? pair_byte_hi(cw[g >> 1], boff) : pair_byte_lo(cw[g >> 1], boff);
@@ -377,37 +284,7 @@ ds_kernel(const uint8_t *__restrict__ codes1, const uint16_t *__restrict__ plane
                         byte = pair_byte_lo(cw[g] >> ksh, boff);
                     byte = min(byte, uint32_t(kHalf * 4));
                     v[g] = *reinterpret_cast<const uint32_t *>(tabb + byte);
-                }
-                refill();
-#pragma unroll
-                for (int b = 0; b < NB; ++b) {
-                    uint32_t xv[GPC];
-                    if constexpr (XREG) {
-#pragma unroll
-                        for (int g = 0; g < GPC; ++g) xv[g] = xr[seg][g][b];
-                    } else {
-                        // GPC * 4 bytes, 16-byte aligned (G is a multiple of GPC)
-                        const uint4 *xq = reinterpret_cast<const uint4 *>(xs + b * G + c * GPC);
-#pragma unroll
-                        for (int i = 0; i < GPC / 4; ++i) {
-                            const uint4 t4 = xq[i];
-                            xv[4 * i] = t4.x;
-                            xv[4 * i + 1] = t4.y;
-                            xv[4 * i + 2] = t4.z;
-                            xv[4 * i + 3] = t4.w;
-                        }
-                    }
-                    float d = 0.0f;
-#pragma unroll
-                    for (int g = 0; g < GPC; ++g)
-                        d = __builtin_amdgcn_fdot2(as_h2(v[g]), as_h2(xv[g]), d, false);
-                    acc[r][b] += ok ? d : 0.0f;
-                }
-            } else {
-                // plane values of this chunk's codes, two per register for v_dot2
-                hf v[GPC];
-#pragma unroll
-                for (int g = 0; g < GPC; ++g) {
+                } else {
                     uint32_t code;
                     if constexpr (K == 1) {
                         const uint32_t w = cw[g >> 1];
@@ -417,35 +294,60 @@ ds_kernel(const uint8_t *__restrict__ codes1, const uint16_t *__restrict__ plane
                     }
                     v[g] = tabh[code];
                 }
-                refill();
-#pragma unroll
-                for (int b = 0; b < NB; ++b) {
-                    if (b < batch) {
-                        const hf *xp = xsh + b * G + c * GPC;
-                        float d = 0.0f;
-#pragma unroll
-                        for (int g = 0; g < GPC; g += 2)
-                            d = __builtin_amdgcn_fdot2(half2v{v[g], v[g + 1]}, half2v{xp[g], xp[g + 1]}, d, false);
-                        acc[r][b] += ok ? d : 0.0f;
-                    }
-                }
             }
+            __builtin_amdgcn_sched_barrier(0);
+            ring[s] = load_chunk(nxt, s);
+            __builtin_amdgcn_sched_barrier(0);
+        };
+        look(0, vb[0]);
+#pragma unroll
+        for (int s = 0; s < D; ++s) {
+            if (s + 1 < D) look(s + 1, vb[(s + 1) & 1]);
+            const VT *v = vb[s & 1];
+            const int seg = s % NSEG;
+            const int c = min(lane + kWave * seg, NC - 1);
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                float d = 0.0f;
+                if constexpr (XREG) {
+#pragma unroll
+                    for (int g = 0; g < GPC; ++g)
+                        d = __builtin_amdgcn_fdot2(as_h2(v[g]), as_h2(xr[seg][g][b]), d, false);
+                } else if constexpr (PAIR) {
+                    // GPC * 4 bytes, 16-byte aligned (G is a multiple of GPC)
+                    const uint4 *xq = reinterpret_cast<const uint4 *>(xs + b * G + c * GPC);
+#pragma unroll
+                    for (int i = 0; i < GPC / 4; ++i) {
+                        const uint4 t4 = xq[i];
+                        d = __builtin_amdgcn_fdot2(as_h2(v[4 * i]), as_h2(t4.x), d, false);
+                        d = __builtin_amdgcn_fdot2(as_h2(v[4 * i + 1]), as_h2(t4.y), d, false);
+                        d = __builtin_amdgcn_fdot2(as_h2(v[4 * i + 2]), as_h2(t4.z), d, false);
+                        d = __builtin_amdgcn_fdot2(as_h2(v[4 * i + 3]), as_h2(t4.w), d, false);
+                    }
+                } else if (b < batch) {
+                    const hf *xp = xsh + b * G + c * GPC;
+#pragma unroll
+                    for (int g = 0; g < GPC; g += 2)
+                        d = __builtin_amdgcn_fdot2(half2v{v[g], v[g + 1]}, half2v{xp[g], xp[g + 1]}, d, false);
+                }
+                acc[b][s / NSEG] += lane_ok[seg] ? d : 0.0f;
+            }
+            __builtin_amdgcn_sched_barrier(0);
         }
-        // rows base/NSEG .. +RB-1 of this wave, reduced together
-        const int row0 = w_begin + base / NSEG;
+        const int nxt2 = __builtin_amdgcn_readfirstlane(nx) / kWave;
+        // rows of chunk cur, RB of them reduced together
+        const int row = r_begin + cur * RB + lane / (kWave / RB);
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
             if (NB == 1 || b < batch) {
-                float v[RB];
-#pragma unroll
-                for (int r = 0; r < RB; ++r) v[r] = acc[r][b];
-                const float s = transpose_reduce<RB>(v, lane);
-                const int row = row0 + lane / (kWave / RB);
-                if ((lane & (kWave / RB - 1)) == 0 && row < w_end)
-                    partial[(size_t(p) * batch + b) * T + orow0 + row] = s;
+                const float sum = transpose_reduce<RB>(acc[b], lane);
+                if ((lane & (kWave / RB - 1)) == 0 && row < r_end)
+                    partial[(size_t(p) * (NB == 1 ? 1 : batch) + b) * T + orow0 + row] = sum;
             }
         }
-    }
+        cur = nxt;
+        nxt = nxt2;
+    } while (cur < nchunks);
 }
 
 // ------------------------------------------------------------------ batch 5 .. 128
