@@ -770,3 +770,29 @@ def test_c_abi_program(aq, orc, case, tmp_path):
         assert np.all(np.isfinite(y)), name
         e = rel_err(y, yref)
         assert np.all(e <= TOL), f"{name} from C: max rel err {e.max():.3e}"
+
+
+# The split kernel at its limits: 8 chunk positions per lane (the largest rows it
+# takes), the plane form's activation staging full (batch x in/8 = 14336 halves),
+# two codebooks, and the two-token pair form; row counts leave waves of a workgroup
+# without a first chunk (fewer chunks than waves) or with many.
+SPLIT_LIMITS = [
+    (300, 32768, 1, 16, 1),    # pair form, activation pairs read from LDS
+    (300, 32768, 1, 16, 3),    # plane form, 3 tokens
+    (77, 28672, 1, 16, 4),     # plane form, 4 x 3584 activations
+    (130, 16384, 2, 16, 1),    # two codebooks, 16 parts
+    (2000, 4096, 1, 16, 2),    # two tokens, activation pairs in registers
+]
+
+
+@pytest.mark.parametrize("case", SPLIT_LIMITS, ids=lambda c: "x".join(map(str, c)))
+def test_split_limits(aq, orc, case):
+    out, in_, K, B, batch = case
+    p = synth.make_problem(out, in_, K, B, batch=batch, sigma_cb=0.02, config=2100 + out + K)
+    codes, cb, x = _dev(p)
+    assert aq.variant_supported("split", codes, cb, x), case
+    yref = orc.gemv(p["codes"], p["codebooks"], p["x"], K, B)
+    ys = [aq.gemv_variant("split", codes, cb, x) for _ in range(2)]
+    check_y(ys[0], yref, f"split {case}")
+    assert bool((ys[0] == ys[1]).all())
+    check_y(aq.gemv_packed(aq.pack_weights(codes, cb), x), yref, f"packed {case}")
