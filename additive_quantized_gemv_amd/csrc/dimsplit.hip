@@ -29,11 +29,13 @@
 // * The K*8 workgroups of one row range get block ids that are equal modulo 8,
 //   so the dispatcher puts them on the same XCD: the codes come from HBM once and
 //   from that XCD's L2 for the other planes.
-// * Each wave walks its rows' 16-byte code chunks with several chunks in flight
-//   (a ring of 5..8 loads, issued branch-free); each looked-up pair is multiplied
-//   with v_dot2_f32_f16 against the matching activation pair x[b][8j + 2q .. +1],
-//   staged in LDS (in registers at batch 1).  Rows are summed across lanes several
-//   at a time by a transposing butterfly.
+// * The waves of a workgroup take the range's rows in chunks of 1..8 rows from an
+//   LDS counter (the waves the LDS serves first take more chunks).  A wave walks a
+//   chunk's 16-byte code pieces with the next chunk's in flight (a ring of 5..8
+//   loads, issued branch-free) and issues each slot's lookups one slot ahead of its
+//   products; each looked-up pair is multiplied with v_dot2_f32_f16 against the
+//   matching activation pair x[b][8j + 2q .. +1], staged in LDS (in registers when
+//   they fit).  A chunk's rows are summed across lanes by a transposing butterfly.
 // * Per-workgroup row sums go to a workspace; a second kernel adds the K*8 parts
 //   in order and writes fp16 y.
 #include <type_traits>
