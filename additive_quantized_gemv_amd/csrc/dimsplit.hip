@@ -133,8 +133,8 @@ ds_kernel(const uint8_t *__restrict__ codes1, const uint16_t *__restrict__ plane
     constexpr bool XREG = PAIR && ds_pair_xreg(NB, NSEG);
     // Rows are handed out in chunks of RB from an LDS counter, so the waves that the LDS
     // serves first take more of them (with a fixed share per wave the last waves ended up
-    // to 5 us after the first, with the LDS idle meanwhile; 11008x4096: 15.2 -> 13.9 us
-    // per call measured on MI355X together with the lookahead below).
+    // to 5 us after the first, with the LDS idle meanwhile; 1x16 11008x4096 on MI355X,
+    // together with the lookahead below: 15.9 -> 15.3 us per call with the part sums).
     __shared__ __attribute__((aligned(16))) uint32_t lds[kDsLdsWords];
     uint32_t *const tab = lds + kCtrWords;                            // PAIR
     uint32_t *const xs = tab + kHalf + 4;                             // PAIR
