@@ -237,37 +237,48 @@ __m512 dec_pair(const C *cr, const uint16_t *cb, int64_t entries, int64_t j) {
     return v;
 }
 
-template <int K, typename C>
+// NB tokens of one row at once: each decoded group pair is used for every token
+// (xf holds the tokens' activations `in` apart); per token the sums are formed exactly
+// as with one token.
+template <int K, int NB, typename C>
 __attribute__((target("avx512f")))
-float row_dec_avx512(const C *codes, const uint16_t *cb, int64_t entries, const float *xf, int64_t G,
-                     int64_t o) {
+void row_dec_avx512(const C *codes, const uint16_t *cb, int64_t entries, const float *xf, int64_t G,
+                    int64_t o, float *s) {
     const C *cr = codes + o * G * K;
-    __m512 acc0 = _mm512_setzero_ps(), acc1 = _mm512_setzero_ps();
+    const int64_t in = G * kGroup;
+    __m512 acc0[NB], acc1[NB];
+    for (int b = 0; b < NB; ++b) acc0[b] = acc1[b] = _mm512_setzero_ps();
     int64_t j = 0;
     for (; j + 4 <= G; j += 4) {
-        acc0 = _mm512_fmadd_ps(dec_pair<K>(cr, cb, entries, j), _mm512_loadu_ps(xf + j * kGroup), acc0);
-        acc1 = _mm512_fmadd_ps(dec_pair<K>(cr, cb, entries, j + 2), _mm512_loadu_ps(xf + (j + 2) * kGroup), acc1);
+        const __m512 v0 = dec_pair<K>(cr, cb, entries, j), v1 = dec_pair<K>(cr, cb, entries, j + 2);
+        for (int b = 0; b < NB; ++b) {
+            acc0[b] = _mm512_fmadd_ps(v0, _mm512_loadu_ps(xf + b * in + j * kGroup), acc0[b]);
+            acc1[b] = _mm512_fmadd_ps(v1, _mm512_loadu_ps(xf + b * in + (j + 2) * kGroup), acc1[b]);
+        }
     }
     if (j + 2 <= G) {
-        acc0 = _mm512_fmadd_ps(dec_pair<K>(cr, cb, entries, j), _mm512_loadu_ps(xf + j * kGroup), acc0);
+        const __m512 v0 = dec_pair<K>(cr, cb, entries, j);
+        for (int b = 0; b < NB; ++b)
+            acc0[b] = _mm512_fmadd_ps(v0, _mm512_loadu_ps(xf + b * in + j * kGroup), acc0[b]);
         j += 2;
     }
-    float s = _mm512_reduce_add_ps(_mm512_add_ps(acc0, acc1));
+    for (int b = 0; b < NB; ++b) s[b] = _mm512_reduce_add_ps(_mm512_add_ps(acc0[b], acc1[b]));
     if (j < G) {
         float w[8] = {};
         for (int k = 0; k < K; ++k) {
             const uint16_t *v = cb + (k * entries + cr[j * K + k]) * kGroup;
             for (int t = 0; t < 8; ++t) w[t] += h2f(v[t]);
         }
-        for (int t = 0; t < 8; ++t) s += w[t] * xf[j * kGroup + t];
+        for (int b = 0; b < NB; ++b)
+            for (int t = 0; t < 8; ++t) s[b] += w[t] * xf[b * in + j * kGroup + t];
     }
-    return s;
 }
 
-template <int K, typename C>
-float row_dec_avx2(const C *codes, const uint16_t *cb, int64_t entries, const float *xf, int64_t G,
-                   int64_t o) {
+template <int K, int NB, typename C>
+void row_dec_avx2(const C *codes, const uint16_t *cb, int64_t entries, const float *xf, int64_t G,
+                  int64_t o, float *s) {
     const C *cr = codes + o * G * K;
+    const int64_t in = G * kGroup;
     auto one = [&](int64_t j) {
         __m256 v = _mm256_setzero_ps();
         for (int k = 0; k < K; ++k)
@@ -275,14 +286,22 @@ float row_dec_avx2(const C *codes, const uint16_t *cb, int64_t entries, const fl
                                      cb + (k * entries + cr[j * K + k]) * kGroup))));
         return v;
     };
-    __m256 acc0 = _mm256_setzero_ps(), acc1 = _mm256_setzero_ps();
+    __m256 acc0[NB], acc1[NB];
+    for (int b = 0; b < NB; ++b) acc0[b] = acc1[b] = _mm256_setzero_ps();
     int64_t j = 0;
     for (; j + 2 <= G; j += 2) {
-        acc0 = _mm256_fmadd_ps(one(j), _mm256_loadu_ps(xf + j * kGroup), acc0);
-        acc1 = _mm256_fmadd_ps(one(j + 1), _mm256_loadu_ps(xf + (j + 1) * kGroup), acc1);
+        const __m256 v0 = one(j), v1 = one(j + 1);
+        for (int b = 0; b < NB; ++b) {
+            acc0[b] = _mm256_fmadd_ps(v0, _mm256_loadu_ps(xf + b * in + j * kGroup), acc0[b]);
+            acc1[b] = _mm256_fmadd_ps(v1, _mm256_loadu_ps(xf + b * in + (j + 1) * kGroup), acc1[b]);
+        }
     }
-    if (j < G) acc0 = _mm256_fmadd_ps(one(j), _mm256_loadu_ps(xf + j * kGroup), acc0);
-    return hsum256(_mm256_add_ps(acc0, acc1));
+    if (j < G) {
+        const __m256 v0 = one(j);
+        for (int b = 0; b < NB; ++b)
+            acc0[b] = _mm256_fmadd_ps(v0, _mm256_loadu_ps(xf + b * in + j * kGroup), acc0[b]);
+    }
+    for (int b = 0; b < NB; ++b) s[b] = hsum256(_mm256_add_ps(acc0[b], acc1[b]));
 }
 
 // ------------------------------------------------------------------ 2x8: pair codebook
@@ -298,11 +317,24 @@ void pair_codebook(const uint16_t *cb, int c1_begin, int c1_end, uint16_t *P) {
     }
 }
 
+template <int K, int NB, typename C>
+void row_dec_nb(Isa isa, const C *codes, const uint16_t *cb, int64_t entries, const float *xf,
+                int64_t G, int64_t o, float *s) {
+    if (isa == kAvx512) row_dec_avx512<K, NB>(codes, cb, entries, xf, G, o, s);
+    else row_dec_avx2<K, NB>(codes, cb, entries, xf, G, o, s);
+}
+
+// nb (1..kDecTokens) tokens of row o
+constexpr int kDecTokens = 4;
 template <int K, typename C>
-float row_dec(Isa isa, const C *codes, const uint16_t *cb, int64_t entries, const float *xf, int64_t G,
-              int64_t o) {
-    return isa == kAvx512 ? row_dec_avx512<K>(codes, cb, entries, xf, G, o)
-                          : row_dec_avx2<K>(codes, cb, entries, xf, G, o);
+void row_dec(Isa isa, const C *codes, const uint16_t *cb, int64_t entries, const float *xf, int64_t G,
+             int64_t o, int nb, float *s) {
+    switch (nb) {
+        case 1: row_dec_nb<K, 1>(isa, codes, cb, entries, xf, G, o, s); break;
+        case 2: row_dec_nb<K, 2>(isa, codes, cb, entries, xf, G, o, s); break;
+        case 3: row_dec_nb<K, 3>(isa, codes, cb, entries, xf, G, o, s); break;
+        default: row_dec_nb<K, 4>(isa, codes, cb, entries, xf, G, o, s); break;
+    }
 }
 
 aqlm_status_t cpu_gemv(const void *codes_, const void *codebooks_, const void *x_, void *y_,
@@ -330,16 +362,21 @@ aqlm_status_t cpu_gemv(const void *codes_, const void *codebooks_, const void *x
         for (int c1 = 0; c1 < 256; c1 += 16) pair_codebook(cb, c1, c1 + 16, P.data());
     }
 
-    std::vector<float> xf(static_cast<size_t>(in));
+    // the decode paths take up to kDecTokens tokens per pass over the codes; the table
+    // and scalar paths one
+    const bool dec = !lut && !(B == 16 && K > 2);
+    const int tb = dec ? kDecTokens : 1;
+    std::vector<float> xf(size_t(tb) * size_t(in));
     std::vector<float> cbt(lut ? size_t(K) * 8 * 256 : 0);
     if (lut) transpose_cb8(cb, K, cbt.data());
     std::vector<float> T(lut ? size_t(E) * 256 : 0);
-    std::vector<float> acc(static_cast<size_t>(out));
+    std::vector<float> acc(size_t(tb) * size_t(out));
     // per-thread lane sums of one row block
     const size_t vacc_rows = lut ? size_t(lut_block_rows(E)) : 0;
     std::vector<float> vacc(size_t(nt) * vacc_rows * 16);
-    for (int b = 0; b < batch; ++b) {
-        for (int64_t i = 0; i < in; ++i) xf[i] = h2f(x[int64_t(b) * in + i]);
+    for (int b0 = 0; b0 < batch; b0 += tb) {
+        const int nb = std::min(tb, batch - b0);
+        for (int64_t i = 0; i < int64_t(nb) * in; ++i) xf[i] = h2f(x[int64_t(b0) * in + i]);
 #pragma omp parallel num_threads(nt)
         {
             const int tid = omp_get_thread_num(), nth = omp_get_num_threads();
@@ -358,22 +395,24 @@ aqlm_status_t cpu_gemv(const void *codes_, const void *codebooks_, const void *x
                 }
             } else {
                 for (int64_t o = o0; o < o1; ++o) {
-                    float s;
+                    float sb[kDecTokens];
                     if (pair)   // the two code bytes of a group as one 16-bit index
-                        s = row_dec<1>(isa, c16, P.data(), 65536, xf.data(), G, o);
+                        row_dec<1>(isa, c16, P.data(), 65536, xf.data(), G, o, nb, sb);
                     else if (B == 8)
-                        s = row_dec<1>(isa, codes, cb, 256, xf.data(), G, o);
+                        row_dec<1>(isa, codes, cb, 256, xf.data(), G, o, nb, sb);
                     else if (K == 1)
-                        s = row_dec<1>(isa, c16, cb, 65536, xf.data(), G, o);
+                        row_dec<1>(isa, c16, cb, 65536, xf.data(), G, o, nb, sb);
                     else if (K == 2)
-                        s = row_dec<2>(isa, c16, cb, 65536, xf.data(), G, o);
+                        row_dec<2>(isa, c16, cb, 65536, xf.data(), G, o, nb, sb);
                     else
-                        s = row_dot_scalar(c16, cb, xf.data(), G, K, o);
-                    acc[o] = s;
+                        sb[0] = row_dot_scalar(c16, cb, xf.data(), G, K, o);
+                    for (int b = 0; b < nb; ++b) acc[size_t(b) * out + o] = sb[b];
                 }
             }
         }
-        for (int64_t o = 0; o < out; ++o) y[int64_t(b) * out + o] = f2h(acc[o]);
+        for (int b = 0; b < nb; ++b)
+            for (int64_t o = 0; o < out; ++o)
+                y[int64_t(b0 + b) * out + o] = f2h(acc[size_t(b) * out + o]);
     }
     return AQLM_OK;
 }

@@ -142,3 +142,18 @@ def test_cpu_gemv_rejects_bad_arguments(aq):
         y = torch.empty(8, dtype=torch.float16)
         assert lib.aqlm_cpu_gemv(codes.data_ptr(), cb.data_ptr(), x.data_ptr(), y.data_ptr(),
                                  out, in_, K, B, batch, 1) == 1
+
+
+@pytest.mark.parametrize("KB", [(2, 8), (1, 8), (1, 16), (2, 16)])
+def test_cpu_gemv_token_blocks_match_single_tokens(aq, KB):
+    """The decode paths take up to 4 tokens per pass over the codes; each token's sums are
+    formed as with one token, so batch 5 (a block of 4 and one more) equals the tokens
+    computed one at a time, bit for bit."""
+    import torch
+    K, B = KB
+    p = synth.make_problem(97, 1032, K, B, batch=5, sigma_cb=0.05, config=37, copy=K * 10 + B)
+    codes, cb, x = _host(p)
+    y = aq.cpu_gemv(codes, cb, x).numpy()
+    for b in range(5):
+        yb = aq.cpu_gemv(codes, cb, x[b:b + 1].contiguous()).numpy()
+        assert np.array_equal(y[b], yb[0]), (KB, b)
