@@ -190,11 +190,14 @@ ds_kernel(const uint8_t *__restrict__ codes1, const uint16_t *__restrict__ plane
             reinterpret_cast<const uint32_t *>(planes) + (size_t(k) * 4 + q) * kEntries + size_t(h) * kHalf);
         uint4 *dst = reinterpret_cast<uint4 *>(tab);
         constexpr int PER = kHalf / 4 / (kDsWaves * kWave);
-        uint4 tmp[PER];
+        // straight from global memory into LDS (global_load_lds_dwordx4: lane l's 16
+        // bytes land at the wave's LDS base + 16 l), no round trip through registers
 #pragma unroll
-        for (int i = 0; i < PER; ++i) tmp[i] = src[threadIdx.x + i * kDsWaves * kWave];
-#pragma unroll
-        for (int i = 0; i < PER; ++i) dst[threadIdx.x + i * kDsWaves * kWave] = tmp[i];
+        for (int i = 0; i < PER; ++i)
+            __builtin_amdgcn_global_load_lds(
+                (const __attribute__((address_space(1))) void *)(src + threadIdx.x + i * kDsWaves * kWave),
+                (__attribute__((address_space(3))) void *)(dst + (threadIdx.x & ~(kWave - 1)) + i * kDsWaves * kWave),
+                16, 0, 0);
         if (threadIdx.x == 0) tab[kHalf] = 0u;
     } else {
         stage_plane(planes, k, t, tabh);
