@@ -183,10 +183,13 @@ aqlm_status_t aqlm_unpack_codes(const void *packed, void *codes, int64_t out_fea
 /*
  * The product of aqlm_gemv from packed weights: codes from aqlm_pack_codes,
  * codebooks from aqlm_pack_codebooks.  Same y, same argument rules.
- * - 16-bit codes, K in {1,2}, batch <= 4: the position-split kernel
- *   (AQLM_VARIANT_SPLIT): each of K*8 workgroups per row range holds one position
- *   pair of one codebook for one half of the code space in LDS (codes of the other
- *   half read a zero word), and a second kernel adds their partial sums.
+ * - 16-bit codes, K in {1,2}, batch <= 4, in_features <= 32768 / K (and batch x
+ *   in_features/8 <= 14336 at batch 3..4): the position-split kernel
+ *   (AQLM_VARIANT_SPLIT).  With one codebook at batch 1 (or 2 with in_features <=
+ *   4096) each of the 8 workgroups of a row range holds one position pair for one
+ *   half of the code space in LDS (codes of the other half read a zero word);
+ *   otherwise each of K*8 workgroups holds one position of one codebook.  A second
+ *   kernel adds their partial sums.
  * - 16-bit codes, batch 5..16 (K = 1) or 5..8 (K = 2), in_features a multiple of 64,
  *   16-byte aligned pointers: the same split on the matrix cores, one position per
  *   workgroup (taken from the pairs while the table is staged; a small kernel first
