@@ -796,3 +796,20 @@ def test_split_limits(aq, orc, case):
     check_y(ys[0], yref, f"split {case}")
     assert bool((ys[0] == ys[1]).all())
     check_y(aq.gemv_packed(aq.pack_weights(codes, cb), x), yref, f"packed {case}")
+
+
+# Row ranges that end inside a row chunk: 4099 rows = 31 ranges of 129 (chunks of 2
+# rows, the last of 1) and one of 100; 1001 rows = 31 ranges of 32 (chunks of 8) and
+# one of 9 (a chunk of 8 and one of 1).
+SPLIT_RAGGED = [(4099, 11008, 1), (1001, 4096, 1), (1001, 4096, 2), (1001, 11008, 3)]
+
+
+@pytest.mark.parametrize("case", SPLIT_RAGGED, ids=lambda c: "x".join(map(str, c)))
+def test_split_ragged_chunks(aq, orc, case):
+    out, in_, batch = case
+    p = synth.make_problem(out, in_, 1, 16, batch=batch, sigma_cb=0.02, config=2200 + out + batch)
+    codes, cb, x = _dev(p)
+    assert aq.variant_supported("split", codes, cb, x), case
+    yref = orc.gemv(p["codes"], p["codebooks"], p["x"], 1, 16)
+    check_y(aq.gemv_variant("split", codes, cb, x), yref, f"split {case}")
+    check_y(aq.gemv_packed(aq.pack_weights(codes, cb), x), yref, f"packed {case}")
