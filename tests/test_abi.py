@@ -206,3 +206,21 @@ def test_python_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(aq, "_lib", None)
     with pytest.raises(ImportError):
         aq._load()
+
+
+def test_traffic_record_keyed_on_code_not_comments():
+    """bench.py reports measured HBM traffic only while the kernel source hashes as it did
+    when the counters were taken; the hash covers the code with comments and whitespace
+    removed, so a comment edit keeps the record and a code edit voids it."""
+    import importlib.util
+    import os
+    spec = importlib.util.spec_from_file_location(
+        "bench_mod", os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "bench.py"))
+    bench = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(bench)
+    a = b"int f(int x) { return x + 1; }  // add one\n/* a block\n   comment */\n"
+    b = b"int f(int x)\n{\n    return x + 1;   // a different comment\n}\n"
+    c = b"int f(int x) { return x + 2; }\n"
+    assert bench.code_text(a) == bench.code_text(b)
+    assert bench.code_text(a) != bench.code_text(c)
+    assert len(bench.source_sha("split")) == 16
