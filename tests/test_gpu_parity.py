@@ -741,7 +741,8 @@ def test_prefill_graph_replay(aq, orc, warm):
 
 # ------------------------------------------------------------ the C ABI from plain C
 
-C_CHECK = [(300, 4096, 2, 8, 1), (257, 2048, 1, 16, 2), (256, 1024, 2, 8, 16)]
+C_CHECK = [(300, 4096, 2, 8, 1), (1001, 4096, 1, 16, 1), (257, 2048, 1, 16, 2), (130, 2048, 2, 16, 1),
+           (256, 1024, 2, 8, 16)]
 
 
 @pytest.mark.parametrize("case", C_CHECK, ids=lambda c: "x".join(map(str, c)))
