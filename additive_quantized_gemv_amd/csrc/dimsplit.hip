@@ -107,8 +107,11 @@ constexpr bool ds_pair_xreg(int nb, int nseg) { return nb * nseg <= 4; }
 
 template <int NSEG>
 struct DsShape {
-    // rows reduced together, and code chunks in flight per lane (a multiple of NSEG)
-    static constexpr int RB = NSEG <= 1 ? 8 : NSEG <= 2 ? 4 : NSEG <= 4 ? 2 : 1;
+    // rows per chunk (reduced together), and code chunks in flight per lane (a multiple
+    // of NSEG).  Measured on MI355X at one chunk position (1x16 11008x4096): chunks of 4
+    // rows 13.8 us per call, of 8 rows 14.9 (the last round of chunks leaves waves
+    // idle longer), of 2 rows 15.1 (too few rows in flight)
+    static constexpr int RB = NSEG <= 2 ? 4 : NSEG <= 4 ? 2 : 1;
     static constexpr int D = NSEG * RB;
 };
 
