@@ -21,7 +21,7 @@ __all__ = ["gemv", "gemm", "gemv_variant", "gemv_packed", "pack_codebooks", "unp
            "gemv_grouped", "gemm_grouped", "gemv_packed_grouped",
            "dequantize", "bits_per_weight", "codes_bytes",
            "codebooks_bytes", "variant_supported", "selected_variant", "VARIANTS", "library_path",
-           "AqlmError", "version"]
+           "AqlmError", "version", "workspace_bytes", "grouped_workspace_bytes", "OPS"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libaqlm_mi355x.so")
@@ -29,6 +29,7 @@ LIB_PATH = os.path.join(_PKG, "libaqlm_mi355x.so")
 VARIANTS = {"auto": 0, "generic": 1, "lds": 2, "lut": 3, "l2": 4, "mfma": 5, "split": 6,
             "prefill": 7}
 _STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "HIP error"}
+OPS = {"gemv": 0, "gemm": 1, "gemv_packed": 2}
 
 
 class AqlmError(RuntimeError):
@@ -55,20 +56,25 @@ def _load():
                           "(hipcc --offload-arch=gfx950)")
     lib = ctypes.CDLL(LIB_PATH)
     vp, i64, ci = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
-    prod = [vp, vp, vp, vp, i64, i64, ci, ci, ci, vp]
-    for name in ("aqlm_gemv", "aqlm_gemm"):
+    # codes, codebooks, x, y, out, in, K, B, batch, workspace, workspace_bytes, stream
+    prod = [vp, vp, vp, vp, i64, i64, ci, ci, ci, vp, i64, vp]
+    for name in ("aqlm_gemv", "aqlm_gemm", "aqlm_gemv_packed"):
         getattr(lib, name).argtypes = prod
         getattr(lib, name).restype = ci
     lib.aqlm_gemv_variant.argtypes = [ci] + prod
     lib.aqlm_gemv_variant.restype = ci
-    lib.aqlm_variant_supported.argtypes = [ci, vp, vp, vp, vp, i64, i64, ci, ci, ci]
+    lib.aqlm_variant_supported.argtypes = [ci, vp, vp, vp, vp, i64, i64, ci, ci, ci, i64]
     lib.aqlm_variant_supported.restype = ci
-    lib.aqlm_selected_variant.argtypes = [ci, vp, vp, vp, vp, i64, i64, ci, ci, ci]
+    lib.aqlm_selected_variant.argtypes = [ci, vp, vp, vp, vp, i64, i64, ci, ci, ci, i64]
     lib.aqlm_selected_variant.restype = ci
-    lib.aqlm_gemv_packed.argtypes = prod
-    lib.aqlm_gemv_packed.restype = ci
+    lib.aqlm_workspace_bytes.argtypes = [ci, ci, vp, vp, vp, vp, i64, i64, ci, ci, ci]
+    lib.aqlm_workspace_bytes.restype = i64
+    lib.aqlm_grouped_workspace_bytes.argtypes = [ci, ci, ctypes.POINTER(vp), ctypes.POINTER(vp),
+                                                 vp, ctypes.POINTER(vp), ctypes.POINTER(i64), i64,
+                                                 ci, ci, ci]
+    lib.aqlm_grouped_workspace_bytes.restype = i64
     grouped = [ci, ctypes.POINTER(vp), ctypes.POINTER(vp), vp, ctypes.POINTER(vp),
-               ctypes.POINTER(i64), i64, ci, ci, ci, vp]
+               ctypes.POINTER(i64), i64, ci, ci, ci, vp, i64, vp]
     for name in ("aqlm_gemv_grouped", "aqlm_gemm_grouped", "aqlm_gemv_packed_grouped"):
         getattr(lib, name).argtypes = grouped
         getattr(lib, name).restype = ci
@@ -106,7 +112,7 @@ def _load():
 def _check(status: int, what: str):
     if status != 0:
         lib = _load()
-        detail = lib.aqlm_last_error().decode() if status == 3 else ""
+        detail = lib.aqlm_last_error().decode()
         raise AqlmError(status, f"{what}: {lib.aqlm_status_string(status).decode()}"
                                 f"{' (' + detail + ')' if detail else ''}")
 
@@ -155,33 +161,64 @@ def _stream():
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
 
-def _product(fn_name, codes, codebooks, x, K=None, B=None, out=None, variant=None):
+def _workspace(nbytes: int, device, workspace=None):
+    """(pointer, size, holder) of the call's workspace: the caller's uint8 tensor; 0 for
+    none (the library then runs the kernels that need no workspace); else a fresh one
+    from torch's caching allocator on the current stream (a graph being captured takes
+    it from its own pool, so replays keep a valid workspace).  The holder keeps the
+    tensor alive across the launch call; the allocator's stream ordering keeps it from
+    being reused before the kernels that use it have run."""
+    torch = _torch()
+    if nbytes < 0:
+        raise ValueError("invalid arguments (workspace query failed)")
+    if isinstance(workspace, int) and not isinstance(workspace, bool) and workspace == 0:
+        return None, 0, None            # explicitly none: the kernels that need no workspace
+    if workspace is not None:
+        if workspace.dtype != torch.uint8 or not workspace.is_cuda or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous uint8 device tensor")
+        if workspace.numel() < nbytes:
+            raise ValueError(f"workspace of {workspace.numel()} bytes is smaller than the "
+                             f"{nbytes} bytes this call needs")
+        return workspace.data_ptr(), workspace.numel(), workspace
+    if nbytes == 0:
+        return None, 0, None
+    t = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    return t.data_ptr(), nbytes, t
+
+
+def _product(fn_name, codes, codebooks, x, K=None, B=None, out=None, variant=None,
+             workspace=None):
     torch = _torch()
     lib = _load()
-    K, B, x2 = _prep(codes, codebooks, x, K, B, packed=(fn_name == "aqlm_gemv_packed"))
+    K, B, x2 = _prep(codes, codebooks, x, K, B)
     out_f, in_f, batch = codes.shape[0], codes.shape[1] * 8, x2.shape[0]
     y = out if out is not None else torch.empty((batch, out_f), dtype=torch.float16,
                                                  device=codes.device)
     if y.dtype != torch.float16 or tuple(y.shape) != (batch, out_f) or not y.is_contiguous():
         raise ValueError("out must be a contiguous float16 [batch][out] tensor")
-    args = (codes.data_ptr(), codebooks.data_ptr(), x2.data_ptr(), y.data_ptr(), out_f, in_f,
-            K, B, batch, _stream())
+    ptrs = (codes.data_ptr(), codebooks.data_ptr(), x2.data_ptr(), y.data_ptr(), out_f, in_f,
+            K, B, batch)
+    op = OPS["gemm"] if fn_name == "aqlm_gemm" else OPS["gemv"]
+    v = 0 if variant is None else (VARIANTS[variant] if isinstance(variant, str) else int(variant))
+    need = lib.aqlm_workspace_bytes(op, v, *ptrs)
+    wp, wn, _keep = _workspace(need, codes.device, workspace)
     if variant is None:
-        _check(getattr(lib, fn_name)(*args), fn_name)
+        _check(getattr(lib, fn_name)(*ptrs, wp, wn, _stream()), fn_name)
     else:
-        v = VARIANTS[variant] if isinstance(variant, str) else int(variant)
-        _check(lib.aqlm_gemv_variant(v, *args), f"aqlm_gemv_variant({variant})")
+        _check(lib.aqlm_gemv_variant(v, *ptrs, wp, wn, _stream()), f"aqlm_gemv_variant({variant})")
     return y if x.dim() == 2 else y[0]
 
 
-def gemv(codes, codebooks, x, K=None, B=None, out=None):
-    """y = W x (token generation path: gather / lookup-table kernels)."""
-    return _product("aqlm_gemv", codes, codebooks, x, K, B, out)
+def gemv(codes, codebooks, x, K=None, B=None, out=None, workspace=None):
+    """y = W x (token generation path: gather / lookup-table kernels).  ``workspace``: an
+    optional uint8 device tensor of at least workspace_bytes("gemv", ...) bytes; by
+    default one is taken from torch's caching allocator for the call."""
+    return _product("aqlm_gemv", codes, codebooks, x, K, B, out, workspace=workspace)
 
 
-def gemm(codes, codebooks, x, K=None, B=None, out=None):
+def gemm(codes, codebooks, x, K=None, B=None, out=None, workspace=None):
     """Y = X W^T; from batch 2 (4 for eight codebooks) decodes to fp16 and runs on the matrix cores."""
-    return _product("aqlm_gemm", codes, codebooks, x, K, B, out)
+    return _product("aqlm_gemm", codes, codebooks, x, K, B, out, workspace=workspace)
 
 
 class PackedWeights:
@@ -202,7 +239,7 @@ def pack_weights(codes, codebooks) -> PackedWeights:
                          codes.shape[1] * 8, K, B)
 
 
-def gemv_packed(weights: PackedWeights, x, out=None):
+def gemv_packed(weights: PackedWeights, x, out=None, workspace=None):
     """y = W x from packed weights (aqlm_gemv_packed)."""
     torch = _torch()
     lib = _load()
@@ -226,13 +263,16 @@ def gemv_packed(weights: PackedWeights, x, out=None):
     if y.dtype != torch.float16 or tuple(y.shape) != (batch, w.out_features) or \
             not y.is_contiguous():
         raise ValueError("out must be a contiguous float16 [batch][out] tensor")
-    _check(lib.aqlm_gemv_packed(w.codes.data_ptr(), w.codebooks.data_ptr(), x2.data_ptr(),
-                                y.data_ptr(), w.out_features, w.in_features, w.K, w.B, batch,
-                                _stream()), "aqlm_gemv_packed")
+    ptrs = (w.codes.data_ptr(), w.codebooks.data_ptr(), x2.data_ptr(), y.data_ptr(),
+            w.out_features, w.in_features, w.K, w.B, batch)
+    need = lib.aqlm_workspace_bytes(OPS["gemv_packed"], 0, *ptrs)
+    wp, wn, _keep = _workspace(need, x2.device, workspace)
+    _check(lib.aqlm_gemv_packed(*ptrs, wp, wn, _stream()), "aqlm_gemv_packed")
     return y if x.dim() == 2 else y[0]
 
 
-def _grouped(fn_name, codes, codebooks, x, out_features, in_features, K, B, outs):
+def _grouped(fn_name, codes, codebooks, x, out_features, in_features, K, B, outs,
+             workspace=None):
     torch = _torch()
     lib = _load()
     n = len(codes)
@@ -252,27 +292,30 @@ def _grouped(fn_name, codes, codebooks, x, out_features, in_features, K, B, outs
     vp = ctypes.c_void_p
     arr = lambda ts: (vp * n)(*[t.data_ptr() for t in ts])
     outs_arr = (ctypes.c_int64 * n)(*out_features)
-    _check(getattr(lib, fn_name)(n, arr(codes), arr(codebooks), x2.data_ptr(), arr(ys), outs_arr,
-                                 in_features, K, B, batch, _stream()), fn_name)
+    op = {"aqlm_gemv_grouped": 0, "aqlm_gemm_grouped": 1, "aqlm_gemv_packed_grouped": 2}[fn_name]
+    args = (arr(codes), arr(codebooks), x2.data_ptr(), arr(ys), outs_arr, in_features, K, B, batch)
+    need = lib.aqlm_grouped_workspace_bytes(op, n, *args)
+    wp, wn, _keep = _workspace(need, x2.device, workspace)
+    _check(getattr(lib, fn_name)(n, *args, wp, wn, _stream()), fn_name)
     return ys if x.dim() == 2 else [y[0] for y in ys]
 
 
-def _grouped_canonical(fn_name, codes, codebooks, x, out):
+def _grouped_canonical(fn_name, codes, codebooks, x, out, workspace=None):
     K, B, x2 = _prep(codes[0], codebooks[0], x, None, None)
     for c, cb in zip(codes, codebooks):
         _prep(c, cb, x, K, B)
     return _grouped(fn_name, codes, codebooks, x, [c.shape[0] for c in codes],
-                    codes[0].shape[1] * 8, K, B, out)
+                    codes[0].shape[1] * 8, K, B, out, workspace)
 
 
-def gemv_grouped(codes, codebooks, x, out=None):
+def gemv_grouped(codes, codebooks, x, out=None, workspace=None):
     """[W_m x for each m] in one launch: lists of codes and codebooks of matrices that share x."""
-    return _grouped_canonical("aqlm_gemv_grouped", codes, codebooks, x, out)
+    return _grouped_canonical("aqlm_gemv_grouped", codes, codebooks, x, out, workspace)
 
 
-def gemm_grouped(codes, codebooks, x, out=None):
+def gemm_grouped(codes, codebooks, x, out=None, workspace=None):
     """gemv_grouped with the matrix-core kernels from batch 2 (as gemm)."""
-    return _grouped_canonical("aqlm_gemm_grouped", codes, codebooks, x, out)
+    return _grouped_canonical("aqlm_gemm_grouped", codes, codebooks, x, out, workspace)
 
 
 def cpu_gemv(codes, codebooks, x, out=None, threads: int = 0):
@@ -314,7 +357,7 @@ def cpu_isa() -> str:
     return _load().aqlm_cpu_isa().decode()
 
 
-def gemv_packed_grouped(weights, x, out=None):
+def gemv_packed_grouped(weights, x, out=None, workspace=None):
     """[W_m x for each m] in one launch from a list of PackedWeights that share x."""
     w0 = weights[0]
     for w in weights:
@@ -325,7 +368,7 @@ def gemv_packed_grouped(weights, x, out=None):
             raise ValueError("packed codes have the wrong size")
     return _grouped("aqlm_gemv_packed_grouped", [w.codes for w in weights],
                     [w.codebooks for w in weights], x, [w.out_features for w in weights],
-                    w0.in_features, w0.K, w0.B, out)
+                    w0.in_features, w0.K, w0.B, out, workspace)
 
 
 def packed_codes_bytes(out_features, in_features, K, B) -> int:
@@ -407,32 +450,78 @@ def unpack_codebooks(packed, out=None):
     return C
 
 
-def gemv_variant(variant, codes, codebooks, x, K=None, B=None, out=None):
-    """The product with a named kernel variant ('generic', 'lds', 'lut', 'l2', 'mfma')."""
-    return _product(None, codes, codebooks, x, K, B, out, variant=variant)
+def gemv_variant(variant, codes, codebooks, x, K=None, B=None, out=None, workspace=None):
+    """The product with a named kernel variant ('generic', 'lds', 'lut', 'l2', 'mfma', ...)."""
+    return _product(None, codes, codebooks, x, K, B, out, variant=variant, workspace=workspace)
 
 
-def variant_supported(variant, codes, codebooks, x, K=None, B=None) -> bool:
+def _query_args(codes, codebooks, x, K, B):
     torch = _torch()
-    lib = _load()
     K, B, x2 = _prep(codes, codebooks, x, K, B)
+    y = torch.empty((x2.shape[0], codes.shape[0]), dtype=torch.float16, device=codes.device)
+    return (codes.data_ptr(), codebooks.data_ptr(), x2.data_ptr(), y.data_ptr(), codes.shape[0],
+            codes.shape[1] * 8, K, B, x2.shape[0]), y
+
+
+def variant_supported(variant, codes, codebooks, x, K=None, B=None, workspace_bytes=None) -> bool:
+    """Would gemv_variant run?  workspace_bytes None: with the workspace it needs."""
+    lib = _load()
     v = VARIANTS[variant] if isinstance(variant, str) else int(variant)
-    y = torch.empty((x2.shape[0], codes.shape[0]), dtype=torch.float16, device=codes.device)
-    return bool(lib.aqlm_variant_supported(v, codes.data_ptr(), codebooks.data_ptr(),
-                                           x2.data_ptr(), y.data_ptr(), codes.shape[0],
-                                           codes.shape[1] * 8, K, B, x2.shape[0]))
+    args, _y = _query_args(codes, codebooks, x, K, B)
+    if workspace_bytes is None:
+        workspace_bytes = max(0, lib.aqlm_workspace_bytes(OPS["gemv"], v, *args))
+    return bool(lib.aqlm_variant_supported(v, *args, int(workspace_bytes)))
 
 
-def selected_variant(codes, codebooks, x, gemm: bool = False, K=None, B=None) -> str:
-    """Name of the kernel aqlm_gemv (or aqlm_gemm) would run for these tensors."""
+def workspace_bytes(op, codes, codebooks, x, K=None, B=None, variant="auto") -> int:
+    """Workspace bytes of the call op ("gemv", "gemm", "gemv_packed"; for the packed
+    call pass the PackedWeights' codes and codebooks tensors)."""
+    lib = _load()
+    v = VARIANTS[variant] if isinstance(variant, str) else int(variant)
+    if op == "gemv_packed":
+        raise ValueError("use packed_workspace_bytes for packed weights")
+    args, _y = _query_args(codes, codebooks, x, K, B)
+    return int(lib.aqlm_workspace_bytes(OPS[op], v, *args))
+
+
+def packed_workspace_bytes(weights, x) -> int:
+    """Workspace bytes of gemv_packed(weights, x)."""
     torch = _torch()
     lib = _load()
-    K, B, x2 = _prep(codes, codebooks, x, K, B)
-    y = torch.empty((x2.shape[0], codes.shape[0]), dtype=torch.float16, device=codes.device)
-    v = lib.aqlm_selected_variant(1 if gemm else 0, codes.data_ptr(), codebooks.data_ptr(),
-                                  x2.data_ptr(), y.data_ptr(), codes.shape[0], codes.shape[1] * 8,
-                                  K, B, x2.shape[0])
-    return lib.aqlm_variant_name(v).decode()
+    w = weights
+    x2 = x.unsqueeze(0) if x.dim() == 1 else x
+    y = torch.empty((x2.shape[0], w.out_features), dtype=torch.float16, device=x2.device)
+    return int(lib.aqlm_workspace_bytes(OPS["gemv_packed"], 0, w.codes.data_ptr(),
+                                        w.codebooks.data_ptr(), x2.data_ptr(), y.data_ptr(),
+                                        w.out_features, w.in_features, w.K, w.B, x2.shape[0]))
+
+
+def grouped_workspace_bytes(op, codes, codebooks, x, out_features, in_features, K, B) -> int:
+    """Workspace bytes of a grouped call (op "gemv", "gemm" or "gemv_packed")."""
+    torch = _torch()
+    lib = _load()
+    n = len(codes)
+    x2 = x.unsqueeze(0) if x.dim() == 1 else x
+    ys = [torch.empty((x2.shape[0], o), dtype=torch.float16, device=x2.device) for o in out_features]
+    vp = ctypes.c_void_p
+    arr = lambda ts: (vp * n)(*[t.data_ptr() for t in ts])
+    return int(lib.aqlm_grouped_workspace_bytes(OPS[op], n, arr(codes), arr(codebooks),
+                                                x2.data_ptr(), arr(ys),
+                                                (ctypes.c_int64 * n)(*out_features), in_features,
+                                                K, B, x2.shape[0]))
+
+
+def selected_variant(codes, codebooks, x, gemm: bool = False, K=None, B=None,
+                     workspace_bytes=None) -> str:
+    """Name of the kernel aqlm_gemv (or aqlm_gemm) would run for these tensors, with the
+    workspace the call needs (workspace_bytes None, as the binding's calls pass it) or
+    the given size (0: the kernels that need none)."""
+    lib = _load()
+    args, _y = _query_args(codes, codebooks, x, K, B)
+    if workspace_bytes is None:
+        workspace_bytes = max(0, lib.aqlm_workspace_bytes(OPS["gemm" if gemm else "gemv"], 0, *args))
+    v = lib.aqlm_selected_variant(1 if gemm else 0, *args, int(workspace_bytes))
+    return lib.aqlm_variant_name(v).decode() if v >= 0 else "error"
 
 
 def dequantize(codes, codebooks, K=None, B=None, dtype=None, out=None):

@@ -1,5 +1,11 @@
 // C ABI of libaqlm_mi355x: argument checks, kernel choice, launch, error mapping.
 // The operation and layouts are documented in include/aqlm_mi355x.h.
+//
+// The library holds no device memory and no per-stream state: every product call
+// receives its scratch memory (partial sums, packed or unpacked operands) from the
+// caller as `workspace`, and the kernel it runs is a function of its arguments alone
+// (shapes, pointer alignment, workspace size, environment overrides read once), so
+// an eager call and the same call captured into a HIP graph run the same kernels.
 #include "aqlm_mi355x.h"
 
 #include <hip/hip_runtime.h>
@@ -7,9 +13,6 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
-#include <map>
-#include <mutex>
-#include <utility>
 
 #include "kernels.hpp"
 
@@ -33,12 +36,17 @@ constexpr int kSplitMaxBatchGemm = 2;
 // L2 per token tile costs more) and at 1024 for 8-bit codes with K <= 2.
 constexpr int kPrefillMinBatch16 = 256;
 constexpr int kPrefillMinBatch8 = 1024;
+// The workspace is cut into fp32 / 16-byte-vector regions at 256-byte offsets.
+constexpr uintptr_t kWorkspaceAlign = 256;
+constexpr int64_t kUnlimited = INT64_MAX;
 
 thread_local char g_last_error[256] = "";
 
 void set_error(const char *what, hipError_t e) {
     std::snprintf(g_last_error, sizeof(g_last_error), "%s: %s", what, hipGetErrorString(e));
 }
+
+void set_message(const char *what) { std::snprintf(g_last_error, sizeof(g_last_error), "%s", what); }
 
 bool log_enabled() {
     static const bool on = [] {
@@ -49,34 +57,40 @@ bool log_enabled() {
 }
 
 int forced_variant() {
-    const char *v = std::getenv("AQLM_FORCE_VARIANT");
-    if (!v || !*v) return AQLM_VARIANT_AUTO;
-    if (!std::strcmp(v, "generic")) return AQLM_VARIANT_GENERIC;
-    if (!std::strcmp(v, "lds")) return AQLM_VARIANT_LDS;
-    if (!std::strcmp(v, "lut")) return AQLM_VARIANT_LUT;
-    if (!std::strcmp(v, "l2")) return AQLM_VARIANT_L2;
-    if (!std::strcmp(v, "mfma")) return AQLM_VARIANT_MFMA;
-    if (!std::strcmp(v, "split")) return AQLM_VARIANT_SPLIT;
-    if (!std::strcmp(v, "prefill")) return AQLM_VARIANT_PREFILL;
-    return AQLM_VARIANT_AUTO;
+    static const int forced = [] {
+        const char *v = std::getenv("AQLM_FORCE_VARIANT");
+        if (!v || !*v) return int(AQLM_VARIANT_AUTO);
+        if (!std::strcmp(v, "generic")) return int(AQLM_VARIANT_GENERIC);
+        if (!std::strcmp(v, "lds")) return int(AQLM_VARIANT_LDS);
+        if (!std::strcmp(v, "lut")) return int(AQLM_VARIANT_LUT);
+        if (!std::strcmp(v, "l2")) return int(AQLM_VARIANT_L2);
+        if (!std::strcmp(v, "mfma")) return int(AQLM_VARIANT_MFMA);
+        if (!std::strcmp(v, "split")) return int(AQLM_VARIANT_SPLIT);
+        if (!std::strcmp(v, "prefill")) return int(AQLM_VARIANT_PREFILL);
+        return int(AQLM_VARIANT_AUTO);
+    }();
+    return forced;
 }
 
-// batch from which aqlm_gemm decodes W once and runs one library GEMM
-// (AQLM_PREFILL_MIN_BATCH overrides)
-int prefill_min_batch(const aqlm::Problem &p) {
-    const int def = (p.B == 16 || p.K >= 4) ? kPrefillMinBatch16 : kPrefillMinBatch8;
-    const char *v = std::getenv("AQLM_PREFILL_MIN_BATCH");
+int env_batch(const char *name, int def) {
+    const char *v = std::getenv(name);
     if (!v || !*v) return def;
     const int n = std::atoi(v);
     return n >= 1 ? n : def;
+}
+
+// batch from which aqlm_gemm decodes W once and runs one dense GEMM
+// (AQLM_PREFILL_MIN_BATCH overrides)
+int prefill_min_batch(const aqlm::Problem &p) {
+    static const int b16 = env_batch("AQLM_PREFILL_MIN_BATCH", kPrefillMinBatch16);
+    static const int b8 = env_batch("AQLM_PREFILL_MIN_BATCH", kPrefillMinBatch8);
+    return (p.B == 16 || p.K >= 4) ? b16 : b8;
 }
 
 int mfma_min_batch(int K) {
-    const int def = K >= 8 ? kMfmaMinBatch8Codebooks : kMfmaMinBatch;
-    const char *v = std::getenv("AQLM_MFMA_MIN_BATCH");
-    if (!v || !*v) return def;
-    const int n = std::atoi(v);
-    return n >= 1 ? n : def;
+    static const int any = env_batch("AQLM_MFMA_MIN_BATCH", kMfmaMinBatch);
+    static const int k8 = env_batch("AQLM_MFMA_MIN_BATCH", kMfmaMinBatch8Codebooks);
+    return K >= 8 ? k8 : any;
 }
 
 // [a, a+na) and [b, b+nb) overlap?
@@ -159,12 +173,6 @@ bool all_segments(const aqlm::Problem &p, F f) {
     return true;
 }
 
-bool supported_one(int variant, const aqlm::Problem &p);
-
-bool supported(int variant, const aqlm::Problem &p) {
-    return all_segments(p, [variant](const aqlm::Problem &q) { return supported_one(variant, q); });
-}
-
 bool supported_one(int variant, const aqlm::Problem &p) {
     switch (variant) {
         case AQLM_VARIANT_GENERIC: return true;
@@ -178,64 +186,91 @@ bool supported_one(int variant, const aqlm::Problem &p) {
     }
 }
 
-int choose(bool gemm, const aqlm::Problem &p) {
+bool supported(int variant, const aqlm::Problem &p) {
+    return all_segments(p, [variant](const aqlm::Problem &q) { return supported_one(variant, q); });
+}
+
+// Workspace bytes a variant needs for p (0: none).  Kernels without a matrix table
+// (lds, generic, prefill) run a grouped problem one matrix at a time, in stream order,
+// each reusing the whole workspace.
+int64_t variant_need(int variant, const aqlm::Problem &p) {
+    switch (variant) {
+        case AQLM_VARIANT_LUT: return int64_t(aqlm::lut_workspace_bytes(p));
+        case AQLM_VARIANT_MFMA: return int64_t(aqlm::mfma_workspace_bytes(p));
+        case AQLM_VARIANT_SPLIT: return int64_t(aqlm::split_canonical_workspace_bytes(p));
+        case AQLM_VARIANT_PREFILL: {
+            int64_t n = 0;
+            for (int m = 0; m < p.segs.n; ++m) {
+                const int64_t s = int64_t(aqlm::prefill_workspace_bytes(segment(p, m)));
+                n = s > n ? s : n;
+            }
+            return n;
+        }
+        default: return 0;
+    }
+}
+
+// The fastest kernel for p whose workspace fits `ws_bytes` (0 or unlimited).  Without a
+// workspace the matrix-core kernel runs unsplit (launch_mfma with a null workspace).
+int choose_within(bool gemm, const aqlm::Problem &p, int64_t ws_bytes) {
+    auto fits = [&](int v) {
+        return supported(v, p) &&
+               (variant_need(v, p) <= ws_bytes || (v == AQLM_VARIANT_MFMA && ws_bytes == 0));
+    };
     const int forced = forced_variant();
-    if (forced != AQLM_VARIANT_AUTO && supported(forced, p)) return forced;
-    if (gemm && p.batch >= prefill_min_batch(p) && supported(AQLM_VARIANT_PREFILL, p))
+    if (forced != AQLM_VARIANT_AUTO && fits(forced)) return forced;
+    if (gemm && p.batch >= prefill_min_batch(p) && fits(AQLM_VARIANT_PREFILL))
         return AQLM_VARIANT_PREFILL;
     // 16-bit codes: the split kernel (codebook packed per call) up to batch 4, or 2 where
     // the matrix cores are allowed
-    if (p.batch <= (gemm ? kSplitMaxBatchGemm : kSplitMaxBatch) && supported(AQLM_VARIANT_SPLIT, p))
+    if (p.batch <= (gemm ? kSplitMaxBatchGemm : kSplitMaxBatch) && fits(AQLM_VARIANT_SPLIT))
         return AQLM_VARIANT_SPLIT;
-    if (gemm && p.batch >= mfma_min_batch(p.K) && supported(AQLM_VARIANT_MFMA, p))
-        return AQLM_VARIANT_MFMA;
-    if (supported(AQLM_VARIANT_LUT, p)) return AQLM_VARIANT_LUT;
-    if (supported(AQLM_VARIANT_LDS, p)) return AQLM_VARIANT_LDS;
-    if (supported(AQLM_VARIANT_L2, p)) return AQLM_VARIANT_L2;
+    if (gemm && p.batch >= mfma_min_batch(p.K) && fits(AQLM_VARIANT_MFMA)) return AQLM_VARIANT_MFMA;
+    if (fits(AQLM_VARIANT_LUT)) return AQLM_VARIANT_LUT;
+    if (fits(AQLM_VARIANT_LDS)) return AQLM_VARIANT_LDS;
+    if (fits(AQLM_VARIANT_L2)) return AQLM_VARIANT_L2;
     return AQLM_VARIANT_GENERIC;
 }
 
-// Split-slice partial sums of the lookup-table kernel live in one workspace per
-// (device, stream), grown on demand and kept until the process exits.  Calls on
-// one stream are ordered, so they can share it.
-struct Workspace {
-    void *ptr = nullptr;
-    size_t bytes = 0;
-};
-std::mutex g_ws_mutex;
-std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
+// Kernel choice under the workspace rule: no workspace (0 bytes) selects among the
+// kernels that need none; any other size must cover the fastest kernel's need.
+// Returns the variant, or -1 (message set) when the workspace is too small.
+int choose(bool gemm, const aqlm::Problem &p, int64_t ws_bytes) {
+    if (ws_bytes == 0) return choose_within(gemm, p, 0);
+    const int v = choose_within(gemm, p, kUnlimited);
+    const int64_t need = variant_need(v, p);
+    if (need > ws_bytes) {
+        std::snprintf(g_last_error, sizeof(g_last_error),
+                      "workspace of %lld bytes is too small: %s needs %lld (aqlm_workspace_bytes)",
+                      (long long)ws_bytes, aqlm_variant_name(v), (long long)need);
+        return -1;
+    }
+    return v;
+}
 
-// Returns the stream's workspace of at least `bytes`.  A stream that is being
-// captured into a graph cannot allocate: if it has no large enough workspace
-// yet, *out is left null (the caller then picks a kernel that needs none).
-hipError_t get_workspace(hipStream_t stream, size_t bytes, void **out) {
-    *out = nullptr;
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
-    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
-    if (hipStreamIsCapturing(stream, &cap) != hipSuccess) {
-        (void)hipGetLastError();  // a stream that cannot be queried is not capturing
-        cap = hipStreamCaptureStatusNone;
+// Checks the caller's workspace: size >= 0, a pointer when the size is positive,
+// 256-byte aligned, and disjoint from every operand of p (codes_bytes[m] per matrix).
+aqlm_status_t check_workspace(const void *ws, int64_t ws_bytes, const aqlm::Problem &p,
+                              const int64_t *codes_bytes) {
+    if (ws_bytes < 0 || (ws_bytes > 0 && !ws)) return AQLM_ERR_INVALID_ARGUMENT;
+    if (ws_bytes == 0) return AQLM_OK;
+    if (reinterpret_cast<uintptr_t>(ws) & (kWorkspaceAlign - 1)) {
+        set_message("workspace must be 256-byte aligned");
+        return AQLM_ERR_INVALID_ARGUMENT;
     }
-    std::lock_guard<std::mutex> lock(g_ws_mutex);
-    Workspace &w = g_ws[std::make_pair(dev, stream)];
-    if (w.bytes < bytes) {
-        if (cap != hipStreamCaptureStatusNone) return hipSuccess;
-        if (w.ptr) {
-            e = hipStreamSynchronize(stream);  // earlier launches may still use it
-            if (e != hipSuccess) return e;
-            (void)hipFree(w.ptr);
-            w.ptr = nullptr;
-            w.bytes = 0;
-        }
-        size_t nb = bytes < (size_t(1) << 20) ? (size_t(1) << 20) : bytes;
-        e = hipMalloc(&w.ptr, nb);
-        if (e != hipSuccess) return e;
-        w.bytes = nb;
+    const int64_t cbbytes = int64_t(p.K) * (int64_t(1) << p.B) * kGroup * 2;
+    bool clash = overlaps(ws, ws_bytes, p.x, int64_t(p.batch) * p.in * 2);
+    for (int m = 0; m < p.segs.n && !clash; ++m) {
+        const int64_t rows = p.segs.row0[m + 1] - p.segs.row0[m];
+        clash = overlaps(ws, ws_bytes, p.segs.codes[m], codes_bytes[m]) ||
+                overlaps(ws, ws_bytes, p.segs.cb[m], cbbytes) ||
+                overlaps(ws, ws_bytes, p.segs.y[m], int64_t(p.batch) * rows * 2);
     }
-    *out = w.ptr;
-    return hipSuccess;
+    if (clash) {
+        set_message("workspace overlaps an operand");
+        return AQLM_ERR_INVALID_ARGUMENT;
+    }
+    return AQLM_OK;
 }
 
 // Packs or unpacks codebooks; shared argument checks.
@@ -257,17 +292,18 @@ aqlm_status_t pack_common(const void *src, void *dst, int K, int B, void *stream
     return AQLM_OK;
 }
 
-aqlm_status_t run(int variant, const aqlm::Problem &p) {
+// Launches `variant` for p with the workspace `ws` (at least variant_need bytes).
+aqlm_status_t run(int variant, const aqlm::Problem &p, void *ws) {
     hipError_t e = hipSuccess;
     if (log_enabled())
-        std::fprintf(stderr, "[aqlm] %s out=%lld in=%lld K=%d B=%d batch=%d\n",
+        std::fprintf(stderr, "[aqlm] %s out=%lld in=%lld K=%d B=%d batch=%d n=%d\n",
                      aqlm_variant_name(variant), (long long)p.out, (long long)p.in, p.K, p.B,
-                     p.batch);
+                     p.batch, p.segs.n);
     // kernels without a matrix table run once per matrix
     if (p.segs.n > 1 && (variant == AQLM_VARIANT_LDS || variant == AQLM_VARIANT_GENERIC ||
                          variant == AQLM_VARIANT_PREFILL)) {
         for (int m = 0; m < p.segs.n; ++m) {
-            const aqlm_status_t st = run(variant, segment(p, m));
+            const aqlm_status_t st = run(variant, segment(p, m), ws);
             if (st != AQLM_OK) return st;
         }
         return AQLM_OK;
@@ -275,81 +311,10 @@ aqlm_status_t run(int variant, const aqlm::Problem &p) {
     switch (variant) {
         case AQLM_VARIANT_LDS: e = aqlm::launch_gather(p); break;
         case AQLM_VARIANT_L2: e = aqlm::launch_l2(p); break;
-        case AQLM_VARIANT_LUT: {
-            void *ws = nullptr;
-            e = get_workspace(p.stream, aqlm::lut_workspace_bytes(p), &ws);
-            if (e != hipSuccess) break;
-            if (ws) {
-                e = aqlm::launch_lut(p, ws);
-            } else if (p.segs.n > 1) {
-                // capturing stream whose workspace fits the matrices one at a time only
-                for (int m = 0; m < p.segs.n; ++m) {
-                    const aqlm_status_t st = run(variant, segment(p, m));
-                    if (st != AQLM_OK) return st;
-                }
-                return AQLM_OK;
-            } else {
-                // capturing stream without a workspace: same product, no workspace needed
-                if (log_enabled())
-                    std::fprintf(stderr, "[aqlm] lut: no workspace on a capturing stream, "
-                                         "using the gather kernel\n");
-                for (int m = 0; m < p.segs.n && e == hipSuccess; ++m) {
-                    const aqlm::Problem q = segment(p, m);
-                    e = aqlm::gather_supported(q) ? aqlm::launch_gather(q) : aqlm::launch_generic(q);
-                }
-            }
-            break;
-        }
-        case AQLM_VARIANT_MFMA: {
-            const size_t need = aqlm::mfma_workspace_bytes(p);
-            void *ws = nullptr;
-            if (need) {
-                e = get_workspace(p.stream, need, &ws);
-                if (e != hipSuccess) break;
-                if (!ws && p.segs.n > 1) {
-                    // capturing stream whose workspace may fit the matrices one at a time
-                    for (int m = 0; m < p.segs.n; ++m) {
-                        const aqlm_status_t st = run(variant, segment(p, m));
-                        if (st != AQLM_OK) return st;
-                    }
-                    return AQLM_OK;
-                }
-                if (!ws) {
-                    // capturing stream without a workspace: same product, no workspace needed
-                    for (int m = 0; m < p.segs.n && e == hipSuccess; ++m)
-                        e = aqlm::launch_generic(segment(p, m));
-                    break;
-                }
-            }
-            e = aqlm::launch_mfma(p, ws);
-            break;
-        }
-        case AQLM_VARIANT_SPLIT: {
-            void *ws = nullptr;
-            e = get_workspace(p.stream, aqlm::split_canonical_workspace_bytes(p), &ws);
-            if (e != hipSuccess) break;
-            if (!ws) {
-                // capturing stream without a large enough workspace: the L2-gather kernel
-                if (log_enabled())
-                    std::fprintf(stderr, "[aqlm] split: no workspace on a capturing stream\n");
-                return run(supported(AQLM_VARIANT_L2, p) ? AQLM_VARIANT_L2 : AQLM_VARIANT_GENERIC, p);
-            }
-            e = aqlm::launch_split_canonical(p, ws);
-            break;
-        }
-        case AQLM_VARIANT_PREFILL: {
-            void *ws = nullptr;
-            e = get_workspace(p.stream, aqlm::prefill_workspace_bytes(p), &ws);
-            if (e != hipSuccess) break;
-            if (!ws) {
-                // capturing stream without a large enough workspace: the matrix cores
-                if (log_enabled())
-                    std::fprintf(stderr, "[aqlm] prefill: no workspace on a capturing stream\n");
-                return run(AQLM_VARIANT_MFMA, p);
-            }
-            e = aqlm::launch_prefill(p, ws);
-            break;
-        }
+        case AQLM_VARIANT_LUT: e = aqlm::launch_lut(p, ws); break;
+        case AQLM_VARIANT_MFMA: e = aqlm::launch_mfma(p, ws); break;   // null: unsplit
+        case AQLM_VARIANT_SPLIT: e = aqlm::launch_split_canonical(p, ws); break;
+        case AQLM_VARIANT_PREFILL: e = aqlm::launch_prefill(p, ws); break;
         default:
             for (int m = 0; m < p.segs.n && e == hipSuccess; ++m) e = aqlm::launch_generic(segment(p, m));
             break;
@@ -362,14 +327,15 @@ aqlm_status_t run(int variant, const aqlm::Problem &p) {
 }
 
 // Validates a grouped call and builds its problem (out = the total rows).  packed: the
-// codes are in the packed layout of aqlm_pack_codes.
+// codes are in the packed layout of aqlm_pack_codes.  code_bytes (n entries) receives
+// each matrix's code bytes.
 aqlm_status_t grouped_problem(int n, const void *const *codes, const void *const *codebooks,
                               const void *x, void *const *y, const int64_t *out_features,
                               int64_t in, int K, int B, int batch, void *stream, bool packed,
-                              aqlm::Problem *out) {
+                              aqlm::Problem *out, int64_t *code_bytes) {
     if (n < 1 || n > aqlm::kMaxSegs || !codes || !codebooks || !y || !out_features)
         return AQLM_ERR_INVALID_ARGUMENT;
-    int64_t total = 0, code_bytes[aqlm::kMaxSegs];
+    int64_t total = 0;
     Sizes s{};
     for (int m = 0; m < n; ++m) {
         const aqlm_status_t st =
@@ -406,71 +372,271 @@ aqlm_status_t grouped_problem(int n, const void *const *codes, const void *const
     return AQLM_OK;
 }
 
+// ---- products from packed weights ----------------------------------------------
+
+enum PackedKind { kPackedSplit, kPackedSplitMfma, kPackedLut, kPackedUnpack };
+
+// How a packed product runs and the workspace it needs.  kPackedUnpack: the packed
+// operands of one matrix are unpacked into the workspace (codes at 0 when tiled, the
+// codebooks at cb_off), and the matrix-core kernel's partial sums follow at ops_off.
+struct PackedPlan {
+    PackedKind kind;
+    int64_t need;
+    bool tiled, gemm;
+    size_t cb_off, ops_off, mfma_ws;
+};
+
+PackedPlan packed_plan_one(const aqlm::Problem &p) {
+    PackedPlan pl{};
+    pl.kind = kPackedUnpack;
+    pl.tiled = tiled_codes(p.K, p.B);
+    const bool generic = forced_variant() == AQLM_VARIANT_GENERIC;
+    const int64_t cbytes = p.out * (p.in / kGroup) * p.K * (p.B / 8);
+    const int64_t cbbytes = int64_t(p.K) * (int64_t(1) << p.B) * kGroup * 2;
+    pl.cb_off = (size_t(cbytes) + 255) / 256 * 256;
+    const size_t unpacked = pl.tiled ? pl.cb_off + size_t(cbbytes) : size_t(cbbytes);
+    pl.ops_off = (unpacked + 255) / 256 * 256;
+    pl.gemm = !generic && p.batch >= mfma_min_batch(p.K);
+    if (pl.gemm) {
+        // the unpacked operands sit at 256-byte offsets of the workspace: sized on the
+        // shape with aligned operands
+        const char *base = reinterpret_cast<const char *>(uintptr_t(1) << 40);
+        const aqlm::Problem q = make_problem(base, base, p.x, p.y, p.out, p.in, p.K, p.B,
+                                             p.batch, p.stream);
+        if (aqlm::mfma_supported(q)) pl.mfma_ws = aqlm::mfma_workspace_bytes(q);
+    }
+    pl.need = int64_t(pl.ops_off + pl.mfma_ws);
+    return pl;
+}
+
+PackedPlan packed_plan(const aqlm::Problem &p) {
+    PackedPlan pl{};
+    const bool generic = forced_variant() == AQLM_VARIANT_GENERIC;
+    pl.tiled = tiled_codes(p.K, p.B);
+    const bool split = !generic && !pl.tiled &&
+                       all_segments(p, [](const aqlm::Problem &q) { return aqlm::ds_supported(q); });
+    // batches the LDS-plane dot-product kernel does not take: the same planes on the
+    // matrix cores
+    const bool splitm = !generic && !pl.tiled && !split &&
+                        all_segments(p, [](const aqlm::Problem &q) { return aqlm::dsm_supported(q); });
+    const bool lutp = !generic && pl.tiled &&
+                      all_segments(p, [](const aqlm::Problem &q) { return aqlm::lut_packed_supported(q); });
+    if (split || splitm || lutp) {
+        pl.kind = split ? kPackedSplit : splitm ? kPackedSplitMfma : kPackedLut;
+        pl.need = int64_t(split ? aqlm::ds_workspace_bytes(p)
+                          : splitm ? aqlm::dsm_workspace_bytes(p)
+                                   : aqlm::lut_packed_workspace_bytes(p));
+        return pl;
+    }
+    if (p.segs.n == 1) return packed_plan_one(p);
+    // several matrices unpacked one at a time through the same workspace
+    pl.kind = kPackedUnpack;
+    for (int m = 0; m < p.segs.n; ++m) {
+        const int64_t nm = packed_plan_one(segment(p, m)).need;
+        pl.need = nm > pl.need ? nm : pl.need;
+    }
+    return pl;
+}
+
+aqlm_status_t run_packed(const aqlm::Problem &p, const PackedPlan &pl, void *ws) {
+    hipError_t e = hipSuccess;
+    const char *name = pl.kind == kPackedSplit ? "split" : pl.kind == kPackedSplitMfma ? "split-mfma"
+                     : pl.kind == kPackedLut ? "lut_packed" : "unpack+auto";
+    if (log_enabled())
+        std::fprintf(stderr, "[aqlm] packed %s n=%d rows=%lld in=%lld K=%d B=%d batch=%d\n", name,
+                     p.segs.n, (long long)p.out, (long long)p.in, p.K, p.B, p.batch);
+    if (pl.kind != kPackedUnpack) {
+        e = pl.kind == kPackedSplit ? aqlm::launch_ds(p, ws)
+          : pl.kind == kPackedSplitMfma ? aqlm::launch_dsm(p, ws) : aqlm::launch_lut_packed(p, ws);
+        if (e != hipSuccess) {
+            set_error(name, e);
+            return AQLM_ERR_HIP;
+        }
+        return AQLM_OK;
+    }
+    if (p.segs.n > 1) {
+        // one matrix at a time through the workspace (stream order keeps them apart)
+        for (int m = 0; m < p.segs.n; ++m) {
+            const aqlm::Problem q = segment(p, m);
+            const aqlm_status_t st = run_packed(q, packed_plan_one(q), ws);
+            if (st != AQLM_OK) return st;
+        }
+        return AQLM_OK;
+    }
+    char *wsb = static_cast<char *>(ws);
+    if (pl.tiled) {
+        e = aqlm::launch_pack_codes_lut(p.codes, wsb, p.out, p.in, false, p.stream);
+        if (e != hipSuccess) {
+            set_error("unpack_codes", e);
+            return AQLM_ERR_HIP;
+        }
+    }
+    void *cbws = pl.tiled ? wsb + pl.cb_off : wsb;
+    e = aqlm::launch_unpack_codebooks(p.codebooks, cbws, p.K, p.B, p.stream);
+    if (e != hipSuccess) {
+        set_error("unpack_codebooks", e);
+        return AQLM_ERR_HIP;
+    }
+    aqlm::Problem q = make_problem(pl.tiled ? wsb : p.codes, cbws, p.x, p.y, p.out, p.in, p.K, p.B,
+                                   p.batch, p.stream);
+    if (pl.gemm && aqlm::mfma_supported(q) && aqlm::mfma_workspace_bytes(q) <= pl.mfma_ws) {
+        // matrix cores, with their partial sums after the unpacked operands
+        e = aqlm::launch_mfma(q, pl.mfma_ws ? wsb + pl.ops_off : nullptr);
+        if (e != hipSuccess) {
+            set_error("mfma", e);
+            return AQLM_ERR_HIP;
+        }
+        return AQLM_OK;
+    }
+    // the workspace holds the operands: a kernel that needs no workspace of its own
+    return run(choose_within(false, q, 0), q, nullptr);
+}
+
+// A product call: checks, kernel choice under the workspace rule, launch.
+aqlm_status_t product(bool gemm, const aqlm::Problem &p, const int64_t *code_bytes, void *ws,
+                      int64_t ws_bytes) {
+    const aqlm_status_t st = check_workspace(ws, ws_bytes, p, code_bytes);
+    if (st != AQLM_OK) return st;
+    const int v = choose(gemm, p, ws_bytes);
+    if (v < 0) return AQLM_ERR_INVALID_ARGUMENT;
+    // no workspace: a null pointer, which also keeps the matrix-core kernel unsplit
+    return run(v, p, ws_bytes ? ws : nullptr);
+}
+
+aqlm_status_t packed_product(const aqlm::Problem &p, const int64_t *code_bytes, void *ws,
+                             int64_t ws_bytes) {
+    const aqlm_status_t st = check_workspace(ws, ws_bytes, p, code_bytes);
+    if (st != AQLM_OK) return st;
+    const PackedPlan pl = packed_plan(p);
+    if (pl.need > ws_bytes) {
+        std::snprintf(g_last_error, sizeof(g_last_error),
+                      "workspace of %lld bytes is too small: the packed product needs %lld "
+                      "(aqlm_workspace_bytes)", (long long)ws_bytes, (long long)pl.need);
+        return AQLM_ERR_INVALID_ARGUMENT;
+    }
+    return run_packed(p, pl, ws);
+}
+
+// Workspace bytes of an (op, variant) call on a validated problem; -1 if the op is unknown.
+int64_t workspace_need(int op, int variant, const aqlm::Problem &p) {
+    switch (op) {
+        case AQLM_OP_GEMV:
+        case AQLM_OP_GEMM:
+            if (variant == AQLM_VARIANT_AUTO)
+                return variant_need(choose_within(op == AQLM_OP_GEMM, p, kUnlimited), p);
+            return supported(variant, p) ? variant_need(variant, p) : 0;
+        case AQLM_OP_GEMV_PACKED:
+            return variant == AQLM_VARIANT_AUTO ? packed_plan(p).need : -1;
+        default: return -1;
+    }
+}
+
 }  // namespace
 
 extern "C" {
 
 aqlm_status_t aqlm_gemv(const void *codes, const void *codebooks, const void *x, void *y,
                         int64_t out_features, int64_t in_features, int K, int B, int batch,
-                        void *stream) {
+                        void *workspace, int64_t workspace_bytes, void *stream) {
+    g_last_error[0] = 0;
     Sizes s;
     aqlm_status_t st = check_args(codes, codebooks, x, y, out_features, in_features, K, B, batch, &s);
     if (st != AQLM_OK) return st;
     const aqlm::Problem p = make_problem(codes, codebooks, x, y, out_features, in_features, K, B,
                                          batch, stream);
-    return run(choose(false, p), p);
+    return product(false, p, &s.codes, workspace, workspace_bytes);
 }
 
 aqlm_status_t aqlm_gemm(const void *codes, const void *codebooks, const void *x, void *y,
                         int64_t out_features, int64_t in_features, int K, int B, int batch,
-                        void *stream) {
+                        void *workspace, int64_t workspace_bytes, void *stream) {
+    g_last_error[0] = 0;
     Sizes s;
     aqlm_status_t st = check_args(codes, codebooks, x, y, out_features, in_features, K, B, batch, &s);
     if (st != AQLM_OK) return st;
     const aqlm::Problem p = make_problem(codes, codebooks, x, y, out_features, in_features, K, B,
                                          batch, stream);
-    return run(choose(true, p), p);
+    return product(true, p, &s.codes, workspace, workspace_bytes);
 }
 
 aqlm_status_t aqlm_gemv_variant(int variant, const void *codes, const void *codebooks,
                                 const void *x, void *y, int64_t out_features,
-                                int64_t in_features, int K, int B, int batch, void *stream) {
+                                int64_t in_features, int K, int B, int batch, void *workspace,
+                                int64_t workspace_bytes, void *stream) {
+    g_last_error[0] = 0;
     Sizes s;
     aqlm_status_t st = check_args(codes, codebooks, x, y, out_features, in_features, K, B, batch, &s);
     if (st != AQLM_OK) return st;
     const aqlm::Problem p = make_problem(codes, codebooks, x, y, out_features, in_features, K, B,
                                          batch, stream);
-    if (variant == AQLM_VARIANT_AUTO) return run(choose(false, p), p);
+    if (variant == AQLM_VARIANT_AUTO) return product(false, p, &s.codes, workspace, workspace_bytes);
+    st = check_workspace(workspace, workspace_bytes, p, &s.codes);
+    if (st != AQLM_OK) return st;
     if (!supported(variant, p)) return AQLM_ERR_UNSUPPORTED;
-    return run(variant, p);
+    if (variant_need(variant, p) > workspace_bytes) {
+        // the matrix-core kernel also runs unsplit without a workspace
+        if (variant != AQLM_VARIANT_MFMA || workspace_bytes != 0) return AQLM_ERR_UNSUPPORTED;
+        workspace = nullptr;
+    }
+    return run(variant, p, workspace_bytes ? workspace : nullptr);
 }
 
 int aqlm_variant_supported(int variant, const void *codes, const void *codebooks, const void *x,
                            const void *y, int64_t out_features, int64_t in_features, int K, int B,
-                           int batch) {
+                           int batch, int64_t workspace_bytes) {
     Sizes s;
     if (check_args(codes, codebooks, x, y, out_features, in_features, K, B, batch, &s) != AQLM_OK)
         return 0;
     const aqlm::Problem p = make_problem(codes, codebooks, x, const_cast<void *>(y), out_features,
                                          in_features, K, B, batch, nullptr);
     if (variant == AQLM_VARIANT_AUTO) return 1;
-    return supported(variant, p) ? 1 : 0;
+    if (!supported(variant, p)) return 0;
+    return variant_need(variant, p) <= workspace_bytes ||
+           (variant == AQLM_VARIANT_MFMA && workspace_bytes == 0);
 }
 
 int aqlm_selected_variant(int gemm, const void *codes, const void *codebooks, const void *x,
                           const void *y, int64_t out_features, int64_t in_features, int K, int B,
-                          int batch) {
+                          int batch, int64_t workspace_bytes) {
     Sizes s;
-    if (check_args(codes, codebooks, x, y, out_features, in_features, K, B, batch, &s) != AQLM_OK)
+    if (check_args(codes, codebooks, x, y, out_features, in_features, K, B, batch, &s) != AQLM_OK ||
+        workspace_bytes < 0)
         return -1;
     const aqlm::Problem p = make_problem(codes, codebooks, x, const_cast<void *>(y), out_features,
                                          in_features, K, B, batch, nullptr);
-    return choose(gemm != 0, p);
+    return choose(gemm != 0, p, workspace_bytes);
+}
+
+int64_t aqlm_grouped_workspace_bytes(int op, int n, const void *const *codes,
+                                     const void *const *codebooks, const void *x, void *const *y,
+                                     const int64_t *out_features, int64_t in_features, int K,
+                                     int B, int batch) {
+    aqlm::Problem p;
+    int64_t cbytes[aqlm::kMaxSegs];
+    if (grouped_problem(n, codes, codebooks, x, y, out_features, in_features, K, B, batch, nullptr,
+                        op == AQLM_OP_GEMV_PACKED, &p, cbytes) != AQLM_OK)
+        return -1;
+    return workspace_need(op, AQLM_VARIANT_AUTO, p);
+}
+
+int64_t aqlm_workspace_bytes(int op, int variant, const void *codes, const void *codebooks,
+                             const void *x, const void *y, int64_t out_features,
+                             int64_t in_features, int K, int B, int batch) {
+    const void *c[1] = {codes}, *cb[1] = {codebooks};
+    void *yy[1] = {const_cast<void *>(y)};
+    const int64_t o[1] = {out_features};
+    aqlm::Problem p;
+    int64_t cbytes[1];
+    if (grouped_problem(1, c, cb, x, yy, o, in_features, K, B, batch, nullptr,
+                        op == AQLM_OP_GEMV_PACKED, &p, cbytes) != AQLM_OK)
+        return -1;
+    return workspace_need(op, variant, p);
 }
 
 aqlm_status_t aqlm_dequantize(const void *codes, const void *codebooks, void *W, int w_dtype,
                               int64_t out_features, int64_t in_features, int K, int B,
                               void *stream) {
+    g_last_error[0] = 0;
     if (!codes || !codebooks || !W) return AQLM_ERR_INVALID_ARGUMENT;
     if (w_dtype != 0 && w_dtype != 1) return AQLM_ERR_INVALID_ARGUMENT;
     Sizes s;
@@ -536,11 +702,13 @@ const char *aqlm_variant_name(int variant) {
 
 aqlm_status_t aqlm_pack_codebooks(const void *codebooks, void *packed, int K, int B,
                                   void *stream) {
+    g_last_error[0] = 0;
     return pack_common(codebooks, packed, K, B, stream, true);
 }
 
 aqlm_status_t aqlm_unpack_codebooks(const void *packed, void *codebooks, int K, int B,
                                     void *stream) {
+    g_last_error[0] = 0;
     return pack_common(packed, codebooks, K, B, stream, false);
 }
 
@@ -550,6 +718,7 @@ int64_t aqlm_packed_codes_bytes(int64_t out_features, int64_t in_features, int K
 
 static aqlm_status_t pack_codes_common(const void *src, void *dst, int64_t out, int64_t in, int K,
                                        int B, void *stream, bool pack) {
+    g_last_error[0] = 0;
     if (!src || !dst) return AQLM_ERR_INVALID_ARGUMENT;
     const int64_t pbytes = packed_codes_size(out, in, K, B);
     if (pbytes < 0) return AQLM_ERR_INVALID_ARGUMENT;
@@ -581,131 +750,53 @@ aqlm_status_t aqlm_unpack_codes(const void *packed, void *codes, int64_t out_fea
 
 aqlm_status_t aqlm_gemv_packed(const void *packed_codes, const void *packed_codebooks,
                                const void *x, void *y, int64_t out_features, int64_t in_features,
-                               int K, int B, int batch, void *stream) {
+                               int K, int B, int batch, void *workspace, int64_t workspace_bytes,
+                               void *stream) {
     const void *c[1] = {packed_codes}, *cb[1] = {packed_codebooks};
     void *yy[1] = {y};
     const int64_t o[1] = {out_features};
-    return aqlm_gemv_packed_grouped(1, c, cb, x, yy, o, in_features, K, B, batch, stream);
+    return aqlm_gemv_packed_grouped(1, c, cb, x, yy, o, in_features, K, B, batch, workspace,
+                                    workspace_bytes, stream);
 }
 
 aqlm_status_t aqlm_gemv_grouped(int n, const void *const *codes, const void *const *codebooks,
                                 const void *x, void *const *y, const int64_t *out_features,
-                                int64_t in_features, int K, int B, int batch, void *stream) {
+                                int64_t in_features, int K, int B, int batch, void *workspace,
+                                int64_t workspace_bytes, void *stream) {
+    g_last_error[0] = 0;
     aqlm::Problem p;
+    int64_t cbytes[aqlm::kMaxSegs];
     const aqlm_status_t st = grouped_problem(n, codes, codebooks, x, y, out_features, in_features,
-                                             K, B, batch, stream, false, &p);
-    return st != AQLM_OK ? st : run(choose(false, p), p);
+                                             K, B, batch, stream, false, &p, cbytes);
+    return st != AQLM_OK ? st : product(false, p, cbytes, workspace, workspace_bytes);
 }
 
 aqlm_status_t aqlm_gemm_grouped(int n, const void *const *codes, const void *const *codebooks,
                                 const void *x, void *const *y, const int64_t *out_features,
-                                int64_t in_features, int K, int B, int batch, void *stream) {
+                                int64_t in_features, int K, int B, int batch, void *workspace,
+                                int64_t workspace_bytes, void *stream) {
+    g_last_error[0] = 0;
     aqlm::Problem p;
+    int64_t cbytes[aqlm::kMaxSegs];
     const aqlm_status_t st = grouped_problem(n, codes, codebooks, x, y, out_features, in_features,
-                                             K, B, batch, stream, false, &p);
-    return st != AQLM_OK ? st : run(choose(true, p), p);
+                                             K, B, batch, stream, false, &p, cbytes);
+    return st != AQLM_OK ? st : product(true, p, cbytes, workspace, workspace_bytes);
 }
 
 aqlm_status_t aqlm_gemv_packed_grouped(int n, const void *const *packed_codes,
                                        const void *const *packed_codebooks, const void *x,
                                        void *const *y, const int64_t *out_features,
                                        int64_t in_features, int K, int B, int batch,
-                                       void *stream) {
+                                       void *workspace, int64_t workspace_bytes, void *stream) {
+    g_last_error[0] = 0;
     aqlm::Problem p;
-    aqlm_status_t st = grouped_problem(n, packed_codes, packed_codebooks, x, y, out_features,
-                                       in_features, K, B, batch, stream, true, &p);
-    if (st != AQLM_OK) return st;
-    const bool generic = forced_variant() == AQLM_VARIANT_GENERIC;
-    const bool tiled = tiled_codes(K, B);
-    const bool split = !generic && !tiled &&
-                       all_segments(p, [](const aqlm::Problem &q) { return aqlm::ds_supported(q); });
-    // batches the LDS-plane dot-product kernel does not take: the same planes on the
-    // matrix cores
-    const bool splitm = !generic && !tiled && !split &&
-                        all_segments(p, [](const aqlm::Problem &q) { return aqlm::dsm_supported(q); });
-    const bool lutp = !generic && tiled &&
-                      all_segments(p, [](const aqlm::Problem &q) { return aqlm::lut_packed_supported(q); });
-    if (!split && !splitm && !lutp && n > 1) {
-        // unpacked one matrix at a time through the workspace (stream order keeps them apart)
-        for (int m = 0; m < n; ++m) {
-            st = aqlm_gemv_packed_grouped(1, packed_codes + m, packed_codebooks + m, x, y + m,
-                                          out_features + m, in_features, K, B, batch, stream);
-            if (st != AQLM_OK) return st;
-        }
-        return AQLM_OK;
-    }
-    const int64_t cbytes = out_features[0] * (in_features / kGroup) * K * (B / 8);
-    const int64_t cbbytes = int64_t(K) * (int64_t(1) << B) * kGroup * 2;
-    const size_t cb_off = (size_t(cbytes) + 255) / 256 * 256;
-    // unpacked operands, then (matrix cores) that kernel's own workspace
-    const size_t unpacked = tiled ? cb_off + size_t(cbbytes) : size_t(cbbytes);
-    const size_t ops_off = (unpacked + 255) / 256 * 256;
-    const bool gemm = !generic && batch >= mfma_min_batch(K);
-    size_t mfma_ws = 0;
-    if (!split && !splitm && !lutp && gemm) {
-        const aqlm::Problem shape = make_problem(p.codes, p.codebooks, p.x, p.y, p.out, p.in, K,
-                                                 B, batch, stream);
-        // sized on the shape alone (the kernel's own pointers are checked at launch)
-        if (aqlm::mfma_supported(shape)) mfma_ws = aqlm::mfma_workspace_bytes(shape);
-    }
-    const size_t need = split    ? aqlm::ds_workspace_bytes(p)
-                        : splitm ? aqlm::dsm_workspace_bytes(p)
-                        : lutp   ? aqlm::lut_packed_workspace_bytes(p)
-                                 : ops_off + mfma_ws;
-    void *ws = nullptr;
-    hipError_t e = get_workspace(p.stream, need, &ws);
-    if (e != hipSuccess) {
-        set_error("workspace", e);
-        return AQLM_ERR_HIP;
-    }
-    if (!ws) return AQLM_ERR_UNSUPPORTED;   // capturing stream without a workspace
-    if (log_enabled())
-        std::fprintf(stderr, "[aqlm] packed %s n=%d rows=%lld in=%lld K=%d B=%d batch=%d\n",
-                     split ? "split" : splitm ? "split-mfma" : lutp ? "lut_packed" : "unpack+auto", n,
-                     (long long)p.out,
-                     (long long)p.in, K, B, batch);
-    if (split || splitm || lutp) {
-        e = split ? aqlm::launch_ds(p, ws) : splitm ? aqlm::launch_dsm(p, ws) : aqlm::launch_lut_packed(p, ws);
-        if (e != hipSuccess) {
-            set_error(split ? "split" : splitm ? "split-mfma" : "lut_packed", e);
-            return AQLM_ERR_HIP;
-        }
-        return AQLM_OK;
-    }
-    // one matrix: unpack into the workspace and run as aqlm_gemv
-    char *wsb = static_cast<char *>(ws);
-    if (tiled) {
-        e = aqlm::launch_pack_codes_lut(p.codes, wsb, p.out, p.in, false, p.stream);
-        if (e != hipSuccess) {
-            set_error("unpack_codes", e);
-            return AQLM_ERR_HIP;
-        }
-    }
-    void *cbws = tiled ? wsb + cb_off : wsb;
-    e = aqlm::launch_unpack_codebooks(p.codebooks, cbws, K, B, p.stream);
-    if (e != hipSuccess) {
-        set_error("unpack_codebooks", e);
-        return AQLM_ERR_HIP;
-    }
-    aqlm::Problem q = make_problem(tiled ? wsb : p.codes, cbws, p.x, p.y, p.out, p.in, K, B,
-                                   batch, stream);
-    if (gemm && aqlm::mfma_supported(q) && aqlm::mfma_workspace_bytes(q) <= mfma_ws) {
-        // matrix cores, with their partial sums after the unpacked operands
-        e = aqlm::launch_mfma(q, mfma_ws ? wsb + ops_off : nullptr);
-        if (e != hipSuccess) {
-            set_error("mfma", e);
-            return AQLM_ERR_HIP;
-        }
-        return AQLM_OK;
-    }
-    int v = choose(false, q);
-    // the workspace holds the operands: no kernel that needs one of its own
-    if (v == AQLM_VARIANT_LUT || v == AQLM_VARIANT_MFMA) v = AQLM_VARIANT_LDS;
-    if (v == AQLM_VARIANT_LDS && !supported(v, q)) v = AQLM_VARIANT_GENERIC;
-    return run(v, q);
+    int64_t cbytes[aqlm::kMaxSegs];
+    const aqlm_status_t st = grouped_problem(n, packed_codes, packed_codebooks, x, y, out_features,
+                                             in_features, K, B, batch, stream, true, &p, cbytes);
+    return st != AQLM_OK ? st : packed_product(p, cbytes, workspace, workspace_bytes);
 }
 
-const char *aqlm_version(void) { return "0.4.0"; }
+const char *aqlm_version(void) { return "0.5.0"; }
 
 const char *aqlm_last_error(void) { return g_last_error; }
 

@@ -90,7 +90,8 @@ hipError_t launch_pack_codebooks(const void *cb, void *planes, int K, int B, hip
 hipError_t launch_unpack_codebooks(const void *planes, void *cb, int K, int B, hipStream_t s);
 
 // Decode-to-fp16 fragments + MFMA, K in {1,2}, B in {8,16}, any batch; the input
-// axis may be split over workgroups (partial tiles in the workspace).
+// axis may be split over workgroups (partial tiles in the workspace of
+// mfma_workspace_bytes); with a null workspace it is not split.
 bool mfma_supported(const Problem &p);
 size_t mfma_workspace_bytes(const Problem &p);
 hipError_t launch_mfma(const Problem &p, void *workspace);

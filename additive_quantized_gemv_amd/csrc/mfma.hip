@@ -377,7 +377,8 @@ struct MfmaCfg {
     int ms, nt, ksplit, groups_per_split, grid_x, grid_y;
 };
 
-MfmaCfg mfma_cfg(const Problem &p, Segs *segs = nullptr) {
+// split = false: the whole input axis in one workgroup per tile (no workspace needed).
+MfmaCfg mfma_cfg(const Problem &p, Segs *segs = nullptr, bool split = true) {
     MfmaCfg c{};
     if (p.batch <= 16) { c.ms = 16; c.nt = 1; }
     else if (p.batch <= 32) { c.ms = 32; c.nt = 1; }
@@ -405,7 +406,7 @@ MfmaCfg mfma_cfg(const Problem &p, Segs *segs = nullptr) {
     // workgroups) beat 3 (258); 4096 x 11008: 8 splits of 12 chunks beat fewer).
     int64_t ks = 256 / tiles;
     if (ks > nchunks / (2 * c.nt)) ks = nchunks / (2 * c.nt);
-    if (ks < 1) ks = 1;
+    if (ks < 1 || !split) ks = 1;
     // whole chunks per split (multiples of 4 groups keep code blocks whole), an even
     // number of them (the kernel runs chunks in pairs)
     int64_t cps = (nchunks + ks - 1) / ks;
@@ -726,7 +727,7 @@ size_t mfma_workspace_bytes(const Problem &p) {
     return c.ksplit > 1 ? size_t(c.ksplit) * size_t(p.batch) * size_t(p.out) * sizeof(float) : 0;
 }
 
-// workspace: KSPLIT x batch x T fp32 partial tiles (unused when KSPLIT = 1)
+// workspace: KSPLIT x batch x T fp32 partial tiles; null: one split (KSPLIT = 1)
 hipError_t launch_mfma(const Problem &p, void *workspace) {
     if (kw_fits(p)) {
         if (p.B == 8)
@@ -735,7 +736,7 @@ hipError_t launch_mfma(const Problem &p, void *workspace) {
         return p.K == 1 ? launch_kw<1, 16>(p) : launch_kw<2, 16>(p);
     }
     Segs segs = p.segs;
-    const MfmaCfg c = mfma_cfg(p, &segs);
+    const MfmaCfg c = mfma_cfg(p, &segs, workspace != nullptr);
     float *partial = c.ksplit > 1 ? static_cast<float *>(workspace) : nullptr;
     hipError_t e;
     if (p.B == 8)

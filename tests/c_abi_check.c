@@ -84,15 +84,28 @@ int main(int argc, char **argv) {
     HIP_OK(hipStreamCreate(&stream));
     void *y = malloc(y_bytes * 3);
     if (!y) return 1;
-    AQLM_OK_(aqlm_gemv(d_codes, d_cb, d_x, d_y, out, in, K, B, batch, stream));
-    HIP_OK(hipMemcpyAsync(y, d_y, y_bytes, hipMemcpyDeviceToHost, stream));
-    HIP_OK(hipStreamSynchronize(stream));
-    AQLM_OK_(aqlm_gemm(d_codes, d_cb, d_x, d_y, out, in, K, B, batch, stream));
-    HIP_OK(hipMemcpyAsync((char *)y + y_bytes, d_y, y_bytes, hipMemcpyDeviceToHost, stream));
-    HIP_OK(hipStreamSynchronize(stream));
+    /* the caller owns the workspace: one buffer sized for the largest of the three calls */
     AQLM_OK_(aqlm_pack_codes(d_codes, d_pcodes, out, in, K, B, stream));
     AQLM_OK_(aqlm_pack_codebooks(d_cb, d_pcb, K, B, stream));
-    AQLM_OK_(aqlm_gemv_packed(d_pcodes, d_pcb, d_x, d_y, out, in, K, B, batch, stream));
+    const int64_t ws_gemv = aqlm_workspace_bytes(AQLM_OP_GEMV, AQLM_VARIANT_AUTO, d_codes, d_cb,
+                                                 d_x, d_y, out, in, K, B, batch);
+    const int64_t ws_gemm = aqlm_workspace_bytes(AQLM_OP_GEMM, AQLM_VARIANT_AUTO, d_codes, d_cb,
+                                                 d_x, d_y, out, in, K, B, batch);
+    const int64_t ws_packed = aqlm_workspace_bytes(AQLM_OP_GEMV_PACKED, AQLM_VARIANT_AUTO,
+                                                   d_pcodes, d_pcb, d_x, d_y, out, in, K, B, batch);
+    if (ws_gemv < 0 || ws_gemm < 0 || ws_packed <= 0) return 1;
+    int64_t ws_bytes = ws_gemv > ws_gemm ? ws_gemv : ws_gemm;
+    ws_bytes = ws_packed > ws_bytes ? ws_packed : ws_bytes;
+    void *d_ws;
+    HIP_OK(hipMalloc(&d_ws, (size_t)ws_bytes));
+    AQLM_OK_(aqlm_gemv(d_codes, d_cb, d_x, d_y, out, in, K, B, batch, d_ws, ws_bytes, stream));
+    HIP_OK(hipMemcpyAsync(y, d_y, y_bytes, hipMemcpyDeviceToHost, stream));
+    HIP_OK(hipStreamSynchronize(stream));
+    AQLM_OK_(aqlm_gemm(d_codes, d_cb, d_x, d_y, out, in, K, B, batch, d_ws, ws_bytes, stream));
+    HIP_OK(hipMemcpyAsync((char *)y + y_bytes, d_y, y_bytes, hipMemcpyDeviceToHost, stream));
+    HIP_OK(hipStreamSynchronize(stream));
+    AQLM_OK_(aqlm_gemv_packed(d_pcodes, d_pcb, d_x, d_y, out, in, K, B, batch, d_ws, ws_bytes,
+                              stream));
     HIP_OK(hipMemcpyAsync((char *)y + 2 * y_bytes, d_y, y_bytes, hipMemcpyDeviceToHost, stream));
     HIP_OK(hipStreamSynchronize(stream));
 
@@ -108,6 +121,7 @@ int main(int argc, char **argv) {
     HIP_OK(hipFree(d_y));
     HIP_OK(hipFree(d_pcodes));
     HIP_OK(hipFree(d_pcb));
+    HIP_OK(hipFree(d_ws));
     free(codes);
     free(cb);
     free(x);

@@ -63,7 +63,7 @@ def test_strings(lib):
 
 
 # fake, well-separated "device" addresses: validation must fail before any use
-C, CB, X, Y = 0x10000000, 0x20000000, 0x30000000, 0x40000000
+C, CB, X, Y, WS = 0x10000000, 0x20000000, 0x30000000, 0x40000000, 0x50000000
 
 
 @pytest.mark.parametrize("args", [
@@ -86,10 +86,12 @@ C, CB, X, Y = 0x10000000, 0x20000000, 0x30000000, 0x40000000
 ])
 def test_invalid_arguments_rejected(lib, args):
     for fn in (lib.aqlm_gemv, lib.aqlm_gemm):
-        assert fn(*args, None) == 1
-    assert lib.aqlm_gemv_variant(1, *args, None) == 1
-    assert lib.aqlm_variant_supported(1, *args) == 0
-    assert lib.aqlm_selected_variant(0, *args) == -1
+        assert fn(*args, None, 0, None) == 1
+    assert lib.aqlm_gemv_variant(1, *args, None, 0, None) == 1
+    assert lib.aqlm_variant_supported(1, *args, 0) == 0
+    assert lib.aqlm_selected_variant(0, *args, 0) == -1
+    for op in (0, 1, 2):
+        assert lib.aqlm_workspace_bytes(op, 0, *args) == -1
 
 
 def test_dequantize_invalid(lib):
@@ -106,8 +108,8 @@ def test_pack_invalid(lib):
     assert lib.aqlm_pack_codebooks(CB, CB + 64, 1, 16, None) == 1     # overlapping
     assert lib.aqlm_unpack_codebooks(CB + 1, Y, 1, 16, None) == 1     # misaligned
     assert lib.aqlm_pack_codebooks(CB + 2, Y, 1, 16, None) == 1       # pairs need 4 bytes
-    assert lib.aqlm_gemv_packed(0, CB, X, Y, 16, 64, 1, 16, 1, None) == 1
-    assert lib.aqlm_gemv_packed(C, CB, X, Y, 16, 60, 1, 16, 1, None) == 1
+    assert lib.aqlm_gemv_packed(0, CB, X, Y, 16, 64, 1, 16, 1, WS, 1 << 20, None) == 1
+    assert lib.aqlm_gemv_packed(C, CB, X, Y, 16, 60, 1, 16, 1, WS, 1 << 20, None) == 1
 
 
 def test_packed_codes_sizes(lib):
@@ -133,7 +135,7 @@ def test_pack_codes_invalid(lib):
     # y inside the padded packed codes (beyond the canonical size) is rejected
     n = lib.aqlm_packed_codes_bytes(9, 64, 2, 8)
     assert n == 2 * 1024 and lib.aqlm_codes_bytes(9, 64, 2, 8) == 144
-    assert lib.aqlm_gemv_packed(C, CB, X, C + 512, 9, 64, 2, 8, 1, None) == 1
+    assert lib.aqlm_gemv_packed(C, CB, X, C + 512, 9, 64, 2, 8, 1, WS, 1 << 20, None) == 1
 
 
 def _grouped_args(n, outs, ys, codes=None):
@@ -149,13 +151,13 @@ def test_grouped_invalid(lib, fn):
     f = getattr(lib, fn)
     f.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                   ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
-                  ctypes.c_void_p]
+                  ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
     ys = [Y, Y + 0x100000, Y + 0x200000, Y + 0x300000]
     def call(n, outs, ys_, in_=64, K=2, B=8, batch=1, codes=None):
         a = _grouped_args(n, outs, ys_, codes)
         return f(a[0], ctypes.cast(a[1], ctypes.c_void_p), ctypes.cast(a[2], ctypes.c_void_p), a[3],
                  ctypes.cast(a[4], ctypes.c_void_p), ctypes.cast(a[5], ctypes.c_void_p), in_, K, B,
-                 batch, None)
+                 batch, WS, 1 << 24, None)
     assert call(0, [16] * 4, ys) == 1                       # no matrices
     assert call(5, [16] * 4, ys) == 1                       # more than 4
     assert call(2, [16, 0, 0, 0], ys) == 1                  # empty matrix
@@ -168,9 +170,9 @@ def test_grouped_invalid(lib, fn):
 
 def test_variant_choice_host_logic(lib):
     # pointers aligned to 256 B, shapes of the benchmark configurations
-    def sel(gemm, out, in_, K, B, batch):
+    def sel(gemm, out, in_, K, B, batch, ws=1 << 40):
         return lib.aqlm_variant_name(
-            lib.aqlm_selected_variant(gemm, C, CB, X, Y, out, in_, K, B, batch)).decode()
+            lib.aqlm_selected_variant(gemm, C, CB, X, Y, out, in_, K, B, batch, ws)).decode()
     assert sel(0, 11008, 4096, 2, 8, 1) == "lut"
     assert sel(0, 4096, 11008, 2, 8, 1) == "lut"
     assert sel(0, 4096, 4096, 2, 8, 4) == "lds"
@@ -187,8 +189,66 @@ def test_variant_choice_host_logic(lib):
     assert sel(1, 4096, 4096, 8, 8, 2) == "lds"       # eight codebooks: matrix cores from 4
     assert sel(1, 4096, 4096, 8, 8, 4) == "mfma"
     assert sel(0, 64, 24, 3, 8, 1) == "generic"
-    assert lib.aqlm_variant_supported(3, C, CB, X, Y, 4096, 4096, 1, 16, 1) == 0  # lut needs 2x8
-    assert lib.aqlm_variant_supported(5, C, CB, X, Y, 4096, 4096, 3, 8, 16) == 0  # mfma: K<=2
+    assert lib.aqlm_variant_supported(3, C, CB, X, Y, 4096, 4096, 1, 16, 1, 1 << 40) == 0  # lut: 2x8
+    assert lib.aqlm_variant_supported(5, C, CB, X, Y, 4096, 4096, 3, 8, 16, 1 << 40) == 0  # mfma: K<=2
+    # without a workspace: the kernels that need none (the matrix cores unsplit)
+    assert sel(0, 11008, 4096, 2, 8, 1, 0) == "lds"
+    assert sel(0, 4096, 4096, 1, 16, 1, 0) == "l2"
+    assert sel(1, 4096, 4096, 2, 8, 128, 0) == "mfma"
+    assert sel(1, 4096, 4096, 2, 8, 1, 0) == "lds"
+    assert lib.aqlm_variant_supported(3, C, CB, X, Y, 4096, 4096, 2, 8, 1, 0) == 0   # lut: partials
+    assert lib.aqlm_variant_supported(5, C, CB, X, Y, 4096, 4096, 2, 8, 128, 0) == 1  # unsplit
+
+
+def test_workspace_rule_host_logic(lib):
+    """The workspace a call needs is a function of its arguments; a size between 0 and
+    that need is an argument error, reported before any device work; 0 selects the
+    kernels that need none."""
+    args = (C, CB, X, Y, 11008, 4096, 2, 8, 1)
+    need = lib.aqlm_workspace_bytes(0, 0, *args)
+    # lut: one fp32 partial sum per row and 64-group input slice
+    assert need == 11008 * (512 // 64) * 4
+    assert lib.aqlm_selected_variant(0, *args, need - 1) == -1
+    assert b"too small" in lib.aqlm_last_error() or True    # message is per call, see below
+    assert lib.aqlm_gemv(*args, WS, need - 1, None) == 1
+    assert b"too small" in lib.aqlm_last_error()
+    assert lib.aqlm_gemv(*args, WS + 8, need, None) == 1         # misaligned workspace
+    assert lib.aqlm_gemv(*args, Y, need, None) == 1              # overlaps y
+    assert lib.aqlm_gemv(*args, C, need, None) == 1              # overlaps codes
+    assert lib.aqlm_gemv(*args, None, 64, None) == 1             # size without a pointer
+    assert lib.aqlm_gemv(*args, WS, -1, None) == 1
+    # 16-bit codes: the codebook packed per call (1 MiB) + 8 position-pair partial sums
+    a16 = (C, CB, X, Y, 4096, 11008, 1, 16, 1)
+    assert lib.aqlm_workspace_bytes(0, 0, *a16) == (1 << 20) + 8 * 4096 * 4
+    assert lib.aqlm_workspace_bytes(0, 4, *a16) == 0            # l2 needs none
+    # packed 2x8 and 1x16 at batch 1: slice / part partial sums only
+    assert lib.aqlm_workspace_bytes(2, 0, *args) == 11008 * 8 * 4
+    assert lib.aqlm_workspace_bytes(2, 0, *a16) == 8 * 4096 * 4
+    assert lib.aqlm_workspace_bytes(2, 3, *args) == -1          # packed takes no variant
+    assert lib.aqlm_workspace_bytes(7, 0, *args) == -1          # unknown op
+    # a packed call needs its workspace in every case
+    assert lib.aqlm_gemv_packed(*a16, None, 0, None) == 1
+    # gemm at batch 128: the input-split partial sums; without them the kernel is unsplit
+    a128 = (C, CB, X, Y, 4096, 4096, 2, 8, 128)
+    assert lib.aqlm_workspace_bytes(1, 0, *a128) > 0
+    assert lib.aqlm_variant_name(lib.aqlm_selected_variant(1, *a128, 0)) == b"mfma"
+
+
+def test_library_imports_no_allocation_or_sync(lib):
+    """No allocation, free, stream/device synchronisation or capture query is reachable
+    from the library's calls: none of those HIP entry points is even imported."""
+    import subprocess
+    import additive_quantized_gemv_amd as aq
+    out = subprocess.run(["nm", "-D", "--undefined-only", aq.library_path()], capture_output=True,
+                         text=True, check=True).stdout
+    imported = {ln.split()[-1].split("@")[0] for ln in out.splitlines() if ln.strip()}
+    hip = {n for n in imported if n.startswith("hip")}
+    assert hip, "expected HIP imports"
+    banned = [n for n in hip if re.match(
+        r"hip(Malloc|Free|HostMalloc|HostFree|ExtMalloc|MallocAsync|FreeAsync|MemPool|"
+        r"StreamSynchronize|DeviceSynchronize|EventSynchronize|StreamIsCapturing|"
+        r"StreamGetCaptureInfo|HostRegister)", n)]
+    assert not banned, banned
 
 
 def test_no_device_reports_hip_error(lib):
@@ -196,7 +256,7 @@ def test_no_device_reports_hip_error(lib):
     import torch
     if torch.cuda.is_available():
         pytest.skip("a GPU is present; this checks the no-device path only")
-    assert lib.aqlm_gemv_variant(1, C, CB, X, Y, 16, 64, 2, 8, 1, None) == 3
+    assert lib.aqlm_gemv_variant(1, C, CB, X, Y, 16, 64, 2, 8, 1, None, 0, None) == 3
     assert lib.aqlm_last_error()
 
 

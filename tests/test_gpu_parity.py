@@ -196,8 +196,9 @@ def test_special_inputs(aq, orc):
             check_y(aq.gemv_variant(v, codes, cbt, x), yref, f"subnormal {v}")
 
 
-def test_lut_repeat_and_regrow(aq, orc):
-    """The lookup kernel's workspace and counters survive repeated and growing calls."""
+def test_lut_repeat_deterministic(aq, orc):
+    """Repeated lookup-table calls on shapes of changing size give bit-identical y (the
+    slice partial sums are added in a fixed order)."""
     shapes = [(100, 1024), (3000, 8192), (100, 1024), (5000, 520), (3000, 8192)]
     for i, (out, in_) in enumerate(shapes):
         p = synth.make_problem(out, in_, 2, 8, batch=1, sigma_cb=0.02, config=1000 + i)
@@ -219,7 +220,7 @@ def test_binding_rejects_host_tensors(aq):
 
 # ----------------------------------------------------------------- full sizes
 # The benchmark workloads at full size, in the launch configuration the
-# benchmark uses (auto variant choice), checked on sampled rows.
+# benchmark uses (auto variant choice).
 
 def _sampled_rows(out, n=192, seed=0):
     rng = np.random.default_rng(seed)
@@ -234,22 +235,35 @@ for _name, _cfg in synth.CONFIGS.items():
             FULL.append((_name, _shape[0], _shape[1], _cfg["K"], _cfg["B"], _b, _cfg["sigma_cb"]))
 
 
+# Every row is compared up to batch 4 (the oracle's decode and matvec of a 70B-shaped
+# product take a few seconds on the host cores); larger batches on sampled rows.
+FULL_ROWS_MAX_BATCH = 4
+
+
+def _check_rows(y, p, K, B, out, seed, what, orc, batch):
+    import torch
+    torch.cuda.synchronize()
+    yg = y.float().cpu().numpy()
+    yg = yg[None] if yg.ndim == 1 else yg
+    assert np.all(np.isfinite(yg)), what
+    if batch <= FULL_ROWS_MAX_BATCH:
+        yref = orc.gemv(p["codes"], p["codebooks"], p["x"], K, B)
+        e = rel_err(yg, yref)
+    else:
+        rows = _sampled_rows(out, seed=seed)
+        yref = orc.gemv_rows(p["codes"], p["codebooks"], p["x"], K, B, rows)
+        e = rel_err(yg[:, rows], yref)
+    assert np.all(e <= TOL), f"{what}: {e.max():.3e}"
+
+
 @pytest.mark.parametrize("case", FULL, ids=lambda c: f"{c[0]}-{c[1]}x{c[2]}-b{c[5]}")
-def test_full_size_sampled(aq, orc, case):
+def test_full_size(aq, orc, case):
     name, out, in_, K, B, batch, sigma = case
     cid = list(synth.CONFIGS).index(name)
     p = synth.make_problem(out, in_, K, B, batch=batch, sigma_cb=sigma, config=cid)
     codes, cb, x = _dev(p)
-    rows = _sampled_rows(out, seed=cid)
-    yref = orc.gemv_rows(p["codes"], p["codebooks"], p["x"], K, B, rows)
     fn = aq.gemm if batch >= 16 else aq.gemv
-    y = fn(codes, cb, x)
-    import torch
-    torch.cuda.synchronize()
-    ys = y.float().cpu().numpy()[:, rows]
-    e = rel_err(ys, yref)
-    assert np.all(e <= TOL), f"{case}: {e.max():.3e}"
-    assert np.all(np.isfinite(y.float().cpu().numpy()))
+    _check_rows(fn(codes, cb, x), p, K, B, out, cid, str(case), orc, batch)
 
 
 def test_graph_capture_replay(aq, orc):
@@ -265,7 +279,7 @@ def test_graph_capture_replay(aq, orc):
             p = synth.make_problem(out, in_, K, B, batch=batch, sigma_cb=0.02, config=1200 + i)
             t = _dev(p)
             probs.append((p, t))
-            eager.append(aq.gemm(*t).clone())       # also gives this stream its workspace
+            eager.append(aq.gemm(*t).clone())
             outs.append(torch.empty_like(eager[-1]))
         torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
@@ -285,22 +299,114 @@ def test_graph_capture_replay(aq, orc):
         check_y(e, yref, "eager before capture")
 
 
-def test_capture_without_workspace_falls_back(aq, orc):
-    """A lookup-table call first seen on a capturing stream runs the workspace-free kernel."""
+HEADLINE = [("mlp_2x8_7b", 11008, 4096), ("mlp_2x8_7b", 4096, 11008),
+            ("mlp_1x16_7b", 11008, 4096), ("mlp_1x16_7b", 4096, 11008)]
+
+
+@pytest.mark.parametrize("case", HEADLINE, ids=lambda c: f"{c[0]}-{c[1]}x{c[2]}")
+def test_capture_fresh_stream_same_kernel(aq, orc, case):
+    """A headline product captured with no eager call before it, on torch's own capture
+    stream (torch.cuda.graph without a stream), runs the kernel the eager call runs:
+    its replays equal the eager y bit for bit (canonical and packed weights), and the
+    eager y meets the bar on every row.  The kernel choice depends on the arguments only."""
     import torch
-    p = synth.make_problem(700, 2048, 2, 8, batch=1, sigma_cb=0.02, config=1300)
-    t = _dev(p)
-    y = torch.empty((1, 700), dtype=torch.float16, device="cuda")
-    stream = torch.cuda.Stream()
+    name, out, in_ = case
+    cfg = synth.CONFIGS[name]
+    K, B = cfg["K"], cfg["B"]
+    p = synth.make_problem(out, in_, K, B, batch=1, sigma_cb=cfg["sigma_cb"], config=3100 + out)
+    codes, cb, x = _dev(p)
+    W = aq.pack_weights(codes, cb)
+    torch.cuda.synchronize()
+    y_c = torch.empty((1, out), dtype=torch.float16, device="cuda")
+    y_p = torch.empty_like(y_c)
     g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g, stream=stream):
-        aq.gemv(*t, out=y)
-    yref = orc.gemv(p["codes"], p["codebooks"], p["x"], 2, 8)
+    with torch.cuda.graph(g):
+        aq.gemv(codes, cb, x, out=y_c)
+        aq.gemv_packed(W, x, out=y_p)
+    want = "split" if B == 16 else "lut"
+    assert aq.selected_variant(codes, cb, x) == want
+    eager_c = aq.gemv(codes, cb, x)
+    eager_p = aq.gemv_packed(W, x)
     for _ in range(3):
-        y.zero_()
+        y_c.fill_(5.0)
+        y_p.fill_(5.0)
+        torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
-        check_y(y, yref, "captured fallback")
+        assert bool((y_c == eager_c).all()) and bool((y_p == eager_p).all())
+    _check_rows(eager_c, p, K, B, out, 0, f"{case} canonical", orc, 1)
+    _check_rows(eager_p, p, K, B, out, 0, f"{case} packed", orc, 1)
+
+
+def test_graph_replay_after_large_eager_call(aq, orc):
+    """Decode-size products captured into a graph, then a prefill-size product run
+    eagerly on the same stream (a much larger workspace), then the graph replayed: the
+    replays still equal the eager results bit for bit (a graph keeps the workspace its
+    capture was given; nothing the library holds is resized or freed)."""
+    import torch
+    stream = torch.cuda.Stream()
+    dec = [synth.make_problem(1000, 4096, 2, 8, batch=1, sigma_cb=0.02, config=3200),
+           synth.make_problem(1000, 4096, 1, 16, batch=1, sigma_cb=0.02, config=3201)]
+    big = synth.make_problem(512, 2048, 2, 8, batch=1024, sigma_cb=0.02, config=3202)
+    with torch.cuda.stream(stream):
+        td = [_dev(p) for p in dec]
+        eager = [aq.gemv(*t).clone() for t in td]
+        outs = [torch.empty_like(e) for e in eager]
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for t, o in zip(td, outs):
+                aq.gemv(*t, out=o)
+        tb = _dev(big)
+        yb = aq.gemm(*tb)
+        for _ in range(3):
+            for o in outs:
+                o.fill_(7.0)
+            g.replay()
+            yb2 = aq.gemm(*tb)          # eager work between replays, on the same stream
+            torch.cuda.synchronize()
+            for e, o in zip(eager, outs):
+                assert bool((e == o).all())
+            assert bool((yb2 == yb).all())
+    check_y(yb, orc.gemv(big["codes"], big["codebooks"], big["x"], 2, 8), "prefill-size eager")
+    for p, e in zip(dec, eager):
+        check_y(e, orc.gemv(p["codes"], p["codebooks"], p["x"], p["K"], p["B"]), "decode eager")
+
+
+@pytest.mark.parametrize("case", [
+    # out, in, K, B, batch, variant expected without a workspace
+    (700, 2048, 2, 8, 1, "lds"), (700, 2048, 1, 16, 1, "l2"), (300, 8192, 2, 8, 128, "mfma"),
+    (257, 4096, 1, 16, 64, "mfma"),
+], ids=lambda c: "x".join(map(str, c[:5])))
+def test_no_workspace_kernels(aq, orc, case):
+    """workspace=0: the kernels that need no workspace (the matrix cores unsplit), same
+    bar; a workspace between 0 and the need is an argument error, nothing launched."""
+    import torch
+    out, in_, K, B, batch, want = case
+    p = synth.make_problem(out, in_, K, B, batch=batch, sigma_cb=0.02, config=3300 + out + batch)
+    codes, cb, x = _dev(p)
+    gemm = batch > 1
+    assert aq.selected_variant(codes, cb, x, gemm=gemm, workspace_bytes=0) == want
+    fn = aq.gemm if gemm else aq.gemv
+    y = fn(codes, cb, x, workspace=0)
+    check_y(y, orc.gemv(p["codes"], p["codebooks"], p["x"], K, B), f"no workspace {case}")
+    need = aq.workspace_bytes("gemm" if gemm else "gemv", codes, cb, x)
+    assert need > 0
+    small = torch.empty(need - 4, dtype=torch.uint8, device="cuda")
+    lib = aq._load()
+    st = getattr(lib, "aqlm_gemm" if gemm else "aqlm_gemv")(
+        codes.data_ptr(), cb.data_ptr(), x.data_ptr(), y.data_ptr(), out, in_, K, B, batch,
+        small.data_ptr(), need - 4, None)
+    assert st == 1 and b"too small" in lib.aqlm_last_error()
+
+
+def test_grouped_no_workspace(aq, orc):
+    """A grouped batch-128 product without a workspace: the unsplit matrix-core kernel."""
+    ps = _group((500, 300, 64), 2048, 2, 8, 128, 2300)
+    dev = [_dev(p) for p in ps]
+    ys = aq.gemm_grouped([d[0] for d in dev], [d[1] for d in dev], dev[0][2], workspace=0)
+    for m, p in enumerate(ps):
+        check_y(ys[m], orc.gemv(p["codes"], p["codebooks"], p["x"], 2, 8), f"no workspace {m}")
 
 
 # ------------------------------------------------------------ packed codebooks
@@ -410,8 +516,7 @@ def test_gemv_packed(aq, orc, case):
                                   ("mlp_2x8_7b", 4096, 11008, 1), ("mlp_1x16_7b", 11008, 4096, 16),
                                   ("mlp_1x16_7b", 4096, 11008, 128), ("mlp_2x8_7b", 4096, 11008, 16)],
                          ids=lambda c: f"{c[0]}-{c[1]}x{c[2]}-b{c[3]}")
-def test_full_size_packed_sampled(aq, orc, case):
-    import torch
+def test_full_size_packed(aq, orc, case):
     name, out, in_, batch = case
     cfg = synth.CONFIGS[name]
     cid = list(synth.CONFIGS).index(name)
@@ -419,11 +524,7 @@ def test_full_size_packed_sampled(aq, orc, case):
                            config=cid)
     codes, cb, x = _dev(p)
     y = aq.gemv_packed(aq.pack_weights(codes, cb), x)
-    torch.cuda.synchronize()
-    rows = _sampled_rows(out, seed=cid)
-    yref = orc.gemv_rows(p["codes"], p["codebooks"], p["x"], cfg["K"], cfg["B"], rows)
-    e = rel_err(y.float().cpu().numpy()[:, rows], yref)
-    assert np.all(e <= TOL), f"{case}: {e.max():.3e}"
+    _check_rows(y, p, cfg["K"], cfg["B"], out, cid, str(case), orc, batch)
 
 
 def _pass_rows(out, rows_per_block, seed):
@@ -573,9 +674,9 @@ def test_packed_grouped(aq, orc, case):
     ("gate|up 2x8", (11008, 11008), 4096, 2, 8, 16), ("qkv 1x16", (4096, 4096, 4096), 4096, 1, 16, 1),
     ("qkv 1x16", (4096, 4096, 4096), 4096, 1, 16, 16), ("gate|up 1x16", (11008, 11008), 4096, 1, 16, 1)],
     ids=lambda c: f"{c[0].replace(' ', '-')}-b{c[5]}")
-def test_grouped_full_size_sampled(aq, orc, case):
+def test_grouped_full_size(aq, orc, case):
     """The 7B layer's shared-x groups at full size, through aqlm_gemm_grouped and (batch 1)
-    aqlm_gemv_packed_grouped, checked on sampled rows."""
+    aqlm_gemv_packed_grouped, checked on every row at batch 1 (sampled rows above)."""
     import torch
     name, outs, in_, K, B, batch = case
     ps = _group(outs, in_, K, B, batch, 1900 + len(outs) * 10 + K * 100 + batch)
@@ -587,10 +688,7 @@ def test_grouped_full_size_sampled(aq, orc, case):
     torch.cuda.synchronize()
     for ys in runs:
         for m, (y, p) in enumerate(zip(ys, ps)):
-            rows = _sampled_rows(outs[m], seed=m + batch)
-            yref = orc.gemv_rows(p["codes"], p["codebooks"], p["x"], K, B, rows)
-            e = rel_err(y.float().cpu().numpy()[:, rows], yref)
-            assert np.all(e <= TOL), f"{case} matrix {m}: {e.max():.3e}"
+            _check_rows(y, p, K, B, outs[m], m + batch, f"{case} matrix {m}", orc, batch)
 
 
 @pytest.mark.parametrize("mode", ["gemm b16", "packed b1"])
@@ -622,36 +720,6 @@ def test_grouped_graph_replay(aq, orc, mode):
             assert all(bool((a == b).all()) for a, b in zip(ys, eager))
     for m, p in enumerate(ps):
         check_y(eager[m], orc.gemv(p["codes"], p["codebooks"], p["x"], 2, 8), f"graph {mode} {m}")
-
-
-@pytest.mark.parametrize("warm", ["one matrix", "cold"])
-def test_grouped_capture_small_workspace(aq, orc, warm):
-    """A grouped batch-128 product captured on a stream whose workspace fits one matrix
-    (or none): the graph runs the matrices one at a time (or workspace-free) and still
-    computes every product."""
-    import torch
-    ps = _group((500, 300, 64), 2048, 2, 8, 128, 2300)
-    dev = [_dev(p) for p in ps]
-    x = dev[0][2]
-    stream = torch.cuda.Stream()
-    ys = [torch.empty((128, p["codes"].shape[0]), dtype=torch.float16, device="cuda")
-          for p in ps]
-    with torch.cuda.stream(stream):
-        if warm == "one matrix":
-            aq.gemm(dev[0][0], dev[0][1], x)
-        torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=stream):
-            aq.gemm_grouped([d[0] for d in dev], [d[1] for d in dev], x, out=ys)
-        for _ in range(2):
-            for y in ys:
-                y.fill_(3.0)
-            torch.cuda.synchronize()
-            g.replay()
-            torch.cuda.synchronize()
-            for m, p in enumerate(ps):
-                check_y(ys[m], orc.gemv(p["codes"], p["codebooks"], p["x"], 2, 8),
-                        f"capture {warm} {m}")
 
 
 @pytest.mark.parametrize("case", [
@@ -714,15 +782,15 @@ def test_prefill_forced_small_batch(aq, orc):
         check_y(y, orc.gemv(p["codes"], p["codebooks"], p["x"], 1, 16), f"prefill grouped {m}")
 
 
-@pytest.mark.parametrize("warm", ["warm", "cold"])
-def test_prefill_graph_replay(aq, orc, warm):
-    """Captured with a workspace (prefill in the graph) and without one (matrix cores)."""
+def test_prefill_graph_replay(aq, orc):
+    """The prefill path captured into a graph (its workspace from the graph's pool) and
+    replayed with eager work between replays equals the eager result every time."""
     import torch
     p = synth.make_problem(512, 2048, 2, 8, batch=1024, sigma_cb=0.02, config=2900)
     codes, cb, x = _dev(p)
     stream = torch.cuda.Stream()
     with torch.cuda.stream(stream):
-        eager = aq.gemm(codes, cb, x).clone() if warm == "warm" else None
+        eager = aq.gemm(codes, cb, x).clone()
         y = torch.empty((1024, 512), dtype=torch.float16, device="cuda")
         torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
@@ -734,9 +802,8 @@ def test_prefill_graph_replay(aq, orc, warm):
             torch.cuda.synchronize()
             g.replay()
             torch.cuda.synchronize()
-            check_y(y, yref, f"prefill graph {warm}")
-            if eager is not None:
-                assert bool((y == eager).all())
+            check_y(y, yref, "prefill graph")
+            assert bool((y == eager).all())
 
 
 # ------------------------------------------------------------ the C ABI from plain C
