@@ -533,6 +533,10 @@ int64_t workspace_need(int op, int variant, const aqlm::Problem &p) {
 
 }  // namespace
 
+namespace aqlm {
+void set_last_error_message(const char *what) { set_message(what); }
+}  // namespace aqlm
+
 extern "C" {
 
 aqlm_status_t aqlm_gemv(const void *codes, const void *codebooks, const void *x, void *y,

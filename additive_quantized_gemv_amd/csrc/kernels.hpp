@@ -37,6 +37,9 @@ struct Problem {
 
 // Every launcher returns the hipError_t of its launch (hipSuccess when queued).
 
+// Sets the calling thread's aqlm_last_error() text (defined with the C ABI).
+void set_last_error_message(const char *what);
+
 // Generic: any K in 1..8, B in {8,16}, any batch, any in % 8 == 0.
 hipError_t launch_generic(const Problem &p);
 

@@ -32,8 +32,9 @@
  * Ownership and memory: every pointer is caller-owned.  The library allocates no
  * device or host memory in any call, keeps no pointer after a call returns, keeps no
  * per-stream or per-device state and never synchronizes a stream: calls are
- * reentrant and may run concurrently on any streams.  Kernels that add partial
- * results in a second pass, or that
+ * reentrant and may run concurrently on any streams (aqlm_gemv_packed_noalloc,
+ * which works in a fixed device array of its own, is the one exception).  Kernels
+ * that add partial results in a second pass, or that
  * re-lay out operands per call, use scratch memory the caller passes as `workspace`
  * (device memory, 256-byte aligned, disjoint from every operand, no initial contents
  * needed) of `workspace_bytes` bytes.  aqlm_workspace_bytes() and
@@ -264,6 +265,27 @@ aqlm_status_t aqlm_gemv_packed(const void *packed_codes, const void *packed_code
                                const void *x, void *y, int64_t out_features, int64_t in_features,
                                int K, int B, int batch, void *workspace, int64_t workspace_bytes,
                                void *stream);
+
+/*
+ * aqlm_gemv_packed without a workspace argument, for callers that cannot allocate or
+ * hold scratch memory (code under HIP graph capture without a memory pool of its
+ * own, tight serving loops, harnesses that forbid allocation).  Same product,
+ * arguments and kernels as aqlm_gemv_packed; the scratch is a fixed device array of
+ * the library of aqlm_noalloc_scratch_bytes() = 16 MiB on each GPU, reserved when the
+ * library's code is loaded on that GPU and held until the process ends.  Its address
+ * is looked up on the first call on each device.  A call whose workspace need
+ * (aqlm_workspace_bytes(AQLM_OP_GEMV_PACKED, ...)) exceeds that size returns
+ * AQLM_ERR_INVALID_ARGUMENT with nothing launched (aqlm_last_error() gives both
+ * sizes).  Every call on one GPU shares the array and leaves its contents behind
+ * (the kernels need no initial contents): calls that may run at the same time on one
+ * GPU (different streams, or graphs replayed concurrently) race on it and must be
+ * ordered by the caller.  No call allocates or frees memory.
+ */
+aqlm_status_t aqlm_gemv_packed_noalloc(const void *packed_codes, const void *packed_codebooks,
+                                       const void *x, void *y, int64_t out_features,
+                                       int64_t in_features, int K, int B, int batch,
+                                       void *stream);
+int64_t aqlm_noalloc_scratch_bytes(void);
 
 /*
  * Several products that read the same activations, in one launch: the linears of a

@@ -284,3 +284,18 @@ def test_traffic_record_keyed_on_code_not_comments():
     assert bench.code_text(a) == bench.code_text(b)
     assert bench.code_text(a) != bench.code_text(c)
     assert len(bench.source_sha("split")) == 16
+
+
+def test_noalloc_rejects_beyond_scratch_on_host(lib):
+    """aqlm_gemv_packed_noalloc refuses a call whose scratch need exceeds its fixed array
+    before touching any device (fake, disjoint addresses; packed 2x8 code tiles above
+    batch 1 are unpacked into the scratch: 58.7 MB for 28672 x 8192)."""
+    lib.aqlm_gemv_packed_noalloc.argtypes = [ctypes.c_void_p] * 4 + [
+        ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lib.aqlm_noalloc_scratch_bytes.restype = ctypes.c_int64
+    big = 0x1000000000
+    assert lib.aqlm_noalloc_scratch_bytes() == 16 << 20
+    assert lib.aqlm_gemv_packed_noalloc(big, 2 * big, 3 * big, 4 * big, 28672, 8192, 2, 8, 2,
+                                        None) == 1
+    assert b"16777216" in lib.aqlm_last_error()
+    assert lib.aqlm_gemv_packed_noalloc(0, CB, X, Y, 16, 64, 1, 16, 1, None) == 1
