@@ -180,7 +180,7 @@ bool supported_one(int variant, const aqlm::Problem &p) {
         case AQLM_VARIANT_LUT: return aqlm::lut_supported(p);
         case AQLM_VARIANT_L2: return aqlm::l2_supported(p);
         case AQLM_VARIANT_MFMA: return aqlm::mfma_supported(p);
-        case AQLM_VARIANT_PREFILL: return aqlm::mfma_supported(p);
+        case AQLM_VARIANT_PREFILL: return aqlm::prefill_supported(p);
         case AQLM_VARIANT_SPLIT: return aqlm::ds_supported(p);
         default: return false;
     }

@@ -54,8 +54,9 @@ hipError_t launch_dequantize(const Problem &p, void *W, int w_fp16);
 // dense fp16 W ([out][in], 16-byte aligned) for the prefill path; same bits as
 // launch_dequantize with w_fp16
 hipError_t launch_dequant16(const Problem &p, void *W);
-// prefill: W decoded once into the workspace, then one fp16 GEMM (hipBLASLt) with fp32
-// accumulation; workspace = W (out*in fp16, 256-byte aligned) + the GEMM's own scratch
+// prefill: W decoded once into the workspace (out*in fp16), then the dense fp16 GEMM
+// kernel with fp32 accumulation
+bool prefill_supported(const Problem &p);
 size_t prefill_workspace_bytes(const Problem &p);
 hipError_t launch_prefill(const Problem &p, void *workspace);
 

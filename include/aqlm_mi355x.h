@@ -102,8 +102,9 @@ typedef enum {
                                  workspace on each call); aqlm_gemv_packed also at batch
                                  5..16 on the matrix cores                               */
     AQLM_VARIANT_PREFILL = 7  /* prefill-size batches: W decoded once to fp16 in the
-                                 workspace, then one fp16 GEMM with fp32 accumulation;
-                                 the same K, B and shapes as AQLM_VARIANT_MFMA           */
+                                 workspace (out*in*2 bytes), then the dense fp16 GEMM
+                                 kernel with fp32 accumulation; any K, B, in % 8 == 0;
+                                 x and codebooks 16-byte aligned                         */
 } aqlm_variant_t;
 
 /* The call a workspace query is about (aqlm_workspace_bytes). */

@@ -753,9 +753,11 @@ def test_grouped_four_and_eight_codebooks(aq, orc, case):
 
 @pytest.mark.parametrize("case", [
     # out, in, K, B, batch (aqlm_gemm from batch 256 (16-bit codes, K >= 4) or 1024: W decoded
-    # once, one library GEMM)
+    # once, then the dense GEMM kernel; in % 64 == 0 stages k-tiles straight into LDS, other
+    # input sizes through registers with the last k-tile's chunks past the input zeroed)
     (300, 4096, 2, 8, 1024), (257, 1024, 1, 16, 600), (96, 512, 4, 8, 513), (1000, 2048, 2, 8, 1100),
-    (64, 256, 8, 8, 300), (130, 512, 2, 16, 256),
+    (64, 256, 8, 8, 300), (130, 512, 2, 16, 256), (200, 520, 2, 8, 1030), (129, 4104, 1, 16, 300),
+    (513, 8, 1, 16, 257), (1100, 1024, 1, 16, 2050),
 ], ids=lambda c: "x".join(map(str, c)))
 def test_prefill(aq, orc, case):
     out, in_, K, B, batch = case
