@@ -18,6 +18,12 @@ bracket the timed region.
 
 value = algorithmic bytes per step (codes + codebooks + x + y of the four
 products, each counted once) / time per step, in GB/s.
+
+Other workloads: mlp70b (the Llama-2-70B MLP shapes in 1x16 at batch 1 and 4),
+layer7b (the seven linears of a Llama-2-7B layer at any batch), ceilings (the
+streaming-read, L2-gather and LDS-read rates that bound the kernels), cpu (the host
+kernel), copy (counter calibration).  The run exits with status 3 when a product
+misses the accuracy bar against the oracle.
 """
 from __future__ import annotations
 
@@ -42,9 +48,17 @@ WORKLOAD = [  # name, out, in, K, B
     ("1x16 11008x4096", 11008, 4096, 1, 16),
     ("1x16 4096x11008", 4096, 11008, 1, 16),
 ]
+WORKLOAD_70B = [  # name, out, in, K, B
+    ("1x16 28672x8192", 28672, 8192, 1, 16),
+    ("1x16 8192x28672", 8192, 28672, 1, 16),
+]
 SIGMA_CB = 0.02
 CONFIG_IDS = {8: 2, 16: 3}     # seed namespace per scheme (the 2x8 and 1x16 MLP workloads)
+CONFIG_IDS_70B = {16: 4}
+TOL = 2e-3                     # per-token bar: max_o |y - y_ref| / (max_o |y_ref| + 1e-6)
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "hbm_traffic.md")
+PROFILE_TRACE = os.path.join(ROOT, "profiles", "kernel_trace_mlp7b_b1.md")
+CLOCK_GHZ = 2.4                # MI355X peak engine clock (for cycle conversions)
 KERNEL_SOURCES = {"lut": "lut.hip", "lut_packed": "lut.hip", "lds": "gather.hip", "l2": "l2gather.hip", "mfma": "mfma.hip",
                   "generic": "generic.hip", "split": "dimsplit.hip"}
 
@@ -87,7 +101,57 @@ def measured_traffic(config_name, variant):
     return None
 
 
-def build_inputs(torch, synth, aq, copies):
+def trace_times(product, variant):
+    """(main kernel us, whole call us) medians from the committed kernel-trace summary, if
+    it was taken on this kernel source; else (None, None)."""
+    if not os.path.exists(PROFILE_TRACE):
+        return None, None
+    want_sha = source_sha(variant)
+    for line in open(PROFILE_TRACE):
+        m = re.match(r"\|\s*trace\s*\|\s*([^|]+?)\s*\|\s*(\w+)\s*\|\s*([0-9a-f]+)\s*\|"
+                     r"\s*([0-9.]+)\s*\|\s*([0-9.]+)\s*\|", line)
+        if m and m.group(1) == product and m.group(2) == variant and m.group(3) == want_sha:
+            return float(m.group(4)), float(m.group(5))
+    return None, None
+
+
+def summarize_trace(trace_dir):
+    """Machine-readable rows for the kernel-trace summary from a rocprofv3 --kernel-trace
+    run of the headline benchmark: per packed product, the median duration of its main
+    kernel and of the whole call (main kernel start to the end of the partial-sum kernel
+    that follows it)."""
+    import csv
+    import glob
+    import statistics
+    files = glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True)
+    if not files:
+        sys.exit(f"no kernel_trace.csv under {trace_dir}")
+    rows = []
+    for f in files:
+        rows += list(csv.DictReader(open(f)))
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    mains = {"lut_packed": "lut_packed_kernel", "split": "ds_kernel"}
+    out = []
+    for name, o, i, K, B in WORKLOAD:
+        variant = "split" if B == 16 else "lut_packed"
+        main_d, call_d = [], []
+        for j, r in enumerate(rows):
+            if not re.search(r"::" + mains[variant] + r"<", r["Kernel_Name"]):
+                continue
+            nxt = next((q for q in rows[j + 1:j + 4] if "partial_sum" in q["Kernel_Name"]), None)
+            if nxt is None or int(nxt["Grid_Size_X"]) != o:
+                continue
+            main_d.append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+            call_d.append((int(nxt["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        if main_d:
+            out.append(f"| trace | {name} | {variant} | {source_sha(variant)} | "
+                       f"{statistics.median(main_d):.2f} | {statistics.median(call_d):.2f} |")
+    print("| key | product | variant | source | main kernel us (median) | call us (median) |")
+    print("|---|---|---|---|---|---|")
+    print("\n".join(out))
+
+
+def build_inputs(torch, synth, aq, copies, workload=WORKLOAD, batch=1, config_ids=CONFIG_IDS):
     """Device tensors: per copy, per workload entry (codes, codebooks, x, problem, packed
     weights); plus y buffers."""
     import numpy as np
@@ -95,16 +159,31 @@ def build_inputs(torch, synth, aq, copies):
     sets = []
     for r in range(copies):
         entry = []
-        for name, out, in_, K, B in WORKLOAD:
-            p = synth.make_problem(out, in_, K, B, batch=1, sigma_cb=SIGMA_CB,
-                                   config=CONFIG_IDS[B] * 10 + (0 if out > in_ else 1), copy=r)
+        for name, out, in_, K, B in workload:
+            p = synth.make_problem(out, in_, K, B, batch=batch, sigma_cb=SIGMA_CB,
+                                   config=config_ids[B] * 10 + (0 if out > in_ else 1), copy=r)
             codes = torch.from_numpy(p["codes"] if B == 8 else p["codes"].view(np.int16)).to(dev)
             cb = torch.from_numpy(p["codebooks"]).to(dev)
             packed = aq.pack_weights(codes, cb)
             entry.append((codes, cb, torch.from_numpy(p["x"]).to(dev), p, packed))
         sets.append(entry)
-    ys = [torch.empty((1, out), dtype=torch.float16, device=dev) for _, out, _, _, _ in WORKLOAD]
+    ys = [torch.empty((batch, out), dtype=torch.float16, device=dev) for _, out, _, _, _ in workload]
     return sets, ys
+
+
+def timed_repeats(torch, np, g, launches_per_replay, min_launches=200, min_seconds=0.010,
+                  repeats=11):
+    """Per-launch seconds of a captured graph of `launches_per_replay` launches: one untimed
+    replay, then `repeats` timed repeats of R replays each, R chosen so that a repeat has at
+    least `min_launches` launches and lasts at least `min_seconds` (whatever --steps is);
+    returns median, p10 and p90 over the repeats."""
+    t1 = time_graph(torch, g, 1)                      # untimed: warms the graph, sizes R
+    reps = max(1, math.ceil(min_launches / launches_per_replay), math.ceil(min_seconds / max(t1, 1e-7)))
+    samples = np.array([time_graph(torch, g, reps) / (reps * launches_per_replay)
+                        for _ in range(repeats)])
+    return {"median": float(np.median(samples)), "p10": float(np.percentile(samples, 10)),
+            "p90": float(np.percentile(samples, 90)), "launches_per_repeat": reps * launches_per_replay,
+            "repeats": repeats}
 
 
 def time_graph(torch, g, replays):
@@ -119,31 +198,78 @@ def time_graph(torch, g, replays):
     return start.elapsed_time(end) * 1e-3  # seconds
 
 
-def cpu_baseline(sets, ys_copy0, budget_s):
-    """The oracle as it stands, on the host cores, over the four products of copy 0."""
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(sets, workload, batch, budget_s):
+    """The oracle as it stands, on the host cores, over the products of one step (copy 0):
+    decode to fp32 W + double matvec, repeated for about `budget_s` seconds with all host
+    threads (median step time), then one step with one thread."""
     import numpy as np
     from oracle import Oracle
     orc = Oracle()
     cores = orc.max_threads()
+    step_bytes = sum(algorithmic_bytes(o, i, K, B, batch) for _, o, i, K, B in workload)
+
+    def one_step(o):
+        t0 = time.perf_counter()
+        for (name, out, in_, K, B), (_, _, _, p, _) in zip(workload, sets[0]):
+            o.gemv(p["codes"], p["codebooks"], p["x"], K, B)
+        return time.perf_counter() - t0
+
+    times, t_all = [], time.perf_counter()
+    while not times or time.perf_counter() - t_all < budget_s:
+        times.append(one_step(orc))
+    t_mt = float(np.median(times))
+    # one thread: the first product once (a whole step would take minutes on the 70B shapes)
+    name0, o0, i0, K0, B0 = workload[0]
+    p0 = sets[0][0][3]
     t0 = time.perf_counter()
-    done_bytes, reps, max_err = 0, 0, 0.0
-    while True:
-        for (name, out, in_, K, B), (_, _, _, p, _), yg in zip(WORKLOAD, sets[0], ys_copy0):
-            yref = orc.gemv(p["codes"], p["codebooks"], p["x"], K, B)
-            done_bytes += algorithmic_bytes(out, in_, K, B)
-            if reps == 0:
-                e = np.max(np.abs(yg - yref)) / (np.max(np.abs(yref)) + 1e-6)
-                max_err = max(max_err, float(e))
-        reps += 1
-        if time.perf_counter() - t0 >= budget_s:
-            break
-    dt = time.perf_counter() - t0
-    return {"value": round(done_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": cores,
+    Oracle(nthreads=1).gemv(p0["codes"], p0["codebooks"], p0["x"], K0, B0)
+    t_1t = time.perf_counter() - t0
+    return {"value": round(step_bytes / t_mt / 1e9, 4), "unit": "GB/s", "cores": cores,
             "kind": "oracle",
-            "sample": f"full decode to fp32 W + double matvec of the four products of one step "
-                      f"(copy 0), repeated {reps}x in {dt:.1f} s",
-            "ms_per_step": round(dt / reps * 1e3, 1),
-            "gpu_vs_oracle_max_rel_err": max_err}
+            "sample": f"full decode to fp32 W + double matvec of the {len(workload)} products of "
+                      f"one step (copy 0): median of {len(times)} steps with {cores} threads; "
+                      f"1 thread: the {name0} product once",
+            "ms_per_step": round(t_mt * 1e3, 1),
+            "value_1thread": round(algorithmic_bytes(o0, i0, K0, B0, batch) / t_1t / 1e9, 4),
+            "ms_1thread_first_product": round(t_1t * 1e3, 1),
+            "cpu_model": cpu_model(), "nproc": os.cpu_count()}
+
+
+def parity_and_provenance(torch, np, aq, sets, workload, call, ys, batch):
+    """Copy 0 of every product through the benchmark's own launch path against the oracle
+    (per-token bar), the dense W of aqlm_dequantize against the oracle's fp32 decode (bit
+    for bit, +0 == -0), and a hash of each product's input bytes."""
+    import hashlib
+    from oracle import Oracle
+    orc = Oracle()
+    out = []
+    for idx, ((name, o, i, K, B), (codes, cb, x, p, _)) in enumerate(zip(workload, sets[0])):
+        call(idx, 0)
+        torch.cuda.synchronize()
+        yg = ys[idx].float().cpu().numpy().astype(np.float64)
+        yref = orc.gemv(p["codes"], p["codebooks"], p["x"], K, B)
+        err = np.max(np.abs(yg - yref), axis=1) / (np.max(np.abs(yref), axis=1) + 1e-6)
+        W = aq.dequantize(codes, cb, dtype=torch.float32)
+        torch.cuda.synchronize()
+        Wref = orc.decode(p["codes"], p["codebooks"], K, B)
+        bitexact = bool(np.array_equal(W.cpu().numpy(), Wref))
+        del W, Wref
+        h = hashlib.sha256()
+        for a in (p["codes"], p["codebooks"], p["x"]):
+            h.update(np.ascontiguousarray(a).tobytes())
+        out.append({"max_rel_err": float(err.max()), "w_bitexact": bitexact,
+                    "seed_hash": h.hexdigest()[:16]})
+    return out
 
 
 def main():
@@ -155,8 +281,11 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--warm", action="store_true", help="also time cache-resident (no rotation)")
-    ap.add_argument("--workload", default="mlp", choices=["mlp", "layer7b", "copy", "cpu"],
+    ap.add_argument("--workload", default="mlp",
+                    choices=["mlp", "mlp70b", "layer7b", "ceilings", "copy", "cpu"],
                     help="mlp: the batch-1 MLP products (default, the headline line); "
+                         "mlp70b: the Llama-2-70B MLP shapes in 1x16 at batch 1 and 4; "
+                         "ceilings: streaming-read, L2-gather and LDS-read rates; "
                          "layer7b: the seven linears of a Llama-2-7B layer through aqlm_gemm; "
                          "cpu: the mlp products on the host cores (aqlm_cpu_gemv, no GPU); "
                          "copy: device-to-device copies of 64 and 256 MiB (reference "
@@ -178,7 +307,12 @@ def main():
     ap.add_argument("--grouped", action="store_true",
                     help="--workload layer7b: q|k|v and gate|up as one grouped call each "
                          "(members share the input); the separate calls are timed beside")
+    ap.add_argument("--summarize-trace", metavar="DIR",
+                    help="print the kernel-trace rows for profiles/ from a rocprofv3 "
+                         "--kernel-trace run of the headline benchmark, and exit")
     args = ap.parse_args()
+    if args.summarize_trace:
+        return summarize_trace(args.summarize_trace)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -204,38 +338,24 @@ def main():
         return layer_bench(args, torch, np, aq, synth)
     if args.workload == "copy":
         return copy_bench(args, torch)
-
-    per_copy = sum(algorithmic_bytes(o, i, K, B) for _, o, i, K, B in WORKLOAD)
-    copies = args.layers or args.copies or max(2, math.ceil(2 * MALL_BYTES / per_copy))
-    t_gen = time.perf_counter()
-    sets, ys = build_inputs(torch, synth, aq, copies)
-    torch.cuda.synchronize()
-    print(f"[bench] {copies} rotation copies, {per_copy * copies / 2**20:.0f} MiB, "
-          f"built in {time.perf_counter() - t_gen:.1f} s", file=sys.stderr, flush=True)
-
-    def call(entry_idx, r, canonical=False):
-        codes, cb, x, _, packed = sets[r][entry_idx]
-        if not canonical:
-            aq.gemv_packed(packed, x, out=ys[entry_idx])
-        else:
-            aq.gemv(codes, cb, x, out=ys[entry_idx])
-
-    variants = ["split" if B == 16 else "lut_packed" for _, _, _, _, B in WORKLOAD]
-    canonical_variants = [aq.selected_variant(*sets[0][i][:3]) for i in range(len(WORKLOAD))]
-
-    # one stream for warmup, capture, replay and events: the warmup's eager calls
-    # give it the lookup kernel's workspace before anything is captured
-    stream = torch.cuda.Stream()
-    torch.cuda.synchronize()
-    with torch.cuda.stream(stream):
-        for s in range(args.warmup):
-            for i in range(len(WORKLOAD)):
-                call(i, s % copies)
-                call(i, s % copies, canonical=True)
-    torch.cuda.synchronize()
-    with torch.cuda.stream(stream):
-        return _timed(args, torch, np, aq, sets, ys, copies, per_copy, call, variants, stream,
-                      canonical_variants)
+    if args.workload == "ceilings":
+        return ceilings_bench(args, torch, np)
+    if args.workload == "mlp70b":
+        rc = 0
+        for batch in (1, 4):
+            rc |= mlp_bench(args, torch, np, aq, synth, WORKLOAD_70B, batch, CONFIG_IDS_70B,
+                            f"AQLM GEMV 1x16 on the Llama-2-70B MLP shapes, batch {batch}: "
+                            f"us/call + achieved HBM GB/s",
+                            "Llama-2-70B MLP projections 28672x8192 and 8192x28672, 1x16 "
+                            f"(2 bits/weight), batch {batch}", canonical=False)
+        if rc:
+            sys.exit(rc)
+        return
+    rc = mlp_bench(args, torch, np, aq, synth, WORKLOAD, 1, CONFIG_IDS, METRIC,
+                   "Llama-2-7B MLP projections 11008x4096 and 4096x11008, 2x8 and 1x16 "
+                   "(2 bits/weight), batch 1", canonical=True)
+    if rc:
+        sys.exit(rc)
 
 
 def capture_on(torch, stream, fn):
@@ -245,20 +365,76 @@ def capture_on(torch, stream, fn):
     return g
 
 
-def _timed(args, torch, np, aq, sets, ys, copies, per_copy, call, variants, stream,
-           canonical_variants):
+def mlp_bench(args, torch, np, aq, synth, workload, batch, config_ids, metric, workload_text,
+              canonical):
+    """Products of `workload` at `batch`, packed weights, rotating copies; one JSON line.
+    Returns the exit status (3 when a product misses the accuracy bar)."""
+    per_copy = sum(algorithmic_bytes(o, i, K, B, batch) for _, o, i, K, B in workload)
+    copies = args.copies or max(2, math.ceil(2 * MALL_BYTES / per_copy))
+    t_gen = time.perf_counter()
+    sets, ys = build_inputs(torch, synth, aq, copies, workload, batch, config_ids)
+    torch.cuda.synchronize()
+    print(f"[bench] {workload_text}: {copies} rotation copies, {per_copy * copies / 2**20:.0f} MiB, "
+          f"built in {time.perf_counter() - t_gen:.1f} s", file=sys.stderr, flush=True)
+
+    def call(entry_idx, r, canonical=False):
+        codes, cb, x, _, packed = sets[r][entry_idx]
+        if not canonical:
+            aq.gemv_packed(packed, x, out=ys[entry_idx])
+        else:
+            aq.gemv(codes, cb, x, out=ys[entry_idx])
+
+    variants = ["split" if B == 16 else "lut_packed" for _, _, _, _, B in workload]
+    canonical_variants = [aq.selected_variant(*sets[0][i][:3]) for i in range(len(workload))]
+
+    # one stream for warmup, capture, replay and events
+    stream = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        for s in range(args.warmup):
+            for i in range(len(workload)):
+                call(i, s % copies)
+                if canonical:
+                    call(i, s % copies, canonical=True)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        result = _timed(args, torch, np, sets, copies, per_copy, call, variants, stream,
+                        canonical_variants, workload, batch, metric, workload_text, canonical)
+    checks = parity_and_provenance(torch, np, aq, sets, workload, call, ys, batch)
+    bad = []
+    for rec, chk in zip(result["per_call"], checks):
+        rec.update(chk)
+        if not (chk["max_rel_err"] <= TOL) or not chk["w_bitexact"]:
+            bad.append(rec["product"])
+    result["accuracy"] = {"bar": f"per token max_o |y - y_ref| / (max_o |y_ref| + 1e-6) <= {TOL}",
+                          "max_rel_err": max(c["max_rel_err"] for c in checks),
+                          "w_bitexact": all(c["w_bitexact"] for c in checks), "failed": bad}
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(sets, workload, batch, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+    if bad:
+        print(f"[bench] accuracy bar missed: {bad}", file=sys.stderr, flush=True)
+        return 3
+    return 0
+
+
+def _timed(args, torch, np, sets, copies, per_copy, call, variants, stream,
+           canonical_variants, workload, batch, metric, workload_text, canonical):
 
     def steps_fn(nsteps):
         def f():
             for s in range(nsteps):
-                for i in range(len(WORKLOAD)):
+                for i in range(len(workload)):
                     call(i, s % copies)
         return f
 
-    # main timed region: exactly args.steps steps
+    # main timed region: exactly args.steps steps (each graph replayed once untimed first)
     full = capture_on(torch, stream, steps_fn(copies))
     tail_n = args.steps % copies
     tail = capture_on(torch, stream, steps_fn(tail_n)) if tail_n else None
+    full.replay()
+    if tail is not None:
+        tail.replay()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record(stream)
@@ -272,64 +448,190 @@ def _timed(args, torch, np, aq, sets, ys, copies, per_copy, call, variants, stre
     print(f"[bench] timed {args.steps} steps: {step_s * 1e6:.2f} us/step", file=sys.stderr,
           flush=True)
 
-    # per-product launches, same rotation, for per-kernel averages
+    # per-product launches, same rotation: repeats of >= 200 launches and >= 10 ms each
+    stream_rates = stream_read_rates(torch, np, stream, sorted({algorithmic_bytes(o, i, K, B, batch)
+                                                                for _, o, i, K, B in workload}))
     per_call = []
-    launches = max(copies, (args.steps // copies) * copies)
-    for i, (name, out, in_, K, B) in enumerate(WORKLOAD):
+    for i, (name, out, in_, K, B) in enumerate(workload):
         g = capture_on(torch, stream, lambda i=i: [call(i, r) for r in range(copies)])
-        dt = time_graph(torch, g, launches // copies) / ((launches // copies) * copies)
-        nbytes = algorithmic_bytes(out, in_, K, B)
-        rec = {"product": name, "variant": variants[i], "us_per_call": round(dt * 1e6, 3),
+        t = timed_repeats(torch, np, g, copies)
+        dt = t["median"]
+        nbytes = algorithmic_bytes(out, in_, K, B, batch)
+        weight_bytes = out * (in_ // 8) * K * (B // 8) + K * (1 << B) * 16
+        us_kernel, us_call_trace = trace_times(name, variants[i]) if batch == 1 else (None, None)
+        rec = {"product": name, "variant": variants[i], "batch": batch,
+               "us_per_call": round(dt * 1e6, 3),
+               "us_per_call_p10": round(t["p10"] * 1e6, 3), "us_per_call_p90": round(t["p90"] * 1e6, 3),
+               "launches_per_repeat": t["launches_per_repeat"], "repeats": t["repeats"],
                "gbps": round(nbytes / dt / 1e9, 1),
-               "pct_hbm_peak": round(100 * nbytes / dt / 1e9 / HBM_PEAK_GBPS, 1),
-               "algorithmic_bytes": nbytes}
+               "pct_hbm_peak": round(100 * nbytes / dt / 1e9 / HBM_PEAK_GBPS, 2),
+               "compressed_weight_gbps": round(weight_bytes / dt / 1e9, 1),
+               "algorithmic_bytes": nbytes,
+               "us_kernel_trace": us_kernel, "us_call_kernel_trace": us_call_trace,
+               "pct_hbm_peak_kernel_trace":
+                   round(100 * nbytes / (us_kernel * 1e-6) / 1e9 / HBM_PEAK_GBPS, 2) if us_kernel else None}
+        sr = stream_rates.get(nbytes)
+        if sr:
+            rec["stream_read_gbps_same_bytes"] = round(sr, 1)
+            rec["pct_of_measured_stream"] = round(100 * nbytes / dt / 1e9 / sr, 1)
         if args.warm:
             gw = capture_on(torch, stream, lambda i=i: [call(i, 0) for _ in range(copies)])
-            dtw = time_graph(torch, gw, launches // copies) / ((launches // copies) * copies)
-            rec["us_per_call_cache_resident"] = round(dtw * 1e6, 3)
-        # the same product from the canonical layout (aqlm_gemv), timed beside it
-        gc = capture_on(torch, stream,
-                        lambda i=i: [call(i, r, canonical=True) for r in range(copies)])
-        dtc = time_graph(torch, gc, launches // copies) / ((launches // copies) * copies)
-        rec["canonical_layout"] = {"variant": canonical_variants[i],
-                                   "us_per_call": round(dtc * 1e6, 3),
-                                   "gbps": round(nbytes / dtc / 1e9, 1)}
+            rec["us_per_call_cache_resident"] = round(timed_repeats(torch, np, gw, copies)["median"] * 1e6, 3)
+        if canonical:
+            # the same product from the canonical layout (aqlm_gemv), timed beside it
+            gc = capture_on(torch, stream,
+                            lambda i=i: [call(i, r, canonical=True) for r in range(copies)])
+            dtc = timed_repeats(torch, np, gc, copies)["median"]
+            rec["canonical_layout"] = {"variant": canonical_variants[i],
+                                       "us_per_call": round(dtc * 1e6, 3),
+                                       "gbps": round(nbytes / dtc / 1e9, 1)}
         per_call.append(rec)
-        print(f"[bench] {name} ({variants[i]}): {rec['us_per_call']} us, {rec['gbps']} GB/s",
+        print(f"[bench] {name} b{batch} ({variants[i]}): {rec['us_per_call']} us "
+              f"(p10 {rec['us_per_call_p10']}, p90 {rec['us_per_call_p90']}), {rec['gbps']} GB/s",
               file=sys.stderr, flush=True)
 
-    step_bytes = per_copy
-    value = step_bytes / step_s / 1e9
-    dom = max(range(len(WORKLOAD)), key=lambda i: per_call[i]["us_per_call"])
+    value = per_copy / step_s / 1e9
+    dom = max(range(len(workload)), key=lambda i: per_call[i]["us_per_call"])
     d = per_call[dom]
     achieved = d["algorithmic_bytes"] / (d["us_per_call"] * 1e-6) / 1e9
-    traffic = measured_traffic(d["product"], d["variant"])
+    traffic = measured_traffic(d["product"], d["variant"]) if batch == 1 else None
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
                 "kernel": f"{d['variant']} ({d['product']})",
-                "algorithmic_bytes_per_launch": d["algorithmic_bytes"]}
-
-    result = {
-        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+                "algorithmic_bytes_per_launch": d["algorithmic_bytes"],
+                "per_launch_time": "median of repeats of whole calls (main + partial-sum kernel) "
+                                   "timed by HIP events on the launch stream"}
+    if d.get("us_kernel_trace"):
+        roofline["frac_kernel_trace"] = round(d["algorithmic_bytes"] / (d["us_kernel_trace"] * 1e-6)
+                                              / 1e9 / HBM_PEAK_GBPS, 4)
+    rocm = "unknown"
+    try:
+        rocm = open("/opt/rocm/.info/version").read().strip()
+    except OSError:
+        pass
+    return {
+        "metric": metric, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(step_s * 1e3, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "fp16 x fp16 -> fp32 (u8/u16 codes)", "data": "synthetic",
-        "config": {"workload": "Llama-2-7B MLP projections 11008x4096 and 4096x11008, "
-                               "2x8 and 1x16 (2 bits/weight), batch 1",
-                   "batch": 1, "rotation_copies": copies,
+        "config": {"workload": workload_text,
+                   "batch": batch, "rotation_copies": copies,
                    "rotation_bytes": per_copy * copies, "launch": "hip graph replay",
-                   "step": "4 products (2 shapes x 2 schemes), packed weights"},
+                   "step": f"{len(workload)} products, packed weights"},
         "per_call": per_call,
         "roofline": roofline,
+        "rocm_version": rocm,
     }
-    if not args.no_cpu_baseline:
-        ys_copy0 = []
-        for i in range(len(WORKLOAD)):
-            call(i, 0)
-            torch.cuda.synchronize()
-            ys_copy0.append(ys[i].float().cpu().numpy().astype(np.float64))
-        result["cpu_baseline"] = cpu_baseline(sets, ys_copy0, args.cpu_seconds)
-    print(json.dumps(result), flush=True)
+
+
+_CEIL = None
+
+
+def _ceil_lib():
+    """The measurement-only kernels of libaqlm_ceilings.so (built beside the library)."""
+    global _CEIL
+    if _CEIL is None:
+        import ctypes
+        path = os.path.join(ROOT, "additive_quantized_gemv_amd", "libaqlm_ceilings.so")
+        if not os.path.exists(path):
+            sys.exit(f"{path} is not built (additive_quantized_gemv_amd/build.py)")
+        lib = ctypes.CDLL(path)
+        vp, i64, ci = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+        lib.ceil_stream_read.argtypes = [vp, i64, ci, vp, vp]
+        lib.ceil_l2_gather.argtypes = [vp, i64, ci, ci, vp, vp]
+        lib.ceil_lds_read.argtypes = [ci, ci, ci, vp, vp]
+        for f in (lib.ceil_stream_read, lib.ceil_l2_gather, lib.ceil_lds_read):
+            f.restype = ci
+        _CEIL = lib
+    return _CEIL
+
+
+def _launch_ok(rc, what):
+    if rc != 0:
+        sys.exit(f"{what}: launch failed ({rc})")
+
+
+def stream_read_rates(torch, np, stream, sizes):
+    """GB/s of one streaming-read launch over each byte count in `sizes` (the best of four
+    grid sizes), rotating over buffers larger than twice the Infinity Cache (fresh data,
+    as the products see)."""
+    import ctypes
+    lib = _ceil_lib()
+    rates = {}
+    sink = torch.empty(2048 * 256, dtype=torch.int32, device="cuda")
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    for n in sizes:
+        n16 = (n + 15) // 16 * 16
+        nbuf = max(2, math.ceil(2 * MALL_BYTES / n16))
+        bufs = [torch.empty(n16, dtype=torch.uint8, device="cuda").fill_(1) for _ in range(nbuf)]
+        best = 0.0
+        for blocks in (256, 512, 1024, 2048):
+            def f(blocks=blocks):
+                for b in bufs:
+                    _launch_ok(lib.ceil_stream_read(b.data_ptr(), n16, blocks, sink.data_ptr(), sp),
+                               "stream_read")
+            g = capture_on(torch, stream, f)
+            best = max(best, n16 / timed_repeats(torch, np, g, nbuf)["median"] / 1e9)
+        rates[n] = best
+        del bufs
+    return rates
+
+
+def ceilings_bench(args, torch, np):
+    """Rates that bound the kernels, from microbenchmarks with the kernels' access patterns
+    (HIP graphs of back-to-back launches, HIP events on the launch stream): streaming read
+    per launch at the product sizes and larger, random 16-byte gathers from an L2-resident
+    1 MiB table, and random LDS reads of 16 and 4 bytes (and 4 bytes with half of the
+    lanes on one word).  Each rate is turned into the floor it sets for the batch-1 kernels."""
+    import ctypes
+    lib = _ceil_lib()
+    stream = torch.cuda.Stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    res = {"workload": "ceiling microbenchmarks (streaming read, L2 gathers, LDS reads)",
+           "cus": cus, "clock_ghz_assumed": CLOCK_GHZ}
+    with torch.cuda.stream(stream):
+        sizes = [algorithmic_bytes(11008, 4096, 2, 8), algorithmic_bytes(11008, 4096, 1, 16),
+                 22 << 20, 58720256, 256 << 20]
+        rates = stream_read_rates(torch, np, stream, sizes)
+        res["stream_read"] = [{"bytes": n, "gbps": round(r, 1), "us": round(n / r / 1e3, 3),
+                               "pct_of_8TBps": round(100 * r / HBM_PEAK_GBPS, 1)}
+                              for n, r in rates.items()]
+        # L2 gathers: 1 MiB table, 8 in flight per thread
+        table = torch.empty(1 << 20, dtype=torch.uint8, device="cuda").fill_(3)
+        blocks, per = cus * 8, 64
+        sink = torch.empty(blocks * 256, dtype=torch.int32, device="cuda")
+        g = capture_on(torch, stream, lambda: [_launch_ok(lib.ceil_l2_gather(
+            table.data_ptr(), 1 << 20, blocks, per, sink.data_ptr(), sp), "l2_gather") for _ in range(4)])
+        t = timed_repeats(torch, np, g, 4)["median"]
+        gathers = blocks * 256 * per
+        rate = gathers / t
+        res["l2_gather"] = {"table_bytes": 1 << 20, "gathers_per_launch": gathers,
+                            "g_per_s": round(rate / 1e9, 2),
+                            "per_clk_per_cu": round(rate / (CLOCK_GHZ * 1e9) / cus, 3),
+                            "floor_us_1x16_11008x4096": round(11008 * 512 / rate * 1e6, 2)}
+        # LDS reads: per-instruction time from two iteration counts (the table fill cancels)
+        lds = {}
+        sink2 = torch.empty(cus * 1024, dtype=torch.int32, device="cuda")
+        for mode, label in ((0, "b128 random"), (1, "b32 random"), (2, "b32 half random half one word")):
+            ts = []
+            for iters in (1024, 3072):
+                g = capture_on(torch, stream, lambda iters=iters: [_launch_ok(lib.ceil_lds_read(
+                    mode, cus, iters, sink2.data_ptr(), sp), "lds_read") for _ in range(2)])
+                ts.append(timed_repeats(torch, np, g, 2, min_launches=20)["median"])
+            per_instr = (ts[1] - ts[0]) / ((3072 - 1024) * 16)     # 16 waves per CU
+            lds[label] = {"ns_per_wave_instr_per_cu": round(per_instr * 1e9, 3),
+                          "cycles_per_wave_instr": round(per_instr * CLOCK_GHZ * 1e9, 2)}
+        # floors for the batch-1 kernels: 2x8 LDS gather (two 16-byte reads per group-row),
+        # 1x16 split (each code looked up by the 8 workgroups of its row range, 4 bytes,
+        # half of the lanes on the zero word)
+        gr = 11008 * 512
+        lds["floor_us_2x8_lds_gather_11008x4096"] = round(
+            2 * gr / 64 / cus * lds["b128 random"]["ns_per_wave_instr_per_cu"] / 1e3, 2)
+        lds["floor_us_1x16_split_11008x4096"] = round(
+            8 * gr / 64 / cus * lds["b32 half random half one word"]["ns_per_wave_instr_per_cu"] / 1e3, 2)
+        res["lds_read"] = lds
+    print(json.dumps(res), flush=True)
 
 
 def copy_bench(args, torch):
@@ -548,25 +850,28 @@ def layer_bench(args, torch, np, aq, synth):
         layer_graph = capture_on(torch, stream, lambda: [call_unit(u, r) for r in range(copies)
                                                          for u in units])
         reps = max(1, args.steps // copies)
-        dt_layer = time_graph(torch, layer_graph, reps) / (reps * copies)
+        t_layer = timed_repeats(torch, np, layer_graph, copies, min_launches=reps * copies,
+                                min_seconds=0.01, repeats=5)
+        dt_layer = t_layer["median"]
         dt_sep = None
         if any(len(u) > 1 for u in units):
             sep_graph = capture_on(torch, stream, lambda: [call(i, r) for r in range(copies)
                                                            for i in range(len(layer))])
-            dt_sep = time_graph(torch, sep_graph, reps) / (reps * copies)
+            dt_sep = timed_repeats(torch, np, sep_graph, copies, min_launches=reps * copies,
+                                   repeats=5)["median"]
         groups = []
         for u in units:
             if len(u) == 1:
                 continue
             g = capture_on(torch, stream, lambda u=u: [call_unit(u, r) for r in range(copies)])
-            dt = time_graph(torch, g, reps) / (reps * copies)
+            dt = timed_repeats(torch, np, g, copies, repeats=5)["median"]
             nbytes = sum(algorithmic_bytes(layer[i][1], layer[i][2], K, B, batch) for i in u)
             groups.append({"linears": "|".join(names[i] for i in u),
                            "us_per_call": round(dt * 1e6, 3), "gbps": round(nbytes / dt / 1e9, 1)})
         per = []
         for i, (name, out, in_) in enumerate(layer):
             g = capture_on(torch, stream, lambda i=i: [call(i, r) for r in range(copies)])
-            dt = time_graph(torch, g, reps) / (reps * copies)
+            dt = timed_repeats(torch, np, g, copies, repeats=5)["median"]
             nbytes = algorithmic_bytes(out, in_, K, B, batch)
             flops = 2.0 * out * in_ * batch
             per.append({"linear": name, "shape": f"{out}x{in_}", "variant": variants[i],
@@ -592,7 +897,7 @@ def layer_bench(args, torch, np, aq, synth):
                         f"{', grouped q|k|v and gate|up' if args.grouped else ''}: "
                         f"layer time and achieved rates",
               "value": round(layer_bytes / dt_layer / 1e9, 1), "unit": "GB/s",
-              "n_gpus": 1, "steps": reps * copies, "warmup": max(2, args.warmup // 10),
+              "n_gpus": 1, "steps": t_layer["launches_per_repeat"], "warmup": max(2, args.warmup // 10),
               "ms_per_step": round(dt_layer * 1e3, 5), "higher_is_better": True,
               "scaling": "weak", "vs_baseline": None,
               "dtype": "fp16 x fp16 -> fp32 (u8/u16 codes)", "data": "synthetic",
@@ -600,6 +905,7 @@ def layer_bench(args, torch, np, aq, synth):
                                      f"11008x4096; down 4096x11008; {args.scheme}, batch {batch}",
                          "batch": batch, "rotation_copies": copies, "launch": "hip graph replay"},
               "layer_us": round(dt_layer * 1e6, 2),
+              "layer_us_p10": round(t_layer["p10"] * 1e6, 2), "layer_us_p90": round(t_layer["p90"] * 1e6, 2),
               "grouped": [names[u[0]] if len(u) == 1 else "|".join(names[i] for i in u)
                           for u in units] if args.grouped else None,
               "layer_us_separate_calls": round(dt_sep * 1e6, 2) if dt_sep else None,

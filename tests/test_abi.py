@@ -302,3 +302,16 @@ def test_noalloc_rejects_beyond_scratch_on_host(lib):
                                         None) == 1
     assert b"16777216" in lib.aqlm_last_error()
     assert lib.aqlm_gemv_packed_noalloc(0, CB, X, Y, 16, 64, 1, 16, 1, None) == 1
+
+
+def test_trace_record_read_back():
+    """bench.py reads the kernel-only times of the headline products from the committed
+    kernel-trace summary while the kernel sources hash as they did when it was taken."""
+    import importlib.util
+    spec = importlib.util.spec_from_file_location("bench_mod", os.path.join(ROOT, "bench.py"))
+    bench = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(bench)
+    for name, o, i, K, B in bench.WORKLOAD:
+        main_us, call_us = bench.trace_times(name, "split" if B == 16 else "lut_packed")
+        assert main_us is not None and 0 < main_us < call_us, name
+    assert bench.trace_times("1x16 4096x11008", "lut_packed") == (None, None)
