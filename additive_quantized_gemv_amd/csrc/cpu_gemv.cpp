@@ -57,8 +57,14 @@ Isa detect() {
 
 }  // namespace
 
+// The kernels below use AVX2, FMA and F16C (AVX-512 ones say so themselves); they run only
+// after detect().  gcc takes a target region, clang an attribute applied to each function.
+#if defined(__clang__)
+#pragma clang attribute push(__attribute__((target("avx2,fma,f16c"))), apply_to = function)
+#else
 #pragma GCC push_options
 #pragma GCC target("avx2,fma,f16c")
+#endif
 
 namespace {
 
@@ -419,7 +425,11 @@ aqlm_status_t cpu_gemv(const void *codes_, const void *codebooks_, const void *x
 
 }  // namespace
 
+#if defined(__clang__)
+#pragma clang attribute pop
+#else
 #pragma GCC pop_options
+#endif
 
 extern "C" {
 
