@@ -31,10 +31,11 @@ constexpr int kMfmaMinBatch8Codebooks = 4;
 // 123.6 / 132.4; batch 4 131.8 / 157.7 against 124.9 / 134.4).
 constexpr int kSplitMaxBatch = 4;
 constexpr int kSplitMaxBatchGemm = 2;
-// Measured on MI355X (7B layer linears, canonical weights): the prefill path overtakes the
-// matrix-core kernels at batch 256 for 16-bit codes (decoding a 1 MiB codebook through
-// L2 per token tile costs more) and at 1024 for 8-bit codes with K <= 2.
-constexpr int kPrefillMinBatch16 = 256;
+// Measured on MI355X (7B layer, seven separate calls, us, matrix cores against prefill):
+// 16-bit codes b256 417 / 542, b512 732 / 576, b1024 1190 / 741 (decoding a 1 MiB codebook
+// through L2 per token tile costs more); 8-bit codes with K <= 2: b512 429 / 540, b1024
+// 690 / 692, b2048 1387 / 1018.
+constexpr int kPrefillMinBatch16 = 512;
 constexpr int kPrefillMinBatch8 = 1024;
 // The workspace is cut into fp32 / 16-byte-vector regions at 256-byte offsets.
 constexpr uintptr_t kWorkspaceAlign = 256;

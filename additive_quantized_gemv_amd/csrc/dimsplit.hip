@@ -29,9 +29,10 @@
 // * The K*8 workgroups of one row range get block ids that are equal modulo 8,
 //   so the dispatcher puts them on the same XCD: the codes come from HBM once and
 //   from that XCD's L2 for the other planes.
-// * The waves of a workgroup take the range's rows in chunks of 1..8 rows from an
+// * The waves of a workgroup take the range's rows in chunks of 4, 2 or 1 rows (fewer
+//   as the chunk positions per lane grow from 1-2 to 3-4 to 5-8) from an
 //   LDS counter (the waves the LDS serves first take more chunks).  A wave walks a
-//   chunk's 16-byte code pieces with the next chunk's in flight (a ring of 5..8
+//   chunk's 16-byte code pieces with the next chunk's in flight (a ring of 4..8
 //   loads, issued branch-free) and issues each slot's lookups one slot ahead of its
 //   products; each looked-up pair is multiplied with v_dot2_f32_f16 against the
 //   matching activation pair x[b][8j + 2q .. +1], staged in LDS (in registers when

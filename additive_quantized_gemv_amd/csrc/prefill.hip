@@ -37,14 +37,16 @@ namespace {
 constexpr int kPfThreads = 256;            // 4 waves
 constexpr int kXcds = 8;
 
-// BK inputs per k-tile (32 or 64): CPR = BK/8 chunks of 16 bytes per staged row.
-template <int TM, int TN, int BK>
+// BK inputs per k-tile (32 or 64): CPR = BK/8 chunks of 16 bytes per staged row.  WM
+// waves along the rows (2 or 4), two along the tokens.
+template <int TM, int TN, int BK, int WM = 2>
 struct PfTile {
-    static constexpr int BM = 64 * TM;                       // rows per workgroup
+    static constexpr int THREADS = 2 * WM * kWave;
+    static constexpr int BM = WM * 32 * TM;                  // rows per workgroup
     static constexpr int BN = 64 * TN;                       // tokens per workgroup
     static constexpr int CPR = BK / 8;                       // chunks per staged row
     static constexpr int ROWB = BK * 2;                      // LDS bytes per staged row
-    static constexpr int RPL = kPfThreads / CPR;             // staged rows per load round
+    static constexpr int RPL = THREADS / CPR;                // staged rows per load round
     static constexpr int LOADS = (BM + BN) / RPL;            // 16-B loads per thread
     static constexpr int BUF = (BM + BN) * ROWB;             // LDS bytes per buffer
     static constexpr int STEPS = BK / 16;                    // MFMA k-steps per k-tile
@@ -178,13 +180,13 @@ prefill_gemm_kernel(const uint16_t *__restrict__ W, const uint16_t *__restrict__
 // fetches the chunk that belongs at its LDS slot.  For in % 64 == 0 (no chunk past
 // the input axis); the stages are separate arrays so that LDS reads of one are not
 // ordered behind the loads into another.
-template <int TM, int TN>
-__global__ void __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+template <int TM, int TN, int WM>
+__global__ void __launch_bounds__(2 * WM * kWave) __attribute__((amdgpu_waves_per_eu(WM / 2, WM / 2)))
 prefill_gemm_dma_kernel(const uint16_t *__restrict__ W, const uint16_t *__restrict__ x,
                         uint16_t *__restrict__ y, int out, int in, int batch, int tiles_n,
                         int ntiles, int per_xcd) {
-    typedef PfTile<TM, TN, 64> T;
-    static_assert(T::RPL == 32 && T::CPR == 8, "8 rows of 8 chunks per wave and round");
+    typedef PfTile<TM, TN, 64, WM> T;
+    static_assert(T::CPR == 8 && T::RPL % 16 == 0, "8 rows of 8 chunks per wave and round");
     __shared__ __attribute__((aligned(1024))) char st0[T::BUF];
     __shared__ __attribute__((aligned(1024))) char st1[T::BUF];
     __shared__ __attribute__((aligned(1024))) char st2[T::BUF];
@@ -197,19 +199,19 @@ prefill_gemm_dma_kernel(const uint16_t *__restrict__ W, const uint16_t *__restri
 
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const int wm = wave & 1, wn = wave >> 1;
+    const int wm = wave % WM, wn = wave / WM;
     const int nk = in / 64;
 
-    // Round i of wave w fills staged rows 8w + 32i .. +7 (1 KB); lane l fills row
-    // 8w + 32i + l/8, slot l%8, i.e. logical chunk (l%8) ^ ((row >> 1) & 7), the same
-    // chunk in every round (32i does not change (row >> 1) & 7).
+    // Round i of wave w fills staged rows 8w + RPL*i .. +7 (1 KB); lane l fills row
+    // 8w + RPL*i + l/8, slot l%8, i.e. logical chunk (l%8) ^ ((row >> 1) & 7), the same
+    // chunk in every round (RPL, a multiple of 16, does not change (row >> 1) & 7).
     const int lrow = 8 * wave + (lane >> 3);
     const int cl = (lane & 7) ^ ((lrow >> 1) & 7);
     const uint16_t *src[T::LOADS];
 #pragma unroll
     for (int i = 0; i < T::LOADS; ++i) {
-        const int r = lrow + 32 * i;
-        src[i] = 32 * i < T::BN ? x + size_t(min(tok0 + r, batch - 1)) * size_t(in) + 8 * cl
+        const int r = lrow + T::RPL * i;
+        src[i] = T::RPL * i < T::BN ? x + size_t(min(tok0 + r, batch - 1)) * size_t(in) + 8 * cl
                                 : W + size_t(min(row0 + r - T::BN, out - 1)) * size_t(in) + 8 * cl;
     }
     // The loads are written in asm so that the compiler does not track them: its wait
@@ -234,7 +236,7 @@ prefill_gemm_dma_kernel(const uint16_t *__restrict__ W, const uint16_t *__restri
             const uint16_t *g = src[i] + size_t(kt) * 64;
             asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
                          :
-                         : "v"(g), "s"(stage + uint32_t(32 * i * T::ROWB))
+                         : "v"(g), "s"(stage + uint32_t(T::RPL * i * T::ROWB))
                          : "memory", "m0");
         }
     };
@@ -349,12 +351,12 @@ PfCfg pf_cfg(const Problem &p) {
 
 size_t w_bytes(const Problem &p) { return (size_t(p.out) * size_t(p.in) * 2 + 255) / 256 * 256; }
 
-template <int TM, int TN>
+template <int TM, int TN, int WM = 2>
 hipError_t launch_pf(const Problem &p, const PfCfg &c, const uint16_t *W) {
     constexpr int BK = 64;
     if (p.in % 64 == 0) {
-        hipLaunchKernelGGL((prefill_gemm_dma_kernel<TM, TN>), dim3(unsigned(c.per_xcd * kXcds)),
-                           dim3(kPfThreads), 0, p.stream, W, static_cast<const uint16_t *>(p.x),
+        hipLaunchKernelGGL((prefill_gemm_dma_kernel<TM, TN, WM>), dim3(unsigned(c.per_xcd * kXcds)),
+                           dim3(2 * WM * kWave), 0, p.stream, W, static_cast<const uint16_t *>(p.x),
                            static_cast<uint16_t *>(p.y), int(p.out), int(p.in), p.batch,
                            c.tiles_n, c.tiles_m * c.tiles_n, c.per_xcd);
         return hipGetLastError();
@@ -384,7 +386,7 @@ hipError_t launch_prefill(const Problem &p, void *workspace) {
     hipError_t e = launch_dequant16(p, W);
     if (e != hipSuccess) return e;
     const PfCfg c = pf_cfg(p);
-    if (c.tm == 4) return launch_pf<4, 2>(p, c, W);
+    if (c.tm == 4) return launch_pf<2, 2, 4>(p, c, W);     // 256 x 128: 8 waves of 64 x 64
     return launch_pf<2, 2>(p, c, W);
 }
 

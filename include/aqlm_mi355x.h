@@ -140,7 +140,7 @@ aqlm_status_t aqlm_gemv(const void *codes, const void *codebooks, const void *x,
  * compares against fp16) with the same arguments; from batch 2 (4 for eight
  * codebooks, 3 for 16-bit codes, which take the split kernel up to batch 2;
  * AQLM_MFMA_MIN_BATCH overrides the first two) it uses the decode-to-fp16 + MFMA
- * kernels, below that it behaves as aqlm_gemv.  From prefill-size batches (256 for
+ * kernels, below that it behaves as aqlm_gemv.  From prefill-size batches (512 for
  * 16-bit codes or K >= 4, 1024 otherwise; AQLM_PREFILL_MIN_BATCH overrides) W is
  * instead decoded once into the workspace as dense fp16 (out*in*2 bytes plus the
  * GEMM's scratch) and multiplied by one fp16 GEMM with fp32 accumulation.

@@ -752,12 +752,12 @@ def test_grouped_four_and_eight_codebooks(aq, orc, case):
 
 
 @pytest.mark.parametrize("case", [
-    # out, in, K, B, batch (aqlm_gemm from batch 256 (16-bit codes, K >= 4) or 1024: W decoded
+    # out, in, K, B, batch (aqlm_gemm from batch 512 (16-bit codes, K >= 4) or 1024: W decoded
     # once, then the dense GEMM kernel; in % 64 == 0 stages k-tiles straight into LDS, other
     # input sizes through registers with the last k-tile's chunks past the input zeroed)
     (300, 4096, 2, 8, 1024), (257, 1024, 1, 16, 600), (96, 512, 4, 8, 513), (1000, 2048, 2, 8, 1100),
-    (64, 256, 8, 8, 300), (130, 512, 2, 16, 256), (200, 520, 2, 8, 1030), (129, 4104, 1, 16, 300),
-    (513, 8, 1, 16, 257), (1100, 1024, 1, 16, 2050),
+    (64, 256, 8, 8, 520), (130, 512, 2, 16, 512), (200, 520, 2, 8, 1030), (129, 4104, 1, 16, 530),
+    (513, 8, 1, 16, 515), (1100, 1024, 1, 16, 2050),
 ], ids=lambda c: "x".join(map(str, c)))
 def test_prefill(aq, orc, case):
     out, in_, K, B, batch = case
@@ -777,7 +777,7 @@ def test_prefill_forced_small_batch(aq, orc):
         codes, cb, x = _dev(p)
         yref = orc.gemv(p["codes"], p["codebooks"], p["x"], 2, 8)
         check_y(aq.gemv_variant("prefill", codes, cb, x), yref, f"prefill forced b{batch}")
-    ps = _group((300, 17, 64), 1024, 1, 16, 512, 2800)
+    ps = _group((300, 17, 64), 1024, 1, 16, 520, 2800)
     dev = [_dev(p) for p in ps]
     ys = aq.gemm_grouped([d[0] for d in dev], [d[1] for d in dev], dev[0][2])
     for m, (y, p) in enumerate(zip(ys, ps)):
