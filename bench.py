@@ -146,9 +146,70 @@ def summarize_trace(trace_dir):
         if main_d:
             out.append(f"| trace | {name} | {variant} | {source_sha(variant)} | "
                        f"{statistics.median(main_d):.2f} | {statistics.median(call_d):.2f} |")
-    print("| key | product | variant | source | main kernel us (median) | call us (median) |")
-    print("|---|---|---|---|---|---|")
-    print("\n".join(out))
+    if out:
+        print("| key | product | variant | source | main kernel us (median) | call us (median) |")
+        print("|---|---|---|---|---|---|")
+        print("\n".join(out))
+        print()
+    print("| kernel | grid (threads) | workgroup | LDS B | VGPR | AGPR | calls | avg us | median us | min us | max us |")
+    print("|---|---|---|---|---|---|---|---|---|---|---|")
+    groups = {}
+    for r in rows:
+        name = short_kernel_name(r["Kernel_Name"])
+        if name is None:
+            continue
+        key = (name, int(r["Grid_Size_X"]), int(r["Workgroup_Size_X"]), int(r["LDS_Block_Size"]),
+               int(r["VGPR_Count"]), int(r["Accum_VGPR_Count"]))
+        groups.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    for key, d in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+        print("| " + " | ".join(str(v) for v in key) + f" | {len(d)} | {statistics.fmean(d):.2f} | "
+              f"{statistics.median(d):.2f} | {min(d):.2f} | {max(d):.2f} |")
+
+
+def short_kernel_name(name):
+    """This library's kernels (and the runtime's buffer copy) without namespaces or
+    parameter lists; None for anything else (torch's own kernels)."""
+    if "aqlm::" not in name and "__amd_rocclr_copyBuffer" not in name:
+        return None
+    n = re.sub(r"^void\s+", "", name)
+    n = n.replace("aqlm::", "").replace("(anonymous namespace)::", "")
+    depth, cut = 0, len(n)
+    for i, ch in enumerate(n):              # drop the parameter list: the first '(' outside <>
+        if ch == "<":
+            depth += 1
+        elif ch == ">":
+            depth -= 1
+        elif ch == "(" and depth == 0:
+            cut = i
+            break
+    return n[:cut].strip()
+
+
+def summarize_pmc(pmc_dir):
+    """Per kernel and grid: the median over its dispatches of each counter of a rocprofv3
+    --pmc run (counter_collection.csv), as a markdown table."""
+    import csv
+    import glob
+    import statistics
+    files = glob.glob(os.path.join(pmc_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        sys.exit(f"no counter_collection.csv under {pmc_dir}")
+    vals, counters = {}, []
+    for f in files:
+        for r in csv.DictReader(open(f)):
+            name = short_kernel_name(r["Kernel_Name"])
+            if name is None:
+                continue
+            c = r["Counter_Name"]
+            if c not in counters:
+                counters.append(c)
+            vals.setdefault((name, int(r["Grid_Size"])), {}).setdefault(c, []).append(float(r["Counter_Value"]))
+    print("| kernel | grid (threads) | dispatches | " + " | ".join(counters) + " |")
+    print("|---|---|---|" + "---|" * len(counters))
+    for (name, grid), cs in vals.items():
+        n = max(len(v) for v in cs.values())
+        cells = [f"{statistics.median(cs[c]):.6g}" if c in cs else "" for c in counters]
+        print(f"| {name} | {grid} | {n} | " + " | ".join(cells) + " |")
 
 
 def build_inputs(torch, synth, aq, copies, workload=WORKLOAD, batch=1, config_ids=CONFIG_IDS):
@@ -308,11 +369,16 @@ def main():
                     help="--workload layer7b: q|k|v and gate|up as one grouped call each "
                          "(members share the input); the separate calls are timed beside")
     ap.add_argument("--summarize-trace", metavar="DIR",
-                    help="print the kernel-trace rows for profiles/ from a rocprofv3 "
-                         "--kernel-trace run of the headline benchmark, and exit")
+                    help="print the kernel-trace tables for profiles/ from a rocprofv3 "
+                         "--kernel-trace run (per-kernel durations; per-product rows for the "
+                         "headline benchmark), and exit")
+    ap.add_argument("--summarize-pmc", metavar="DIR",
+                    help="print per-kernel counter medians from a rocprofv3 --pmc run, and exit")
     args = ap.parse_args()
     if args.summarize_trace:
         return summarize_trace(args.summarize_trace)
+    if args.summarize_pmc:
+        return summarize_pmc(args.summarize_pmc)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
