@@ -37,6 +37,7 @@
 // load), its B fragments the matching activations straight from global memory
 // (L2-resident), and the 16 partial tiles are added in LDS, in wave order, at
 // the end: no partial sums leave the workgroup.
+#include <algorithm>
 #include <type_traits>
 
 #include "device_common.hpp"
@@ -703,6 +704,353 @@ bool kw_fits(const Problem &p) {
     return maxu <= lim;
 }
 
+// ------------------------------------ batch > 64, 8-bit codes, K <= 2, in % 64 == 0
+//
+// The same product with every global load moved to the load units' LDS path.  A
+// workgroup of NW waves owns 32*NW rows x 32*TN tokens; wave w owns rows 32w .. 32w+31
+// and all the tokens, so each of its weight fragments is decoded once (lane l: row
+// l % 32, one group of 8 inputs) and used for TN MFMAs.  Per k-tile of 64 inputs
+// (8 groups):
+// * the activations (TN*32 rows of 128 bytes, chunks permuted by the row's place in
+//   the bank period) and the codes (32*NW rows of 8*K bytes) arrive by
+//   global_load_lds_dwordx4 / global_load_lds_dword in rings three k-tiles deep,
+//   issued two (activations) and three (codes) k-tiles ahead;
+// * the codebook gathers of k-tile kt+1 (from the LDS-resident codebooks) are issued
+//   between the MFMAs of k-tile kt, two per k-step, and folded after them;
+// * one barrier per k-tile; no register holds staged data.
+// Lane l of a wave takes groups 4(l/32) .. 4(l/32)+3 of its row in the four k-steps
+// of a k-tile (one 8-byte code read), and the activation fragment of the same group,
+// so both MFMA operands hold the same 8 inputs in a lane.
+//
+// LDS bounds it: LDS serves 128 bytes per clock, so a 64-lane 16-byte read takes 8
+// cycles free of bank conflicts and ~13 with random 16-byte entries (the gathers).  Per
+// k-tile and CU (NW = 8, TN = 4) the activation fragments take ~1024 cycles and the
+// gathers ~850, against 1024 cycles of MFMAs; measured on MI355X a k-tile takes ~0.85
+// us (~2040 cycles) in a workgroup with the CU to itself.  Two alternatives measured
+// slower: 64-row wave tiles at one wave per SIMD (each activation fragment used twice,
+// but nothing hides the latency: ~1.1 us per k-tile), and 8 copies of the codebooks
+// spread over the bank period (9.8 instead of 13.2 cycles per gather in isolation,
+// no gain in the kernel).
+constexpr int kDqXcds = 8;
+
+template <int NW, int TN, int K>
+struct DqTile {
+    static constexpr int THREADS = NW * kWave;
+    static constexpr int BM = 32 * NW;           // rows per workgroup
+    static constexpr int BN = 32 * TN;           // tokens per workgroup
+    static constexpr int XB = BN * 128;          // activation stage: BN rows of 64 fp16
+    static constexpr int CR = 8 * K;             // code bytes per row and k-tile
+    static constexpr int CS = BM * CR;           // code stage
+    static constexpr int XR = BN / (8 * NW);     // activation rounds per wave (8 rows of 128 B)
+    static constexpr int CRW = CS / (256 * NW);  // code rounds per wave (64 dwords)
+    static constexpr int LOADS = XR + CRW;       // loads per wave and k-tile
+    static_assert(XR >= 1 && BN % (8 * NW) == 0, "whole activation rounds per wave");
+    static_assert(CRW >= 1 && CS % (256 * NW) == 0, "whole code rounds per wave");
+    static_assert(NW % 2 == 0, "8*NW rows per activation round, a multiple of 16");
+    // chunk c of staged activation row r
+    static __device__ __forceinline__ uint32_t off(int r, int c) {
+        return uint32_t(r) * 128u + (uint32_t(c ^ ((r >> 1) & 7)) << 4);
+    }
+};
+
+template <int K, int NW, int TN, int NS>
+__global__ void __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(2, 2)))
+mfma_dq_kernel(const uint16_t *__restrict__ x, float *__restrict__ partial, int in, int batch,
+               int kt_per_split, int tiles_m, int tiles_n, int ntiles, int per_xcd,
+               const Segs segs) {
+    typedef DqTile<NW, TN, K> T;
+    __shared__ __attribute__((aligned(1024))) char xs0[T::XB];
+    __shared__ __attribute__((aligned(1024))) char xs1[T::XB];
+    __shared__ __attribute__((aligned(1024))) char xs2[T::XB];
+    __shared__ __attribute__((aligned(256))) char cs0[T::CS];
+    __shared__ __attribute__((aligned(256))) char cs1[T::CS];
+    __shared__ __attribute__((aligned(256))) char cs2[T::CS];
+    __shared__ uint4 cbs[K * 256];
+
+    // workgroup b runs on XCD b % 8; each XCD takes a contiguous run of tiles, row
+    // tiles fastest, so the workgroups of one XCD share a split's activations in its L2
+    const int b = blockIdx.x;
+    const int L = (b % kDqXcds) * per_xcd + b / kDqXcds;
+    if (L >= ntiles) return;                     // the whole workgroup: no barrier skipped
+    const int per_split = tiles_m * tiles_n;
+    const int split = L / per_split;
+    const int rem = L - split * per_split;
+    const int tn = rem / tiles_m, tm = rem - tn * tiles_m;
+
+    // this row tile's matrix (row tiles of each matrix numbered consecutively, segs.aux0)
+    const int mi = seg_of<NS>(segs.n, segs.aux0, tm);
+    const int out = pick(segs.row0, mi + 1) - pick(segs.row0, mi);
+    const int rows_all = seg_total<NS>(segs.n, segs.row0);
+    const uint8_t *__restrict__ codes = static_cast<const uint8_t *>(pick(segs.codes, mi));
+    const uint4 *__restrict__ cbg = static_cast<const uint4 *>(pick(segs.cb, mi));
+    uint16_t *__restrict__ y = static_cast<uint16_t *>(pick(segs.y, mi));
+    const int row0 = (tm - pick(segs.aux0, mi)) * T::BM;
+    const int tok0 = tn * T::BN;
+    const int G = in / kGroup;
+    const int kt0 = split * kt_per_split;
+    const int nk = min(kt_per_split, G / 8 - kt0);   // >= 1
+
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int m = lane & 31, h = lane >> 5;
+
+    // Codebooks: K*256 vectors, loaded first (clamped duplicates past the end), stored
+    // once the rings are in flight.
+    constexpr int CBE = K * 256;
+    constexpr int CBPT = (CBE + T::THREADS - 1) / T::THREADS;
+    uint4 cbv[CBPT];
+#pragma unroll
+    for (int i = 0; i < CBPT; ++i) cbv[i] = cbg[min(int(threadIdx.x) + i * T::THREADS, CBE - 1)];
+
+    // Activation round i of wave w fills staged rows 8(w + NW*i) .. +7 (1 KiB); lane l
+    // fills row 8(w + NW*i) + l/8, slot l%8, i.e. logical chunk (l%8) ^ ((row >> 1) & 7),
+    // the same chunk in every round (8*NW is a multiple of 16).  Rows past the batch are
+    // clamped duplicates whose outputs are never stored.
+    const int xrow = 8 * wave + (lane >> 3);
+    const int xcl = (lane & 7) ^ ((xrow >> 1) & 7);
+    const uint16_t *xsrc[T::XR];
+#pragma unroll
+    for (int i = 0; i < T::XR; ++i)
+        xsrc[i] = x + size_t(min(tok0 + xrow + 8 * NW * i, batch - 1)) * size_t(in) +
+                  size_t(kt0) * 64 + 8 * xcl;
+    // Code round j of wave w fills code-stage bytes 256 (w*CRW + j) .. +255: lane l the
+    // dword q = 64 (w*CRW + j) + l, byte 4q % CR of row 4q / CR.  Rows past the matrix are
+    // clamped duplicates.
+    const uint8_t *csrc[T::CRW];
+#pragma unroll
+    for (int j = 0; j < T::CRW; ++j) {
+        const int q = 64 * (wave * T::CRW + j) + lane;
+        const int r = 4 * q / T::CR;
+        csrc[j] = codes + size_t(min(row0 + r, out - 1)) * size_t(G) * K + size_t(kt0) * T::CR +
+                  (4 * q) % T::CR;
+    }
+    auto lds_addr = [&](char *p, uint32_t wave_off) {
+        return __builtin_amdgcn_readfirstlane(
+            uint32_t(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char *)p)) + wave_off);
+    };
+    const uint32_t xa0 = lds_addr(xs0, 1024u * wave), xa1 = lds_addr(xs1, 1024u * wave),
+                   xa2 = lds_addr(xs2, 1024u * wave);
+    const uint32_t ca0 = lds_addr(cs0, 256u * T::CRW * wave), ca1 = lds_addr(cs1, 256u * T::CRW * wave),
+                   ca2 = lds_addr(cs2, 256u * T::CRW * wave);
+    // The loads are asm so that the compiler does not track them (its wait insertion
+    // would make LDS reads wait for every load into LDS in flight); the waits they need
+    // are the explicit vmcnt ones.  No output register; m0 holds the wave's LDS
+    // destination, and no other code of this kernel uses m0.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+    auto dma_x = [&](uint32_t stage, int kt) {
+#pragma unroll
+        for (int i = 0; i < T::XR; ++i) {
+            const uint16_t *g = xsrc[i] + size_t(kt) * 64;
+            asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+                         :
+                         : "v"(g), "s"(stage + uint32_t(1024 * NW * i))
+                         : "memory", "m0");
+        }
+    };
+    auto dma_c = [&](uint32_t stage, int kt) {
+#pragma unroll
+        for (int j = 0; j < T::CRW; ++j) {
+            const uint8_t *g = csrc[j] + size_t(kt) * T::CR;
+            asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off"
+                         :
+                         : "v"(g), "s"(stage + uint32_t(256 * j))
+                         : "memory", "m0");
+        }
+    };
+#pragma clang diagnostic pop
+    // s_waitcnt vmcnt(N) (expcnt and lgkmcnt not waited for)
+    auto wait_vm = [](auto n) {
+        constexpr int N = decltype(n)::value;
+        __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+    };
+
+    // this lane's codes of a k-tile: groups 4h .. 4h+3 of row 32w + m
+    const int coff = (32 * wave + m) * T::CR + 4 * K * h;
+    auto read_codes = [&](const char *cst) -> u32x2 {
+        if constexpr (K == 2) return *reinterpret_cast<const u32x2 *>(cst + coff);
+        else return u32x2{*reinterpret_cast<const uint32_t *>(cst + coff), 0u};
+    };
+    // codebook vectors of group 4h + s
+    auto gather = [&](const u32x2 &cw, int s, uint4 &v0, uint4 &v1) {
+        if constexpr (K == 2) {
+            const uint32_t w = s < 2 ? cw.x : cw.y;
+            v0 = cbs[(w >> (16 * (s & 1))) & 0xFFu];
+            v1 = cbs[256 + ((w >> (16 * (s & 1) + 8)) & 0xFFu)];
+        } else {
+            v0 = cbs[(cw.x >> (8 * s)) & 0xFFu];
+        }
+    };
+    // K = 2: the fp16 sum rounds the exact sum once, the value aqlm_dequantize writes
+    auto fold = [&](const uint4 &v0, const uint4 &v1) -> half8 {
+        if constexpr (K == 2) return __builtin_bit_cast(half8, v0) + __builtin_bit_cast(half8, v1);
+        else return __builtin_bit_cast(half8, v0);
+    };
+
+    float16v acc[TN];
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[j] = float16v{};
+
+    // Prologue: codes of k-tiles 0..2 and activations of 0..1 in flight; the codebook
+    // store waits for everything; then k-tile 0 is decoded, and a barrier frees code
+    // stage 0 for k-tile 3.  Past the last k-tile the loads are clamped duplicates into
+    // stages nobody reads (no conditional load).
+    dma_c(ca0, 0);
+    dma_x(xa0, 0);
+    dma_c(ca1, min(1, nk - 1));
+    dma_x(xa1, min(1, nk - 1));
+    dma_c(ca2, min(2, nk - 1));
+#pragma unroll
+    for (int i = 0; i < CBPT; ++i) cbs[min(int(threadIdx.x) + i * T::THREADS, CBE - 1)] = cbv[i];
+    wait_vm(std::integral_constant<int, 0>{});
+    __syncthreads();
+    half8 acur[4];
+    {
+        const u32x2 cw = read_codes(cs0);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            uint4 v0, v1{};
+            gather(cw, s, v0, v1);
+            acur[s] = fold(v0, v1);
+        }
+    }
+    __syncthreads();
+
+    // k-tile kt: activations in stage kt % 3, codes of kt+1 in code stage (kt+1) % 3;
+    // the step refills activation stage (kt+2) % 3 and code stage kt % 3.
+    int kt = 0;
+    auto step = [&](const char *xcur, const char *cnext, uint32_t xdma, uint32_t cdma) {
+        dma_x(xdma, min(kt + 2, nk - 1));
+        dma_c(cdma, min(kt + 3, nk - 1));
+        auto frags = [&](int s, half8 (&xb)[TN]) {
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+                xb[j] = *reinterpret_cast<const half8 *>(xcur + T::off(32 * j + m, 4 * h + s));
+        };
+        half8 xb[2][TN];
+        uint4 g0[4], g1[4];
+        frags(0, xb[0]);
+        const u32x2 cw = read_codes(cnext);
+        // Order pinned per k-step: the next step's fragment reads, then this step's two
+        // gathers, then its MFMAs, so that an MFMA waits for its own fragments only.
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            if (s + 1 < 4) frags(s + 1, xb[(s + 1) & 1]);
+            gather(cw, s, g0[s], g1[s]);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+                acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(xb[s & 1][j], acur[s], acc[j], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int s = 0; s < 4; ++s) acur[s] = fold(g0[s], g1[s]);
+        // this wave's loads of k-tile kt+1 (activations) and kt+2 (codes) have landed;
+        // its LDS reads of this k-tile were consumed above
+        wait_vm(std::integral_constant<int, T::LOADS>{});
+        __builtin_amdgcn_s_barrier();
+        return ++kt < nk;
+    };
+    while (step(xs0, cs1, xa2, ca0) && step(xs1, cs2, xa0, ca1) && step(xs2, cs0, xa1, ca2)) {
+    }
+    wait_vm(std::integral_constant<int, 0>{});   // no load may land after the workgroup ends
+
+    // result register r of lane l: token 32j + 8(r/4) + 4h + r%4, row 32w + m; 32 lanes
+    // store 32 consecutive rows of one token
+    const int lrow = row0 + 32 * wave + m;
+    const size_t prow = size_t(pick(segs.row0, mi)) + lrow;
+    const bool full = row0 + T::BM <= out && tok0 + T::BN <= batch;
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int tok = tok0 + 32 * j + 8 * (r >> 2) + 4 * h + (r & 3);
+            if (full || (lrow < out && tok < batch)) {
+                if (partial)
+                    partial[(size_t(split) * batch + tok) * rows_all + prow] = acc[j][r];
+                else
+                    y[size_t(tok) * out + lrow] = f2h_bits(acc[j][r]);
+            }
+        }
+    }
+}
+
+struct DqCfg {
+    int tn, ksplit, kt_per_split, tiles_m, tiles_n, ntiles, per_xcd;
+};
+
+constexpr int kDqWaves = 8;
+
+// From batch 65: at 33..64 tokens the tiled kernel above measured faster on the 7B layer.
+bool dq_fits(const Problem &p) {
+    return p.B == 8 && (p.K == 1 || p.K == 2) && p.batch > 64 && p.in % 64 == 0;
+}
+
+// split = false: the whole input axis in one workgroup per tile (no workspace needed).
+DqCfg dq_cfg(const Problem &p, Segs *segs = nullptr, bool split = true) {
+    DqCfg c{};
+    // 64-token tiles up to batch 128 (more tiles, fewer input-axis splits: measured faster
+    // on the 7B shapes at batch 128), 128-token tiles above
+    c.tn = p.batch > 128 ? 4 : 2;
+    const int bm = 32 * kDqWaves, bn = 32 * c.tn;
+    int tm = 0;
+    for (int m = 0; m < p.segs.n; ++m) {
+        if (segs) segs->aux0[m] = tm;
+        tm += (p.segs.row0[m + 1] - p.segs.row0[m] + bm - 1) / bm;
+    }
+    if (segs) segs->aux0[p.segs.n] = tm;
+    c.tiles_m = tm;
+    c.tiles_n = (p.batch + bn - 1) / bn;
+    const int64_t tiles = int64_t(c.tiles_m) * c.tiles_n;
+    const int64_t nkt = p.in / 64;
+    // One workgroup per CU (a workgroup of 8 waves fills its registers).  Each split adds
+    // a batch x out fp32 partial sum written and read back, so splits keep at least 16
+    // k-tiles unless that leaves fewer than 64 workgroups (then at least 4).  Measured on
+    // MI355X, 7B shapes: 4096 x 4096 at batch 256 takes 32.9 us in 4 splits against 34.6
+    // in 8, 4096 x 11008 41.7 in 8 against 47.5 in 4.
+    const int64_t fill = 256 / tiles;
+    int64_t ks = std::min(fill, nkt / 16);
+    if (tiles * std::max<int64_t>(ks, 1) < 64) ks = std::min(fill, nkt / 4);
+    if (ks < 1 || !split) ks = 1;
+    const int64_t kps = (nkt + ks - 1) / ks;
+    c.kt_per_split = int(kps);
+    c.ksplit = int((nkt + kps - 1) / kps);
+    const int64_t n = tiles * c.ksplit;
+    c.ntiles = int(n);
+    c.per_xcd = int((n + kDqXcds - 1) / kDqXcds);
+    return c;
+}
+
+template <int K, int TN>
+hipError_t launch_dq_t(const Problem &p, const DqCfg &c, const Segs &segs, float *partial) {
+    const dim3 g(c.per_xcd * kDqXcds), b(kDqWaves * kWave);
+    const uint16_t *x = static_cast<const uint16_t *>(p.x);
+    if (segs.n == 1)
+        hipLaunchKernelGGL((mfma_dq_kernel<K, kDqWaves, TN, 1>), g, b, 0, p.stream, x, partial,
+                           int(p.in), p.batch, c.kt_per_split, c.tiles_m, c.tiles_n, c.ntiles,
+                           c.per_xcd, segs);
+    else
+        hipLaunchKernelGGL((mfma_dq_kernel<K, kDqWaves, TN, kMaxSegs>), g, b, 0, p.stream, x,
+                           partial, int(p.in), p.batch, c.kt_per_split, c.tiles_m, c.tiles_n,
+                           c.ntiles, c.per_xcd, segs);
+    return hipGetLastError();
+}
+
+template <int K>
+hipError_t launch_dq_k(const Problem &p, const DqCfg &c, const Segs &segs, float *partial) {
+    if (c.tn == 4) return launch_dq_t<K, 4>(p, c, segs, partial);
+    return launch_dq_t<K, 2>(p, c, segs, partial);
+}
+
+hipError_t launch_dq(const Problem &p, void *workspace) {
+    Segs segs = p.segs;
+    const DqCfg c = dq_cfg(p, &segs, workspace != nullptr);
+    float *partial = c.ksplit > 1 ? static_cast<float *>(workspace) : nullptr;
+    const hipError_t e = p.K == 1 ? launch_dq_k<1>(p, c, segs, partial) : launch_dq_k<2>(p, c, segs, partial);
+    if (e != hipSuccess || c.ksplit == 1) return e;
+    return launch_partial_sum_segs(partial, segs, p.batch, c.ksplit, p.stream);
+}
+
 }  // namespace
 
 bool mfma_supported(const Problem &p) {
@@ -723,6 +1071,10 @@ bool mfma_supported(const Problem &p) {
 
 size_t mfma_workspace_bytes(const Problem &p) {
     if (kw_fits(p)) return 0;
+    if (dq_fits(p)) {
+        const DqCfg c = dq_cfg(p);
+        return c.ksplit > 1 ? size_t(c.ksplit) * size_t(p.batch) * size_t(p.out) * sizeof(float) : 0;
+    }
     const MfmaCfg c = mfma_cfg(p);
     return c.ksplit > 1 ? size_t(c.ksplit) * size_t(p.batch) * size_t(p.out) * sizeof(float) : 0;
 }
@@ -735,6 +1087,7 @@ hipError_t launch_mfma(const Problem &p, void *workspace) {
                  : p.K == 4 ? launch_kw<4, 8>(p) : launch_kw<8, 8>(p);
         return p.K == 1 ? launch_kw<1, 16>(p) : launch_kw<2, 16>(p);
     }
+    if (dq_fits(p)) return launch_dq(p, workspace);
     Segs segs = p.segs;
     const MfmaCfg c = mfma_cfg(p, &segs, workspace != nullptr);
     float *partial = c.ksplit > 1 ? static_cast<float *>(workspace) : nullptr;

@@ -373,6 +373,42 @@ def test_graph_replay_after_large_eager_call(aq, orc):
         check_y(e, orc.gemv(p["codes"], p["codebooks"], p["x"], p["K"], p["B"]), "decode eager")
 
 
+DQ = [
+    # out, in, K, B, batch: the matrix-core kernel with DMA-staged operands (8-bit codes,
+    # K <= 2, batch > 64, in a multiple of 64; 64-token tiles up to batch 128)
+    (300, 4096, 2, 8, 128),      # ragged row tile, input axis split
+    (4096, 4096, 2, 8, 128),     # 16 row tiles x 2 token tiles x 4 splits of 16 k-tiles
+    (257, 1024, 1, 8, 70),       # one codebook; the second token tile holds 6 tokens
+    (512, 640, 2, 8, 65),        # 10 k-tiles; a second token tile of one token
+    (1000, 2048, 2, 8, 200),     # 128-token tiles, the second ragged
+    (64, 64, 2, 8, 100),         # a single k-tile: every prologue load clamped
+    (520, 1536, 1, 8, 129),
+    (96, 192, 2, 8, 1000),       # 8 token tiles of a 3-k-tile product
+]
+
+
+@pytest.mark.parametrize("case", DQ, ids=lambda c: "x".join(map(str, c)))
+def test_mfma_dma_staged(aq, orc, case):
+    """Batched matrix cores on 8-bit codes: with the workspace (input axis split, partial
+    sums added in split order) and without it (one split), both against the oracle on
+    sampled rows, and the two outputs within the bar of each other."""
+    import torch
+    out, in_, K, B, batch = case
+    p = synth.make_problem(out, in_, K, B, batch=batch, sigma_cb=0.02, config=4100 + out + batch)
+    codes, cb, x = _dev(p)
+    assert aq.selected_variant(codes, cb, x, gemm=True) in ("mfma", "prefill")
+    rows = _sampled_rows(out, seed=out + batch)
+    yref = orc.gemv_rows(p["codes"], p["codebooks"], p["x"], K, B, rows)
+    y1 = aq.gemv_variant("mfma", codes, cb, x)
+    y0 = aq.gemv_variant("mfma", codes, cb, x, workspace=0)
+    torch.cuda.synchronize()
+    for y, what in ((y1, "split"), (y0, "unsplit")):
+        yg = y.float().cpu().numpy()
+        assert np.all(np.isfinite(yg)), what
+        e = rel_err(yg[:, rows], yref)
+        assert np.all(e <= TOL), f"{what} {case}: {e.max():.3e}"
+
+
 @pytest.mark.parametrize("case", [
     # out, in, K, B, batch, variant expected without a workspace
     (700, 2048, 2, 8, 1, "lds"), (700, 2048, 1, 16, 1, "l2"), (300, 8192, 2, 8, 128, "mfma"),
@@ -624,7 +660,9 @@ GROUPED = [
     ((300, 17), 1024, 1, 16, 16),
     ((120, 40, 64, 8), 4096, 2, 8, 32),      # four matrices, two token tiles
     ((200, 33, 100), 11008, 2, 8, 16),       # three units per wave
-    ((130, 70), 512, 2, 8, 128),             # tiled, split partial sums
+    ((130, 70), 512, 2, 8, 128),             # DMA-staged matrix cores, split partial sums
+    ((300, 257, 40), 1024, 1, 8, 70),        # the same, one codebook, three matrices
+    ((130, 70), 520, 2, 8, 128),             # tiled (in not a multiple of 64)
     ((129, 300), 2048, 1, 16, 64),
 ]
 
