@@ -33,10 +33,13 @@ constexpr int kSplitMaxBatch = 4;
 constexpr int kSplitMaxBatchGemm = 2;
 // Measured on MI355X (7B layer, seven separate calls, us, matrix cores against prefill):
 // 16-bit codes b256 417 / 542, b512 732 / 576, b1024 1190 / 741 (decoding a 1 MiB codebook
-// through L2 per token tile costs more); 8-bit codes with K <= 2: b512 429 / 540, b1024
-// 690 / 692, b2048 1387 / 1018.
+// through L2 per token tile costs more).  8-bit codes with K <= 2 on the tiled kernel
+// (inputs not a multiple of 64): b512 429 / 540, b1024 690 / 692, b2048 1387 / 1018.  On
+// the kernel with DMA-staged operands (inputs a multiple of 64) the matrix cores stay
+// ahead at every batch measured: b1024 584 / 681, b2048 912 / 1013, b4096 1795 / 1881.
 constexpr int kPrefillMinBatch16 = 512;
 constexpr int kPrefillMinBatch8 = 1024;
+constexpr int kPrefillMinBatch8Staged = 1 << 30;
 // The workspace is cut into fp32 / 16-byte-vector regions at 256-byte offsets.
 constexpr uintptr_t kWorkspaceAlign = 256;
 constexpr int64_t kUnlimited = INT64_MAX;
@@ -85,7 +88,9 @@ int env_batch(const char *name, int def) {
 int prefill_min_batch(const aqlm::Problem &p) {
     static const int b16 = env_batch("AQLM_PREFILL_MIN_BATCH", kPrefillMinBatch16);
     static const int b8 = env_batch("AQLM_PREFILL_MIN_BATCH", kPrefillMinBatch8);
-    return (p.B == 16 || p.K >= 4) ? b16 : b8;
+    static const int b8s = env_batch("AQLM_PREFILL_MIN_BATCH", kPrefillMinBatch8Staged);
+    if (p.B == 16 || p.K >= 4) return b16;
+    return p.in % 64 == 0 ? b8s : b8;
 }
 
 int mfma_min_batch(int K) {

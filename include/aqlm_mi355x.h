@@ -141,9 +141,11 @@ aqlm_status_t aqlm_gemv(const void *codes, const void *codebooks, const void *x,
  * codebooks, 3 for 16-bit codes, which take the split kernel up to batch 2;
  * AQLM_MFMA_MIN_BATCH overrides the first two) it uses the decode-to-fp16 + MFMA
  * kernels, below that it behaves as aqlm_gemv.  From prefill-size batches (512 for
- * 16-bit codes or K >= 4, 1024 otherwise; AQLM_PREFILL_MIN_BATCH overrides) W is
- * instead decoded once into the workspace as dense fp16 (out*in*2 bytes plus the
- * GEMM's scratch) and multiplied by one fp16 GEMM with fp32 accumulation.
+ * 16-bit codes or K >= 4, 1024 for 8-bit codes with K <= 2 when in_features is not a
+ * multiple of 64; AQLM_PREFILL_MIN_BATCH overrides) W is instead decoded once into the
+ * workspace as dense fp16 (out*in*2 bytes) and multiplied by one fp16 GEMM with fp32
+ * accumulation.  8-bit codes with K <= 2 and in_features a multiple of 64 stay on the
+ * matrix-core decode kernels at every batch.
  */
 aqlm_status_t aqlm_gemm(const void *codes, const void *codebooks, const void *x, void *y,
                         int64_t out_features, int64_t in_features, int K, int B, int batch,

@@ -186,8 +186,11 @@ def test_variant_choice_host_logic(lib):
     assert sel(1, 4096, 4096, 1, 16, 128) == "mfma"
     assert sel(1, 4096, 4096, 1, 16, 256) == "mfma"        # prefill from 512 (16-bit codes)
     assert sel(1, 4096, 4096, 1, 16, 512) == "prefill"
-    assert sel(1, 4096, 4096, 2, 8, 512) == "mfma"         # and from 1024 for 2x8
-    assert sel(1, 4096, 4096, 2, 8, 1024) == "prefill"
+    assert sel(1, 4096, 4096, 2, 8, 1024) == "mfma"        # 2x8, inputs a multiple of 64:
+    assert sel(1, 4096, 4096, 2, 8, 8192) == "mfma"        # the matrix cores at any batch
+    assert sel(1, 4096, 4128, 2, 8, 512) == "mfma"         # other 2x8: prefill from 1024
+    assert sel(1, 4096, 4128, 2, 8, 1024) == "prefill"
+    assert sel(1, 4096, 4096, 4, 8, 512) == "prefill"      # K >= 4: from 512
     assert sel(1, 4096, 4096, 2, 8, 8) == "mfma"
     assert sel(1, 4096, 4096, 2, 8, 1) == "lut"
     assert sel(1, 4096, 4096, 8, 8, 2) == "lds"       # eight codebooks: matrix cores from 4

@@ -347,7 +347,7 @@ def test_graph_replay_after_large_eager_call(aq, orc):
     stream = torch.cuda.Stream()
     dec = [synth.make_problem(1000, 4096, 2, 8, batch=1, sigma_cb=0.02, config=3200),
            synth.make_problem(1000, 4096, 1, 16, batch=1, sigma_cb=0.02, config=3201)]
-    big = synth.make_problem(512, 2048, 2, 8, batch=1024, sigma_cb=0.02, config=3202)
+    big = synth.make_problem(512, 2048, 1, 16, batch=1024, sigma_cb=0.02, config=3202)
     with torch.cuda.stream(stream):
         td = [_dev(p) for p in dec]
         eager = [aq.gemv(*t).clone() for t in td]
@@ -368,7 +368,7 @@ def test_graph_replay_after_large_eager_call(aq, orc):
             for e, o in zip(eager, outs):
                 assert bool((e == o).all())
             assert bool((yb2 == yb).all())
-    check_y(yb, orc.gemv(big["codes"], big["codebooks"], big["x"], 2, 8), "prefill-size eager")
+    check_y(yb, orc.gemv(big["codes"], big["codebooks"], big["x"], 1, 16), "prefill-size eager")
     for p, e in zip(dec, eager):
         check_y(e, orc.gemv(p["codes"], p["codebooks"], p["x"], p["K"], p["B"]), "decode eager")
 
@@ -790,10 +790,11 @@ def test_grouped_four_and_eight_codebooks(aq, orc, case):
 
 
 @pytest.mark.parametrize("case", [
-    # out, in, K, B, batch (aqlm_gemm from batch 512 (16-bit codes, K >= 4) or 1024: W decoded
-    # once, then the dense GEMM kernel; in % 64 == 0 stages k-tiles straight into LDS, other
-    # input sizes through registers with the last k-tile's chunks past the input zeroed)
-    (300, 4096, 2, 8, 1024), (257, 1024, 1, 16, 600), (96, 512, 4, 8, 513), (1000, 2048, 2, 8, 1100),
+    # out, in, K, B, batch (aqlm_gemm from batch 512 (16-bit codes, K >= 4) or 1024 (2x8 with
+    # in not a multiple of 64): W decoded once, then the dense GEMM kernel; in % 64 == 0 stages
+    # k-tiles straight into LDS, other input sizes through registers with the last k-tile's
+    # chunks past the input zeroed)
+    (300, 4128, 2, 8, 1024), (257, 1024, 1, 16, 600), (96, 512, 4, 8, 513), (1000, 2080, 2, 8, 1100),
     (64, 256, 8, 8, 520), (130, 512, 2, 16, 512), (200, 520, 2, 8, 1030), (129, 4104, 1, 16, 530),
     (513, 8, 1, 16, 515), (1100, 1024, 1, 16, 2050),
 ], ids=lambda c: "x".join(map(str, c)))
@@ -826,8 +827,9 @@ def test_prefill_graph_replay(aq, orc):
     """The prefill path captured into a graph (its workspace from the graph's pool) and
     replayed with eager work between replays equals the eager result every time."""
     import torch
-    p = synth.make_problem(512, 2048, 2, 8, batch=1024, sigma_cb=0.02, config=2900)
+    p = synth.make_problem(512, 2048, 1, 16, batch=1024, sigma_cb=0.02, config=2900)
     codes, cb, x = _dev(p)
+    assert aq.selected_variant(codes, cb, x, gemm=True) == "prefill"
     stream = torch.cuda.Stream()
     with torch.cuda.stream(stream):
         eager = aq.gemm(codes, cb, x).clone()
@@ -836,7 +838,7 @@ def test_prefill_graph_replay(aq, orc):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=stream):
             aq.gemm(codes, cb, x, out=y)
-        yref = orc.gemv(p["codes"], p["codebooks"], p["x"], 2, 8)
+        yref = orc.gemv(p["codes"], p["codebooks"], p["x"], 1, 16)
         for _ in range(3):
             y.fill_(3.0)
             torch.cuda.synchronize()
