@@ -494,9 +494,13 @@ def _timed(args, torch, np, sets, copies, per_copy, call, variants, stream,
                     call(i, s % copies)
         return f
 
-    # main timed region: exactly args.steps steps (each graph replayed once untimed first)
-    full = capture_on(torch, stream, steps_fn(copies))
-    tail_n = args.steps % copies
+    # Main timed region: exactly args.steps steps, captured as one graph of up to 256 steps
+    # (a whole number of rotations when there are more steps: that graph replayed, then a
+    # graph of the remainder), so that the graph launches themselves add little to a step;
+    # each graph replayed once untimed first.
+    per_graph = args.steps if args.steps <= 256 else copies * max(1, 256 // copies)
+    full = capture_on(torch, stream, steps_fn(per_graph))
+    tail_n = args.steps % per_graph
     tail = capture_on(torch, stream, steps_fn(tail_n)) if tail_n else None
     full.replay()
     if tail is not None:
@@ -504,7 +508,7 @@ def _timed(args, torch, np, sets, copies, per_copy, call, variants, stream,
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record(stream)
-    for _ in range(args.steps // copies):
+    for _ in range(args.steps // per_graph):
         full.replay()
     if tail is not None:
         tail.replay()
