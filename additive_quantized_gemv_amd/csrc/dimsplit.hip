@@ -100,11 +100,12 @@ __device__ __forceinline__ void stage_plane(const uint16_t *__restrict__ planes,
     }
 }
 
-// ds_kernel's pair form: one codebook, batch 1 (activation pairs in registers up to 4
-// chunk positions per lane, else read from LDS) or batch 2 with one chunk position
-// (two codebooks measured slower in it: 149 against 144 us per 2x16 7B layer)
+// ds_kernel's pair form: one codebook, batch 1 (activation pairs in registers up to 7
+// chunk positions per lane, 117 VGPRs at 7, else read from LDS; measured on MI355X,
+// 1x16 8192x28672 with 7: 42.4 against 52.1 us per call) or batch 2 with one chunk
+// position (two codebooks measured slower in it: 149 against 144 us per 2x16 7B layer)
 constexpr bool ds_pair_form(int K, int nb, int nseg) { return K == 1 && (nb == 1 || nseg == 1) && nb <= 2; }
-constexpr bool ds_pair_xreg(int nb, int nseg) { return nb * nseg <= 4; }
+constexpr bool ds_pair_xreg(int nb, int nseg) { return nb * nseg <= 7; }
 
 template <int NSEG>
 struct DsShape {
