@@ -166,6 +166,70 @@ def summarize_trace(trace_dir):
               f"{statistics.median(d):.2f} | {min(d):.2f} | {max(d):.2f} |")
 
 
+def summarize_traffic(copy_fetch, copy_write, fetch_dir, write_dir):
+    """Per packed batch-1 product of the headline run: HBM bytes per launch (main kernel +
+    partial-sum kernel) from rocprofv3 FETCH_SIZE and WRITE_SIZE passes, scaled by what the
+    same counters read for the 256 MiB device copy of `--workload copy`; markdown rows, the
+    machine-readable ones in the form measured_traffic() reads."""
+    import csv
+    import glob
+    import statistics
+
+    def rows_of(d):
+        files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+        if not files:
+            sys.exit(f"no counter_collection.csv under {d}")
+        rows = []
+        for f in files:
+            rows += list(csv.DictReader(open(f)))
+        rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+        return rows
+
+    def factor(d):
+        vals = [float(r["Counter_Value"]) for r in rows_of(d) if "copyBuffer" in r["Kernel_Name"]]
+        return (256 * 2**20) / (max(vals) * 1024)
+
+    f_fetch, f_write = factor(copy_fetch), factor(copy_write)
+    fetch, write = rows_of(fetch_dir), rows_of(write_dir)
+    mains = {"lut_packed": "lut_packed_kernel", "split": "ds_kernel"}
+
+    def per_product(rows, name, out, variant):
+        main, red = [], []
+        for j, r in enumerate(rows):
+            if not re.search(r"::" + mains[variant] + r"<", r["Kernel_Name"]):
+                continue
+            if j > 0 and "pack_pairs" in rows[j - 1]["Kernel_Name"]:
+                continue                     # the canonical-layout call
+            nxt = next((q for q in rows[j + 1:j + 4] if "partial_sum" in q["Kernel_Name"]), None)
+            if nxt is None or int(nxt["Grid_Size"]) != out:
+                continue
+            main.append(float(r["Counter_Value"]))
+            red.append(float(nxt["Counter_Value"]))
+        return (statistics.median(main), statistics.median(red)) if main else (None, None)
+
+    print(f"Calibration: bytes read = FETCH_SIZE x 1024 x {f_fetch:.4f}, bytes written = WRITE_SIZE x "
+          f"1024 x {f_write:.4f} (the 256 MiB copy).")
+    print()
+    print("| product | variant | FETCH KiB (+ reduce) | WRITE KiB (+ reduce) | bytes / launch | algorithmic bytes | ratio |")
+    print("|---|---|---|---|---|---|---|")
+    machine = []
+    for name, o, i, K, B in WORKLOAD:
+        variant = "split" if B == 16 else "lut_packed"
+        fm, fr = per_product(fetch, name, o, variant)
+        wm, wr = per_product(write, name, o, variant)
+        if fm is None or wm is None:
+            continue
+        nbytes = int(round((fm + fr) * 1024 * f_fetch + (wm + wr) * 1024 * f_write))
+        alg = algorithmic_bytes(o, i, K, B, 1)
+        print(f"| {name} | {variant} | {fm:.1f} (+{fr:.1f}) | {wm:.1f} (+{wr:.1f}) | {nbytes} | {alg} | "
+              f"{nbytes / alg:.2f} |")
+        machine.append(f"| traffic | {name} | {variant} | {source_sha(variant)} | {nbytes} |")
+    print()
+    print("| key | product | variant | source | bytes |")
+    print("|---|---|---|---|---|")
+    print("\n".join(machine))
+
+
 def short_kernel_name(name):
     """This library's kernels (and the runtime's buffer copy) without namespaces or
     parameter lists; None for anything else (torch's own kernels)."""
@@ -374,11 +438,17 @@ def main():
                          "headline benchmark), and exit")
     ap.add_argument("--summarize-pmc", metavar="DIR",
                     help="print per-kernel counter medians from a rocprofv3 --pmc run, and exit")
+    ap.add_argument("--summarize-traffic", nargs=4,
+                    metavar=("COPY_FETCH", "COPY_WRITE", "FETCH", "WRITE"),
+                    help="print the HBM traffic rows for profiles/ from rocprofv3 FETCH_SIZE and "
+                         "WRITE_SIZE runs of --workload copy and of the headline benchmark, and exit")
     args = ap.parse_args()
     if args.summarize_trace:
         return summarize_trace(args.summarize_trace)
     if args.summarize_pmc:
         return summarize_pmc(args.summarize_pmc)
+    if args.summarize_traffic:
+        return summarize_traffic(*args.summarize_traffic)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
