@@ -102,18 +102,21 @@ __device__ __forceinline__ void stage_plane(const uint16_t *__restrict__ planes,
 
 // ds_kernel's pair form: one codebook, batch 1 (activation pairs in registers up to 7
 // chunk positions per lane, 117 VGPRs at 7, else read from LDS; measured on MI355X,
-// 1x16 8192x28672 with 7: 42.4 against 52.1 us per call) or batch 2 with one chunk
-// position (two codebooks measured slower in it: 149 against 144 us per 2x16 7B layer)
-constexpr bool ds_pair_form(int K, int nb, int nseg) { return K == 1 && (nb == 1 || nseg == 1) && nb <= 2; }
-constexpr bool ds_pair_xreg(int nb, int nseg) { return nb * nseg <= 7; }
+// 1x16 8192x28672 with 7: 42.4 against 52.1 us per call) or batch b with b x positions
+// <= 8, every token's pairs in registers (measured on MI355X: 1x16 28672x8192 at batch
+// 4, 82.9 against 90.7 us per call in the plane form; two codebooks measured slower in
+// the pair form: 149 against 144 us per 2x16 7B layer)
+constexpr bool ds_pair_form(int K, int nb, int nseg) { return K == 1 && (nb == 1 || nb * nseg <= 8); }
+constexpr bool ds_pair_xreg(int nb, int nseg) { return nb == 1 ? nseg <= 7 : nb * nseg <= 8; }
 
-template <int NSEG>
+// W = chunk positions x tokens whose activation pairs a lane holds (NSEG in the plane form)
+template <int W, int NSEG>
 struct DsShape {
     // rows per chunk (reduced together), and code chunks in flight per lane (a multiple
     // of NSEG).  Measured on MI355X at one chunk position (1x16 11008x4096): chunks of 4
     // rows 13.8 us per call, of 8 rows 14.9 (the last round of chunks leaves waves
     // idle longer), of 2 rows 15.1 (too few rows in flight)
-    static constexpr int RB = NSEG <= 2 ? 4 : NSEG <= 4 ? 2 : 1;
+    static constexpr int RB = W <= 2 ? 4 : W <= 4 ? 2 : 1;
     static constexpr int D = NSEG * RB;
 };
 
@@ -124,8 +127,8 @@ ds_kernel(const uint8_t *__restrict__ codes1, const uint16_t *__restrict__ plane
           int batch, int nranges, int rows_per_range, const Segs segs) {
     constexpr int P = K * 8;                 // parts
     constexpr int GPC = 8 / K;               // groups per 16-byte chunk
-    constexpr int RB = DsShape<NSEG>::RB;
-    constexpr int D = DsShape<NSEG>::D;
+    constexpr int RB = DsShape<(ds_pair_form(K, NB, NSEG) ? NB : 1) * NSEG, NSEG>::RB;
+    constexpr int D = DsShape<(ds_pair_form(K, NB, NSEG) ? NB : 1) * NSEG, NSEG>::D;
     // PAIR (one codebook; batch 1, or batch 2 with NSEG = 1; the activation pairs sit in
     // registers when they fit without spilling, XREG, else they are read from LDS):
     // part (k, q, h) = position pair q of codebook k for code half h; LDS words

@@ -499,9 +499,12 @@ PACKED = [
     (300, 4096, 1, 16, 1), (65, 520, 1, 16, 1), (1, 64, 1, 16, 1), (257, 11008, 1, 16, 1),
     (130, 2048, 1, 16, 2), (77, 1024, 1, 16, 3), (160, 8192, 1, 16, 4), (96, 512, 2, 16, 1),
     (50, 1024, 2, 16, 4), (64, 512, 1, 16, 8), (1000, 28672, 1, 16, 1),
-    # the split kernel's two forms: pairs at batch 1 up to 4 chunk positions per lane
-    # (in 16384) and at batch 2 with one; one position per workgroup past that
+    # the split kernel's two forms: pairs at batch 1 (activations in registers up to 7 chunk
+    # positions per lane, in 28672) and at batch b with b x positions <= 8 (batch 2 up to
+    # in 16384, 3..4 up to 8192); one position per workgroup past that
     (64, 16384, 1, 16, 1), (40, 20480, 1, 16, 1), (100, 11008, 1, 16, 2), (33, 2048, 2, 16, 2),
+    (70, 32768, 1, 16, 1), (100, 16384, 1, 16, 2), (129, 8192, 1, 16, 3), (200, 8192, 1, 16, 4),
+    (64, 4104, 1, 16, 4), (48, 24576, 1, 16, 2), (1, 64, 1, 16, 4),
     # 2x8: the tiled lookup-table kernel at batch 1 (ragged rows, partial slices), else unpacked
     (40, 512, 2, 8, 1), (65, 520, 2, 8, 1), (1, 64, 2, 8, 1), (300, 4096, 2, 8, 1),
     (257, 11008, 2, 8, 1), (1023, 4160, 2, 8, 1), (5000, 512, 2, 8, 1), (96, 512, 2, 8, 4),
