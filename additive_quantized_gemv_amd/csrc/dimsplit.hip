@@ -12,7 +12,8 @@
 // * Codebooks are taken pre-packed as position pairs, [K][4][65536] x 2 fp16
 //   (aqlm_pack_codebooks: a one-time layout change of the weights): word (k, q, c)
 //   holds positions 2q and 2q+1 of entry c.
-// * Batch <= 4, pair form (one codebook; batch 1, or batch 2 with in <= 4096): a
+// * Batch <= 4, pair form (one codebook; batch 1, or batch b with b x chunk positions
+//   per lane <= 8, e.g. batch 4 with in <= 8192): a
 //   workgroup owns positions (2q, 2q+1) of the codebook for one half h of the code
 //   space (32768 words = 128 KiB, followed by a zero word).  Every lane looks up
 //   every code, at byte min(4*code - h*128 KiB, 128 KiB) (unsigned): a code of the
@@ -30,7 +31,8 @@
 //   so the dispatcher puts them on the same XCD: the codes come from HBM once and
 //   from that XCD's L2 for the other planes.
 // * The waves of a workgroup take the range's rows in chunks of 4, 2 or 1 rows (fewer
-//   as the chunk positions per lane grow from 1-2 to 3-4 to 5-8) from an
+//   as the chunk positions per lane, times the tokens whose activation pairs a lane
+//   holds in the pair form, grow from 1-2 to 3-4 to 5-8) from an
 //   LDS counter (the waves the LDS serves first take more chunks).  A wave walks a
 //   chunk's 16-byte code pieces with the next chunk's in flight (a ring of 4..8
 //   loads, issued branch-free) and issues each slot's lookups one slot ahead of its
