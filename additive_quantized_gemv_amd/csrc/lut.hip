@@ -323,16 +323,29 @@ pack_codes_kernel(const uint16_t *__restrict__ codes, uint16_t *__restrict__ pac
     }
 }
 
+// packed tiles -> codes [out][G]: thread i reads tile lane i (16 bytes: the code pairs of
+// 8 rows for one group) and writes them to the 8 rows; consecutive threads hold
+// consecutive groups, so every read is contiguous and each row's writes coalesce
 __global__ void __launch_bounds__(256)
 unpack_codes_kernel(const uint16_t *__restrict__ packed, uint16_t *__restrict__ codes, int out,
                     int G, int nslices) {
-    const int64_t n = int64_t(out) * G;
     const int NQ = (out + 7) / 8;
-    for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+    const int64_t lanes = int64_t(nslices) * NQ * kWave;
+    const uint4 *__restrict__ tiles = reinterpret_cast<const uint4 *>(packed);
+    for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < lanes;
          i += int64_t(gridDim.x) * blockDim.x) {
-        const int row = int(i / G), j = int(i % G);
-        const int s = j / kSlice, jl = j % kSlice;
-        codes[i] = packed[((size_t(s) * NQ + row / 8) * kWave + jl) * 8 + row % 8];
+        const int jl = int(i % kWave);
+        const int64_t t = i / kWave;
+        const int q = int(t % NQ), s = int(t / NQ);
+        const int j = s * kSlice + jl;
+        if (j >= G) continue;                    // padding groups of the last slice
+        const uint4 v = tiles[i];
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            const int row = 8 * q + r;
+            if (row < out) codes[size_t(row) * G + j] = uint16_t(w[r >> 1] >> (16 * (r & 1)));
+        }
     }
 }
 
@@ -470,7 +483,7 @@ hipError_t launch_pack_codes_lut(const void *src, void *dst, int64_t out, int64_
                                  hipStream_t s) {
     const int G = int(in / kGroup);
     const int nslices = (G + kSlice - 1) / kSlice;
-    const int64_t work = pack ? int64_t(nslices) * ((out + 7) / 8) * kWave : out * G;
+    const int64_t work = int64_t(nslices) * ((out + 7) / 8) * kWave;   // tile lanes
     const int blocks = int((work + 255) / 256 < 4096 ? (work + 255) / 256 : 4096);
     if (pack)
         hipLaunchKernelGGL(pack_codes_kernel, dim3(blocks), dim3(256), 0, s,
