@@ -7,10 +7,12 @@
 //   it gives the streaming read rate a single kernel of that size reaches.
 // * l2_gather: random 16-byte reads from a table that stays in L2 (the 1 MiB codebook
 //   of 16-bit codes): the L2 request rate that bounds an L2-gather decode.
-// * lds_read: random LDS reads from a 128 KiB table per CU, in three patterns: 16-byte
-//   reads (a gather of codebook vectors from LDS), 4-byte reads, and 4-byte reads with
-//   half of the lanes on one shared word (the position-pair lookups of the codebook-split
-//   kernel, where codes of the other half of the code space read a zero word).
+// * lds_read: random LDS reads from a 128 KiB table per CU, in four patterns: 16-byte
+//   reads (a gather of codebook vectors from LDS), 4-byte reads, 4-byte reads with half
+//   of the lanes on one shared word (the position-pair lookups of the codebook-split
+//   kernel, where codes of the other half of the code space read a zero word), and
+//   16-byte reads with one lane in eight active (a workgroup holding one eighth of the
+//   code space as whole vectors, looking up only the codes that fall in it).
 //
 // Every kernel folds what it read into one word per thread, stored to `sink`, so that
 // no load is removed; indices come from a counter-based integer hash.
@@ -70,22 +72,27 @@ __global__ void __launch_bounds__(256) l2_gather_kernel(const uint4 *__restrict_
 constexpr int kLdsBytes = 128 * 1024;
 
 // MODE 0: 16-byte random reads; 1: 4-byte random reads; 2: 4-byte reads, odd lanes on
-// one shared word.  1024 threads per workgroup (16 waves), one workgroup per CU.  Each
-// thread draws 8 random byte addresses once; iteration i reads them XORed with a
-// wave-uniform offset (one VALU operation per read, so the LDS, not the index
-// arithmetic, sets the rate; odd lanes in mode 2 keep the shared word).
+// one shared word; 3: 16-byte random reads issued with one lane in eight active (the
+// active lanes drawn at random once per read slot, the others masked off).  1024
+// threads per workgroup (16 waves), one workgroup per CU.  Each thread draws 8 random
+// byte addresses once; iteration i reads them XORed with a wave-uniform offset (one
+// VALU operation per read, so the LDS, not the index arithmetic, sets the rate; odd
+// lanes in mode 2 keep the shared word).
 template <int MODE>
 __global__ void __launch_bounds__(1024) lds_read_kernel(int iters, uint32_t *__restrict__ sink) {
     __shared__ __attribute__((aligned(16))) uint32_t tab[kLdsBytes / 4];
     for (int i = threadIdx.x; i < kLdsBytes / 4; i += blockDim.x) tab[i] = mix(uint32_t(i));
     __syncthreads();
     const uint32_t t = threadIdx.x;
-    constexpr uint32_t align = MODE == 0 ? 16u : 4u;
+    constexpr uint32_t align = (MODE == 0 || MODE == 3) ? 16u : 4u;
     uint32_t addr[8];
+    bool act[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-        addr[j] = (mix(t * 0x9e3779b9u + uint32_t(j)) % uint32_t(kLdsBytes)) & ~(align - 1);
+        const uint32_t r = mix(t * 0x9e3779b9u + uint32_t(j));
+        addr[j] = (r % uint32_t(kLdsBytes)) & ~(align - 1);
         if (MODE == 2 && (t & 1)) addr[j] = kLdsBytes - 4;
+        act[j] = MODE != 3 || (r >> 29) == 0;
     }
     const uint32_t keep = (MODE == 2 && (t & 1)) ? 0u : ~0u;
     const char *base = reinterpret_cast<const char *>(tab);
@@ -96,6 +103,15 @@ __global__ void __launch_bounds__(1024) lds_read_kernel(int iters, uint32_t *__r
             uint4 v[8];
 #pragma unroll
             for (int j = 0; j < 8; ++j) v[j] = *reinterpret_cast<const uint4 *>(base + (addr[j] ^ off));
+#pragma unroll
+            for (int j = 0; j < 8; ++j) acc ^= v[j].x ^ v[j].y ^ v[j].z ^ v[j].w;
+        } else if constexpr (MODE == 3) {
+            uint4 v[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                v[j] = make_uint4(0u, 0u, 0u, 0u);
+                if (act[j]) v[j] = *reinterpret_cast<const uint4 *>(base + (addr[j] ^ off));
+            }
 #pragma unroll
             for (int j = 0; j < 8; ++j) acc ^= v[j].x ^ v[j].y ^ v[j].z ^ v[j].w;
         } else {
@@ -133,7 +149,7 @@ int ceil_l2_gather(const void *table, int64_t table_bytes, int blocks, int per_t
     return int(hipGetLastError());
 }
 
-// mode 0/1/2 as lds_read_kernel; sink holds blocks * 1024 words.
+// mode 0..3 as lds_read_kernel; sink holds blocks * 1024 words.
 int ceil_lds_read(int mode, int blocks, int iters, void *sink, void *stream) {
     if (blocks < 1 || iters < 8 || iters % 8) return int(hipErrorInvalidValue);
     const hipStream_t s = static_cast<hipStream_t>(stream);
@@ -141,6 +157,7 @@ int ceil_lds_read(int mode, int blocks, int iters, void *sink, void *stream) {
     if (mode == 0) hipLaunchKernelGGL(lds_read_kernel<0>, dim3(blocks), dim3(1024), 0, s, iters, k);
     else if (mode == 1) hipLaunchKernelGGL(lds_read_kernel<1>, dim3(blocks), dim3(1024), 0, s, iters, k);
     else if (mode == 2) hipLaunchKernelGGL(lds_read_kernel<2>, dim3(blocks), dim3(1024), 0, s, iters, k);
+    else if (mode == 3) hipLaunchKernelGGL(lds_read_kernel<3>, dim3(blocks), dim3(1024), 0, s, iters, k);
     else return int(hipErrorInvalidValue);
     return int(hipGetLastError());
 }

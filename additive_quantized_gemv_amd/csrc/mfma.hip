@@ -722,15 +722,18 @@ bool kw_fits(const Problem &p) {
 // of a k-tile (one 8-byte code read), and the activation fragment of the same group,
 // so both MFMA operands hold the same 8 inputs in a lane.
 //
-// LDS bounds it: LDS serves 128 bytes per clock, so a 64-lane 16-byte read takes 8
-// cycles free of bank conflicts and ~13 with random 16-byte entries (the gathers).  Per
-// k-tile and CU (NW = 8, TN = 4) the activation fragments take ~1024 cycles and the
-// gathers ~850, against 1024 cycles of MFMAs; measured on MI355X a k-tile takes ~0.85
-// us (~2040 cycles) in a workgroup with the CU to itself.  Two alternatives measured
-// slower: 64-row wave tiles at one wave per SIMD (each activation fragment used twice,
-// but nothing hides the latency: ~1.1 us per k-tile), and 8 copies of the codebooks
-// spread over the bank period (9.8 instead of 13.2 cycles per gather in isolation,
-// no gain in the kernel).
+// No one unit bounds it.  Per k-tile and CU (NW = 8, TN = 4) the MFMAs take 1024
+// cycles, the activation-fragment reads ~1024 LDS cycles (8 per conflict-free 64-lane
+// 16-byte read) and the gathers ~850 (~13 per random one); measured on MI355X a k-tile
+// takes ~0.85 us (~2040 cycles), with the LDS active ~45% of the time.  Timing variants
+// that each drop one phase (their results wrong, timing only) at batch 2048: without
+// the staging loads -27%, without the gathers -12%, without the fragment reads -10%,
+// without the barrier -5%, without the MFMAs -4%: the phases add up more than they
+// overlap at two waves per SIMD.  Measured slower: 64-row wave tiles at one wave per
+// SIMD (~1.1 us per k-tile), 8 copies of the codebooks over the bank period (9.8
+// instead of 13.2 cycles per gather in isolation, no gain in the kernel), and staging
+// through registers (global loads, then ds_write one k-tile later) instead of the LDS
+// DMA (3-4% slower).
 constexpr int kDqXcds = 8;
 
 template <int NW, int TN, int K>

@@ -753,7 +753,8 @@ def ceilings_bench(args, torch, np):
         # LDS reads: per-instruction time from two iteration counts (the table fill cancels)
         lds = {}
         sink2 = torch.empty(cus * 1024, dtype=torch.int32, device="cuda")
-        for mode, label in ((0, "b128 random"), (1, "b32 random"), (2, "b32 half random half one word")):
+        for mode, label in ((0, "b128 random"), (1, "b32 random"), (2, "b32 half random half one word"),
+                            (3, "b128 random, one lane in eight")):
             ts = []
             for iters in (1024, 3072):
                 g = capture_on(torch, stream, lambda iters=iters: [_launch_ok(lib.ceil_lds_read(
@@ -770,6 +771,10 @@ def ceilings_bench(args, torch, np):
             2 * gr / 64 / cus * lds["b128 random"]["ns_per_wave_instr_per_cu"] / 1e3, 2)
         lds["floor_us_1x16_split_11008x4096"] = round(
             8 * gr / 64 / cus * lds["b32 half random half one word"]["ns_per_wave_instr_per_cu"] / 1e3, 2)
+        # the same codes looked up as whole vectors by the 8 workgroups of a row range, each
+        # holding one eighth of the code space (one lane in eight finds its code there)
+        lds["floor_us_1x16_slab_11008x4096"] = round(
+            8 * gr / 64 / cus * lds["b128 random, one lane in eight"]["ns_per_wave_instr_per_cu"] / 1e3, 2)
         res["lds_read"] = lds
     print(json.dumps(res), flush=True)
 
