@@ -353,12 +353,27 @@ def cpu_baseline(sets, workload, batch, budget_s):
     while not times or time.perf_counter() - t_all < budget_s:
         times.append(one_step(orc))
     t_mt = float(np.median(times))
-    # one thread: the first product once (a whole step would take minutes on the 70B shapes)
+    # one thread: the first product once (a whole step would take minutes on the 70B shapes),
+    # its decode and its matvec timed apart
     name0, o0, i0, K0, B0 = workload[0]
     p0 = sets[0][0][3]
+    o1 = Oracle(nthreads=1)
     t0 = time.perf_counter()
-    Oracle(nthreads=1).gemv(p0["codes"], p0["codebooks"], p0["x"], K0, B0)
+    W0 = o1.decode(p0["codes"], p0["codebooks"], K0, B0)
+    t_dec = time.perf_counter() - t0
+    o1.matvec(W0, p0["x"])
     t_1t = time.perf_counter() - t0
+    del W0
+    # all threads: the same product's decode and matvec apart (median of 3)
+    dec_mt, mv_mt = [], []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        W0 = orc.decode(p0["codes"], p0["codebooks"], K0, B0)
+        t1 = time.perf_counter()
+        orc.matvec(W0, p0["x"])
+        dec_mt.append(t1 - t0)
+        mv_mt.append(time.perf_counter() - t1)
+        del W0
     return {"value": round(step_bytes / t_mt / 1e9, 4), "unit": "GB/s", "cores": cores,
             "kind": "oracle",
             "sample": f"full decode to fp32 W + double matvec of the {len(workload)} products of "
@@ -367,6 +382,10 @@ def cpu_baseline(sets, workload, batch, budget_s):
             "ms_per_step": round(t_mt * 1e3, 1),
             "value_1thread": round(algorithmic_bytes(o0, i0, K0, B0, batch) / t_1t / 1e9, 4),
             "ms_1thread_first_product": round(t_1t * 1e3, 1),
+            "ms_1thread_first_product_decode": round(t_dec * 1e3, 1),
+            "ms_1thread_first_product_matvec": round((t_1t - t_dec) * 1e3, 1),
+            "ms_first_product_decode": round(float(np.median(dec_mt)) * 1e3, 2),
+            "ms_first_product_matvec": round(float(np.median(mv_mt)) * 1e3, 2),
             "cpu_model": cpu_model(), "nproc": os.cpu_count()}
 
 
