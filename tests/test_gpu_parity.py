@@ -270,8 +270,11 @@ def test_graph_capture_replay(aq, orc):
     """Products captured in a HIP graph and replayed several times, with eager work and
     synchronisations between replays, match the eager results every time."""
     import torch
+    # batch 128 and 200 with 8-bit codes: the DMA-staged matrix-core kernel, at 128 with
+    # input-axis splits and the partial-sum kernel
     cases = [(1000, 4096, 2, 8, 1), (1000, 4096, 1, 16, 1), (512, 1024, 2, 8, 4),
-             (512, 1024, 2, 8, 32), (512, 1024, 1, 16, 16)]
+             (512, 1024, 2, 8, 32), (512, 1024, 1, 16, 16), (512, 1024, 2, 8, 128),
+             (300, 2048, 1, 8, 200)]
     stream = torch.cuda.Stream()
     probs, eager, outs = [], [], []
     with torch.cuda.stream(stream):
