@@ -719,6 +719,51 @@ size_t dsm_workspace_bytes(const Problem &p) {
     return dsm_partial_bytes(p) + size_t(p.batch) * size_t(p.in) * 2;
 }
 
+namespace {
+
+// The parts of one matrix added in order, each workgroup on the XCD that ran its row range
+// (range rr: block ids equal to rr modulo 8 in ds_kernel), so that it finds the parts in
+// that XCD's L2.  One wave per workgroup, 64 rows of one range, token blockIdx.y; every
+// part's load is issued before the first add.  Measured on MI355X (1x16 4096 x 11008,
+// batch 1, packed): 14.15 against 14.85 us per call with the rows handed out in order.
+template <int P>
+__global__ void __launch_bounds__(64)
+ds_partial_sum_kernel(const float *__restrict__ partial, uint16_t *__restrict__ y, int out,
+                      int batch, int rows_per_range, int nranges, int chunks) {
+    const int b = blockIdx.x;
+    const int rest = b >> 3;
+    const int c = rest % chunks;
+    const int rr = (rest / chunks) * 8 + (b & 7);
+    if (rr >= nranges) return;
+    const int row = rr * rows_per_range + c * 64 + int(threadIdx.x);
+    if (row >= min(out, (rr + 1) * rows_per_range)) return;
+    const int tok = blockIdx.y;
+    float v[P];
+#pragma unroll
+    for (int q = 0; q < P; ++q) v[q] = partial[(size_t(q) * batch + tok) * out + row];
+    float s = 0.0f;
+#pragma unroll
+    for (int q = 0; q < P; ++q) s += v[q];
+    y[size_t(tok) * out + row] = f2h_bits(s);
+}
+
+hipError_t launch_ds_partial_sum(const Problem &p, const DsCfg &c, const Segs &segs, const float *partial) {
+    if (segs.n > 1) return launch_partial_sum_segs(partial, segs, p.batch, p.K * 8, p.stream);
+    const int chunks = (c.rows_per_range + 63) / 64;
+    const dim3 g(unsigned(c.nranges_padded * chunks), unsigned(p.batch)), b(64);
+    uint16_t *y = static_cast<uint16_t *>(segs.y[0]);
+    const int out = segs.row0[1];
+    if (p.K == 1)
+        hipLaunchKernelGGL(ds_partial_sum_kernel<8>, g, b, 0, p.stream, partial, y, out, p.batch,
+                           c.rows_per_range, c.nranges, chunks);
+    else
+        hipLaunchKernelGGL(ds_partial_sum_kernel<16>, g, b, 0, p.stream, partial, y, out, p.batch,
+                           c.rows_per_range, c.nranges, chunks);
+    return hipGetLastError();
+}
+
+}  // namespace
+
 hipError_t launch_dsm(const Problem &p, void *workspace) {
     Segs segs = p.segs;
     const DsCfg c = ds_cfg(p, &segs);
@@ -733,7 +778,7 @@ hipError_t launch_dsm(const Problem &p, void *workspace) {
     if (e != hipSuccess) return e;
     e = p.K == 1 ? launch_m1<1>(p, c, segs, xT, partial) : launch_m1<2>(p, c, segs, xT, partial);
     if (e != hipSuccess) return e;
-    return launch_partial_sum_segs(partial, segs, p.batch, p.K * 8, p.stream);
+    return launch_ds_partial_sum(p, c, segs, partial);
 }
 
 bool ds_supported(const Problem &p) {
@@ -765,7 +810,7 @@ hipError_t launch_ds(const Problem &p, void *workspace) {
     float *partial = static_cast<float *>(workspace);
     hipError_t e = p.K == 1 ? launch1<1>(p, c, segs, partial) : launch1<2>(p, c, segs, partial);
     if (e != hipSuccess) return e;
-    return launch_partial_sum_segs(partial, segs, p.batch, p.K * 8, p.stream);
+    return launch_ds_partial_sum(p, c, segs, partial);
 }
 
 size_t split_canonical_pack_bytes(const Problem &p) {

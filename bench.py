@@ -115,6 +115,17 @@ def trace_times(product, variant):
     return None, None
 
 
+def _product_call(variant, o, i, K, main_name, psum_grid):
+    """Whether a main kernel and the partial-sum kernel after it are a call of the packed
+    product (o, i, K): lut_packed by the partial sum's grid (one thread per output row);
+    split by its kernel's template arguments (the chunk positions per lane follow from in),
+    since its partial sum's grid is rounded to whole row ranges."""
+    if variant == "lut_packed":
+        return psum_grid == o
+    nseg = -(-((i // 8) // (8 // K)) // 64)
+    return re.search(rf"ds_kernel<{K}, 1, {nseg}, 1>", main_name) is not None
+
+
 def summarize_trace(trace_dir):
     """Machine-readable rows for the kernel-trace summary from a rocprofv3 --kernel-trace
     run of the headline benchmark: per packed product, the median duration of its main
@@ -139,7 +150,7 @@ def summarize_trace(trace_dir):
             if not re.search(r"::" + mains[variant] + r"<", r["Kernel_Name"]):
                 continue
             nxt = next((q for q in rows[j + 1:j + 4] if "partial_sum" in q["Kernel_Name"]), None)
-            if nxt is None or int(nxt["Grid_Size_X"]) != o:
+            if nxt is None or not _product_call(variant, o, i, K, r["Kernel_Name"], int(nxt["Grid_Size_X"])):
                 continue
             main_d.append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
             call_d.append((int(nxt["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
@@ -193,7 +204,7 @@ def summarize_traffic(copy_fetch, copy_write, fetch_dir, write_dir):
     fetch, write = rows_of(fetch_dir), rows_of(write_dir)
     mains = {"lut_packed": "lut_packed_kernel", "split": "ds_kernel"}
 
-    def per_product(rows, name, out, variant):
+    def per_product(rows, name, out, in_, K, variant):
         main, red = [], []
         for j, r in enumerate(rows):
             if not re.search(r"::" + mains[variant] + r"<", r["Kernel_Name"]):
@@ -201,7 +212,7 @@ def summarize_traffic(copy_fetch, copy_write, fetch_dir, write_dir):
             if j > 0 and "pack_pairs" in rows[j - 1]["Kernel_Name"]:
                 continue                     # the canonical-layout call
             nxt = next((q for q in rows[j + 1:j + 4] if "partial_sum" in q["Kernel_Name"]), None)
-            if nxt is None or int(nxt["Grid_Size"]) != out:
+            if nxt is None or not _product_call(variant, out, in_, K, r["Kernel_Name"], int(nxt["Grid_Size"])):
                 continue
             main.append(float(r["Counter_Value"]))
             red.append(float(nxt["Counter_Value"]))
@@ -215,8 +226,8 @@ def summarize_traffic(copy_fetch, copy_write, fetch_dir, write_dir):
     machine = []
     for name, o, i, K, B in WORKLOAD:
         variant = "split" if B == 16 else "lut_packed"
-        fm, fr = per_product(fetch, name, o, variant)
-        wm, wr = per_product(write, name, o, variant)
+        fm, fr = per_product(fetch, name, o, i, K, variant)
+        wm, wr = per_product(write, name, o, i, K, variant)
         if fm is None or wm is None:
             continue
         nbytes = int(round((fm + fr) * 1024 * f_fetch + (wm + wr) * 1024 * f_write))
