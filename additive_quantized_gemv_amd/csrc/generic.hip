@@ -157,6 +157,62 @@ partial_sum_kernel(const float *__restrict__ partial, uint16_t *__restrict__ y, 
     y[i] = f2h_bits(s);
 }
 
+// Batched sums, four consecutive rows of one token per thread (16-byte loads, one 8-byte
+// store): with one output per thread the 1.6 M outputs of a batch-128 12288-row sum run as
+// ~24,000 waves of two loads each, in several latency-bound rounds.  Needs T, every
+// matrix's first row and each y_m 4-element aligned (the launcher checks); parts added in
+// order as above.
+template <int NS, int PMAX>
+__global__ void __launch_bounds__(64)
+partial_sum4_kernel(const float *__restrict__ partial, int batch, int parts, const Segs segs) {
+    const int T = seg_total<NS>(segs.n, segs.row0);
+    const int64_t n = int64_t(batch) * T;
+    const int g = (blockIdx.x * blockDim.x + threadIdx.x) * 4;   // first of four global rows
+    const int b = blockIdx.y;
+    if (g >= T) return;
+    const int64_t i = int64_t(b) * T + g;
+    float4 v[PMAX];
+#pragma unroll
+    for (int q = 0; q < PMAX; ++q)
+        v[q] = *reinterpret_cast<const float4 *>(partial + int64_t(min(q, parts - 1)) * n + i);
+    float s0 = 0.0f, s1 = 0.0f, s2 = 0.0f, s3 = 0.0f;
+#pragma unroll
+    for (int q = 0; q < PMAX; ++q) {
+        const bool in = q < parts;
+        s0 += in ? v[q].x : 0.0f;
+        s1 += in ? v[q].y : 0.0f;
+        s2 += in ? v[q].z : 0.0f;
+        s3 += in ? v[q].w : 0.0f;
+    }
+    const int m = seg_of<NS>(segs.n, segs.row0, g);
+    const int out_m = pick(segs.row0, m + 1) - pick(segs.row0, m);
+    uint16_t *dst = static_cast<uint16_t *>(pick(segs.y, m)) + int64_t(b) * out_m + (g - pick(segs.row0, m));
+    *reinterpret_cast<uint2 *>(dst) = uint2{f2h_bits(s0) | (uint32_t(f2h_bits(s1)) << 16),
+                                            f2h_bits(s2) | (uint32_t(f2h_bits(s3)) << 16)};
+}
+
+// the four-row form applies: more than one token, and every row range and output row
+// 4-element aligned
+bool psum4_fits(const float *partial, const Segs &segs, int batch) {
+    if (batch < 2 || (reinterpret_cast<uintptr_t>(partial) & 15u)) return false;
+    for (int m = 0; m <= segs.n; ++m)
+        if (segs.row0[m] % 4) return false;
+    for (int m = 0; m < segs.n; ++m)
+        if (reinterpret_cast<uintptr_t>(segs.y[m]) & 7u) return false;
+    return true;
+}
+
+template <int PMAX>
+void launch_psum4(const float *partial, const Segs &segs, int batch, int parts, hipStream_t s) {
+    const int T = segs.row0[segs.n];
+    const dim3 grid(unsigned((T / 4 + 63) / 64), unsigned(batch));
+    if (segs.n == 1)
+        hipLaunchKernelGGL((partial_sum4_kernel<1, PMAX>), grid, dim3(64), 0, s, partial, batch, parts, segs);
+    else
+        hipLaunchKernelGGL((partial_sum4_kernel<kMaxSegs, PMAX>), grid, dim3(64), 0, s, partial, batch,
+                           parts, segs);
+}
+
 template <int PMAX>
 void launch_psum(const float *partial, const Segs &segs, int batch, int parts, hipStream_t s) {
     constexpr int TPB = PMAX > 0 ? 64 : 256;
@@ -179,6 +235,14 @@ void launch_psum(const float *partial, const Segs &segs, int batch, int parts, h
 
 hipError_t launch_partial_sum_segs(const float *partial, const Segs &segs, int batch, int parts,
                                    hipStream_t s) {
+    if (parts <= 32 && psum4_fits(partial, segs, batch)) {
+        if (parts <= 2) launch_psum4<2>(partial, segs, batch, parts, s);
+        else if (parts <= 4) launch_psum4<4>(partial, segs, batch, parts, s);
+        else if (parts <= 8) launch_psum4<8>(partial, segs, batch, parts, s);
+        else if (parts <= 16) launch_psum4<16>(partial, segs, batch, parts, s);
+        else launch_psum4<32>(partial, segs, batch, parts, s);
+        return hipGetLastError();
+    }
     if (parts <= 8) launch_psum<8>(partial, segs, batch, parts, s);
     else if (parts <= 16) launch_psum<16>(partial, segs, batch, parts, s);
     else if (parts <= 24) launch_psum<24>(partial, segs, batch, parts, s);
